@@ -1,0 +1,282 @@
+"""CPU oracle for block-retrieval sparse attention (plain NumPy, float64).
+
+THIS IS TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it.  The HIP library never
+calls it, links it or falls back to it, and it shares no code with the HIP
+library: the two meet only in the seeded inputs of ``synth``.
+
+What it computes, in the pages' order
+-------------------------------------
+The method shared by MemLong, InfLLM, Landmark Attention and
+RetrievalAttention is: a long key/value memory cut into fixed-length blocks,
+one or more representative vectors per block, a relevance score between the
+query and each block's representatives, exact top-k block selection, and
+softmax attention over the local context plus the selected blocks.
+
+* O1 representatives (``reps_*``): block tiling from MemLong section 2.2.1
+  (non-overlapping chunks) and Landmark Attention "proposed method"
+  (fixed-length blocks); representative tokens from InfLLM "method" (a few
+  tokens of each memory unit stand for it); given vectors from Landmark (one
+  landmark key per block) and MemLong section 2.3.2 (the stored chunk
+  embedding r^m = r^q).
+* O2 eligibility (``eligible_range``): InfLLM "method" -- the memory holds
+  what lies outside the local window.
+* O3 scores (``scores_dot_max``, ``scores_cosine``): Landmark "proposed
+  method" (similarity between the query and the landmark key), InfLLM
+  "method" (block-level relevance), MemLong section 2.3.2 (cosine similarity
+  between r^q and the stored embeddings).
+* O4 selection (``select_topk``): MemLong section 2.3.2 (TopK of the cosine
+  scores, done with an exact index, section 2.4.2).
+* O5 attended set (``attended_mask``): InfLLM "method" (local tokens plus a
+  few relevant memory units), MemLong section 2.3.4 (retrieved chunks plus
+  the current chunk), Landmark "proposed method" (a block's tokens are
+  loaded only when its landmark is selected).
+* O6 attention (``attention``): MemLong Figure 3 (local context is causal;
+  retrieved chunks are visible in full), RetrievalAttention "proposed
+  method" (exact attention over the tokens that matter).
+
+Readings where the pages are silent (the same list is kept with the design
+notes): attention sinks are the first S tokens; the window is the last W
+tokens of memory; a partial tail block is never a candidate; a block wholly
+inside sinks or window is not a candidate; ties go to the lower block index
+and NaN ranks last; scores are exact-product float64 sums rounded once to
+float32; softmax scale is 1/sqrt(d) and scores carry no scale; query head h
+reads kv head h // G; several representatives combine by max; the selection
+is per query head for dot scores and per sequence for cosine scores; local
+and retrieved tokens share one softmax with no gate; query j of n sits at
+position N - n + j; the cosine of a zero vector is 0.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+against brute force, exact rational arithmetic, closed forms or independent
+library routines.  The pages print no worked numbers, so no value here is
+pinned to a printed value.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# storage rounding
+
+
+_FMT = {"f32": (24, -126), "bf16": (8, -126)}  # significand bits, min normal exponent
+
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest ``dtype`` value, ties to even.
+
+    Plain definition of IEEE round-to-nearest-even with p significand bits:
+    find the binade of |x| (clamped at the smallest normal binade so that
+    subnormals get the fixed subnormal spacing), express x in units of that
+    binade's spacing, round to the nearest integer with ties to even
+    (``np.rint``), and scale back.  Results beyond the largest finite value
+    become infinities.  Returns float64 holding exactly representable values.
+    """
+    p, emin = _FMT[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(x[fin])            # x = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e - 1, emin)        # binade exponent, floor(log2|x|)
+    spacing_exp = e - (p - 1)
+    out[fin] = np.ldexp(np.rint(np.ldexp(x[fin], -spacing_exp)), spacing_exp)
+    big = (2.0 - 2.0 ** (1 - p)) * 2.0 ** 127
+    over = fin & (np.abs(np.where(fin, out, 0.0)) > big)
+    out[over] = np.copysign(np.inf, x[over])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O1: block representatives
+
+
+def reps_mean(K: np.ndarray, B: int, dtype: str) -> np.ndarray:
+    """Mean key of every complete block: [nb][1][d], rounded once to ``dtype``.
+
+    K is one kv head's memory, [N][d] float64 holding the stored values.
+    """
+    nb = K.shape[0] // B
+    d = K.shape[1]
+    s = K[: nb * B].reshape(nb, B, d).sum(axis=1)
+    return round_to_dtype(s / B, dtype)[:, None, :]
+
+
+def reps_topnorm(K: np.ndarray, B: int, R: int) -> np.ndarray:
+    """The R keys of every complete block with the largest L2 norm: [nb][R][d].
+
+    Stand-in for InfLLM's representative tokens.  Squared norms are float64
+    sums; order is (norm descending, token index ascending); the chosen keys
+    are copied unchanged, in that order.
+    """
+    nb = K.shape[0] // B
+    out = np.empty((nb, R, K.shape[1]))
+    for b in range(nb):
+        blk = K[b * B:(b + 1) * B]
+        n2 = (blk * blk).sum(axis=1)
+        order = sorted(range(B), key=lambda t: (-n2[t], t))
+        out[b] = blk[order[:R]]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O2: eligibility
+
+
+def eligible_range(N: int, B: int, S: int, W: int) -> tuple[int, int]:
+    """Candidate blocks [lo, hi): complete blocks with a token outside sinks and window.
+
+    Tokens outside the sinks [0, S) and the window [N - W, N) are [S, N - W).
+    Block b = [bB, bB + B) meets it iff b >= floor(S / B) and
+    b < ceil((N - W) / B); it must also be complete, b < floor(N / B).
+    """
+    nb = N // B
+    lo = min(S // B, nb)
+    if N - W <= S:
+        return lo, lo
+    hi = min(nb, -(-(N - W) // B))
+    return lo, max(lo, hi)
+
+
+# ---------------------------------------------------------------------------
+# O3: scores
+
+
+def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """Query head h reads kv head floor(h / G), G = n_q_heads / n_kv_heads."""
+    return h // (n_q_heads // n_kv_heads)
+
+
+def scores_dot_max(q: np.ndarray, reps: np.ndarray) -> np.ndarray:
+    """s_b = float32( max_r q . rep_{b,r} ) for one query head; q [d], reps [nb][R][d]."""
+    dots = reps @ q                      # [nb][R], float64
+    return dots.max(axis=1).astype(np.float32)
+
+
+def scores_cosine(rq: np.ndarray, E: np.ndarray) -> np.ndarray:
+    """s_b = float32( rq . e_b / (|rq| |e_b|) ), 0 when a norm is 0; E [nb][D]."""
+    dot = E @ rq
+    nq = math.sqrt(float(rq @ rq))
+    ne = np.sqrt((E * E).sum(axis=1))
+    den = nq * ne
+    s = np.zeros_like(dot)
+    ok = den != 0
+    s[ok] = dot[ok] / den[ok]
+    return s.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# O4: top-k
+
+
+def select_topk(scores: np.ndarray, lo: int, hi: int, k: int):
+    """First min(k, hi - lo) candidates by (score descending, index ascending).
+
+    NaN ranks after every number.  Returns (idx int32 [k], vals float32 [k]);
+    unused slots hold -1 and -inf.
+    """
+    def key(b):
+        s = float(scores[b])
+        return (1, 0.0, b) if math.isnan(s) else (0, -s, b)
+
+    order = sorted(range(lo, hi), key=key)[:k]
+    idx = np.full(k, -1, dtype=np.int32)
+    vals = np.full(k, -np.inf, dtype=np.float32)
+    idx[: len(order)] = order
+    vals[: len(order)] = scores[order] if order else []
+    return idx, vals
+
+
+# ---------------------------------------------------------------------------
+# O5: attended token set
+
+
+def attended_mask(N: int, B: int, S: int, W: int, idx) -> np.ndarray:
+    """Boolean [N]: sinks [0, S), window [max(N - W, 0), N), and every selected block.
+
+    A set: a token counted by several parts is still one token.
+    """
+    T = np.zeros(N, dtype=bool)
+    T[: min(S, N)] = True
+    T[max(N - W, 0):] = True
+    for b in idx:
+        b = int(b)
+        if b >= 0:
+            T[b * B: min((b + 1) * B, N)] = True
+    return T
+
+
+# ---------------------------------------------------------------------------
+# O6: attention
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, T: np.ndarray, scale: float) -> np.ndarray:
+    """Exact softmax attention of n queries over the set T, causal in position.
+
+    Q [n][d], K and V [N][d] float64, T boolean [N].  Query j sits at
+    position N - n + j and sees the tokens of T at or before it.  Softmax is
+    computed with its maximum subtracted.  An empty set raises ValueError.
+    """
+    n, N = Q.shape[0], K.shape[0]
+    out = np.empty((n, V.shape[1]))
+    pos = np.arange(N)
+    for j in range(n):
+        sel = T & (pos <= N - n + j)
+        if not sel.any():
+            raise ValueError(f"query {j}: empty attended set")
+        z = scale * (K[sel] @ Q[j])
+        w = np.exp(z - z.max())
+        out[j] = (w / w.sum()) @ V[sel]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# composition: one step over a whole workload
+
+
+def build_reps(K_bg: np.ndarray, mode: str, B: int, R: int, dtype: str, given=None) -> np.ndarray:
+    """O1 for one (batch, head): [nb][R][d]."""
+    if mode == "mean":
+        return reps_mean(K_bg, B, dtype)
+    if mode == "topnorm":
+        return reps_topnorm(K_bg, B, R)
+    if mode in ("given", "embed"):
+        return np.asarray(given, dtype=np.float64)
+    raise ValueError(mode)
+
+
+def step(q, K, V, reps, *, block: int, k: int, sinks: int, window: int, mode: str,
+         rq=None, scale=None, heads=None):
+    """One pass of the path (O3 -> O6) with representatives already built.
+
+    q [β][Hq][n][d], K/V [β][Hkv][N][d], reps [β][Hr][nb][R][Dr] (all float64),
+    rq [β][Dr] for cosine scoring.  ``heads`` limits the work to a list of
+    (β, h) pairs.  Returns dicts keyed by (β, h) -- for cosine scoring the
+    score/selection key is (β, 0) -- of scores, idx, vals and out.
+    """
+    Bt, Hq, n, d = q.shape
+    Hkv, N = K.shape[1], K.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    lo, hi = eligible_range(N, block, sinks, window)
+    nb_all = reps.shape[2]
+    pairs = heads if heads is not None else [(b, h) for b in range(Bt) for h in range(Hq)]
+    res = {"scores": {}, "idx": {}, "vals": {}, "out": {}, "range": (lo, hi)}
+    for (b, h) in pairs:
+        g = kv_head_of(h, Hq, Hkv)
+        if mode == "embed":
+            key = (b, 0)
+            if key not in res["idx"]:
+                s = np.full(nb_all, np.nan, dtype=np.float32)
+                s[lo:hi] = scores_cosine(rq[b], reps[b, 0, lo:hi, 0, :])
+                res["scores"][key] = s
+                res["idx"][key], res["vals"][key] = select_topk(s, lo, hi, k)
+        else:
+            key = (b, h)
+            s = np.full(nb_all, np.nan, dtype=np.float32)
+            s[lo:hi] = scores_dot_max(q[b, h, -1], reps[b, g, lo:hi])
+            res["scores"][key] = s
+            res["idx"][key], res["vals"][key] = select_topk(s, lo, hi, k)
+        T = attended_mask(N, block, sinks, window, res["idx"][key])
+        res["out"][(b, h)] = attention(q[b, h], K[b, g], V[b, g], T, scale)
+    return res

@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP library's binding, only on a host with a GPU."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this host")
+    import block_retrieval_sparse_amd as brs
+
+    return brs

@@ -1,0 +1,616 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something other
+than itself -- exact rational arithmetic, brute force over tiny inputs, closed
+forms, or an independent library routine.  ``test_planted_mistakes`` then
+plants plausible mistakes in the oracle (on the CPU) and requires that some
+check catches every one of them.
+
+Page references: MemLong section 2.3.2 (cosine top-k over chunk embeddings;
+memory of K-V plus index-aligned embeddings), Figure 3 (retrieved chunks fully
+visible, local context causal); InfLLM "method" (window + block memory units
+with representative tokens); Landmark Attention "proposed method" (one
+landmark per fixed-length block, query-landmark similarity decides retrieval);
+MoNIM section 2.1 (kNN lookup over a key-value store: the token-level special
+case used below).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.brs_oracle as O
+
+# ---------------------------------------------------------------------------
+# independent exact helpers (Fraction arithmetic)
+
+
+def rne_fraction(x: Fraction, p: int, emin: int = -126) -> Fraction:
+    """Exact round-to-nearest-even of a rational to p significand bits."""
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    unit = Fraction(2) ** (e - p + 1)
+    n = round(x / unit)  # Fraction.__round__ rounds half to even
+    return n * unit
+
+
+def exact(v) -> Fraction:
+    return Fraction(float(v))
+
+
+def bf16_values(rng, shape) -> np.ndarray:
+    """float64 array of exact bfloat16 values (independent of the oracle's rounding)."""
+    t = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# checks (reach the oracle through the module so mistakes can be planted)
+
+
+def check_round_f32():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-40, 38, 4000),
+                        [1e-45, 3e-39, -2.5e-40, 3.4028235e38, 3.5e38, 1 + 2 ** -24, 1 + 3 * 2 ** -24]])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float32).astype(np.float64)
+    got = O.round_to_dtype(x, "f32")
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+
+
+def check_round_bf16():
+    rng = np.random.default_rng(2)
+    x32 = (rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000)).astype(np.float32)
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.4028235e38, 1e-39], dtype=np.float32)
+    x32 = np.concatenate([x32, ties])
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_to_dtype(x32.astype(np.float64), "bf16")
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+    # float64 inputs: compare with exact rational rounding (no double rounding)
+    x64 = rng.standard_normal(300) * 3
+    got = O.round_to_dtype(x64, "bf16")
+    for a, b in zip(x64, got):
+        assert Fraction(float(b)) == rne_fraction(Fraction(float(a)), 8)
+
+
+def check_eligible_bruteforce():
+    for N in range(1, 70):
+        for B in (1, 2, 3, 5, 8, 16):
+            for S in (0, 1, 3, 7, 16, 40):
+                for W in (0, 1, 4, 9, 16, 33, 80):
+                    nb = N // B
+                    union = set(range(min(S, N))) | set(range(max(N - W, 0), N))
+                    want = [b for b in range(nb) if any(t not in union for t in range(b * B, (b + 1) * B))]
+                    lo, hi = O.eligible_range(N, B, S, W)
+                    assert list(range(lo, hi)) == want, (N, B, S, W, lo, hi, want)
+
+
+def check_eligible_workloads():
+    # closed form evaluated by hand for the five workloads
+    assert O.eligible_range(4096, 64, 4, 256) == (0, 60)
+    assert O.eligible_range(32768, 50, 0, 512) == (0, 646)
+    assert O.eligible_range(131072, 128, 128, 4096) == (1, 992)
+    assert O.eligible_range(82432, 512, 0, 512) == (0, 160)
+    assert O.eligible_range(1048576, 64, 0, 0) == (0, 16384)
+
+
+def check_mean_exact():
+    rng = np.random.default_rng(3)
+    for dtype, p in (("bf16", 8), ("f32", 24)):
+        for B in (1, 3, 64):
+            K = bf16_values(rng, (B * 4 + B // 2, 5)) if dtype == "bf16" else \
+                rng.standard_normal((B * 4 + B // 2, 5)).astype(np.float32).astype(np.float64)
+            got = O.reps_mean(K, B, dtype)
+            assert got.shape == (4, 1, 5)
+            for b in range(4):
+                for i in range(5):
+                    s = sum(exact(K[t, i]) for t in range(b * B, (b + 1) * B))
+                    assert exact(got[b, 0, i]) == rne_fraction(s / B, p)
+    # a block of identical keys has that key as its mean
+    K = np.repeat(bf16_values(rng, (1, 8)), 64, axis=0)
+    assert np.array_equal(O.reps_mean(K, 64, "bf16")[0, 0], K[0])
+
+
+def check_topnorm_bruteforce():
+    rng = random.Random(4)
+    for trial in range(60):
+        B, R, d = rng.randint(1, 7), rng.randint(1, 4), rng.randint(1, 4)
+        R = min(R, B)
+        vals = [[rng.choice([-2, -1, 0, 1, 2, 0.5, 3]) for _ in range(d)] for _ in range(2 * B)]
+        K = np.array(vals, dtype=np.float64)
+        got = O.reps_topnorm(K, B, R)
+        for b in range(2):
+            toks = list(range(b * B, (b + 1) * B))
+            norms = {t: sum(Fraction(x) ** 2 for x in vals[t]) for t in toks}
+            # brute force: the ordered R-tuple that no other ordering beats
+            best = max(itertools.permutations(toks, R),
+                       key=lambda perm: [(norms[t], -t) for t in perm])
+            assert np.array_equal(got[b], K[list(best)]), (trial, b)
+    # one key scaled up becomes the first representative
+    K = np.array([[1.0, 0.0], [0.0, 1.0], [10.0, 0.0], [0.5, 0.5]])
+    assert np.array_equal(O.reps_topnorm(K, 4, 1)[0, 0], [10.0, 0.0])
+    # equal norms: lower token first
+    K = np.array([[0.0, 2.0], [2.0, 0.0], [-2.0, 0.0], [1.0, 1.0]])
+    assert np.array_equal(O.reps_topnorm(K, 4, 3)[0], K[[0, 1, 2]])
+
+
+def check_dot_exact_mips():
+    """B = 1, R = 1: scores are exact maximum-inner-product values over the keys
+    (the kNN key-value lookup of MoNIM section 2.1), rounded once to float32."""
+    rng = np.random.default_rng(5)
+    for d in (4, 64, 128):
+        q = bf16_values(rng, (d,))
+        keys = bf16_values(rng, (50, d))
+        got = O.scores_dot_max(q, keys[:, None, :])
+        for b in range(50):
+            s = sum(exact(q[i]) * exact(keys[b, i]) for i in range(d))
+            assert Fraction(float(got[b])) == rne_fraction(s, 24), (d, b)
+    # hand example and max over representatives
+    q = np.array([1.0, 2.0])
+    reps = np.array([[[3.0, 4.0]], [[-1.0, 0.0]]])
+    assert O.scores_dot_max(q, reps).tolist() == [11.0, -1.0]
+    reps2 = np.array([[[1.0, 0.0], [0.0, 5.0], [2.0, 2.0]]])
+    assert O.scores_dot_max(q, reps2).tolist() == [10.0]
+    # R copies of one representative score like that representative
+    r = bf16_values(rng, (7, 1, 128))
+    q = bf16_values(rng, (128,))
+    assert np.array_equal(O.scores_dot_max(q, np.repeat(r, 4, axis=1)), O.scores_dot_max(q, r))
+
+
+def check_cosine():
+    from scipy.spatial.distance import cosine as scipy_cosine_distance
+
+    rng = np.random.default_rng(6)
+    rq = bf16_values(rng, (768,))
+    E = bf16_values(rng, (40, 768))
+    got = O.scores_cosine(rq, E)
+    want = np.array([1.0 - scipy_cosine_distance(rq, e) for e in E])
+    assert np.max(np.abs(got - want)) < 2e-7
+    # cos(x, x) = 1, cos(x, -x) = -1, zero vector scores 0
+    E2 = np.stack([rq, -rq, np.zeros(768), 2.0 * rq])
+    assert O.scores_cosine(rq, E2).tolist() == [1.0, -1.0, 0.0, 1.0]
+    assert O.scores_cosine(np.zeros(768), E).tolist() == [0.0] * 40
+    # scale invariance (power-of-two scales are exact)
+    assert np.array_equal(O.scores_cosine(4.0 * rq, 0.5 * E), got)
+    # unit-norm inputs: a plain dot product
+    u = rq / np.linalg.norm(rq)
+    V = E / np.linalg.norm(E, axis=1, keepdims=True)
+    assert np.max(np.abs(O.scores_cosine(u, V) - (V @ u))) < 1e-7
+
+
+def _key(s, b):
+    return (1, 0.0, b) if math.isnan(s) else (0, -s, b)
+
+
+def check_topk_bruteforce():
+    rng = random.Random(7)
+    for trial in range(300):
+        n = rng.randint(1, 8)
+        s = np.array([rng.choice([0.5, 1.0, 1.0, -2.0, 3.0, float("nan"), 7.25]) for _ in range(n)],
+                     dtype=np.float32)
+        lo = rng.randint(0, n)
+        hi = rng.randint(lo, n)
+        k = rng.randint(1, n + 2)
+        idx, vals = O.select_topk(s, lo, hi, k)
+        m = min(k, hi - lo)
+        # exhaustive: the one m-subset whose every member beats every non-member
+        cands = range(lo, hi)
+        winners = [c for c in itertools.combinations(cands, m)
+                   if all(_key(s[a], a) < _key(s[z], z) for a in c for z in cands if z not in c)]
+        assert len(winners) == 1
+        want = sorted(winners[0], key=lambda b: _key(s[b], b))
+        assert idx[:m].tolist() == list(want), (trial, s, lo, hi, k, idx)
+        assert idx[m:].tolist() == [-1] * (k - m)
+        assert np.array_equal(vals[:m], s[list(want)], equal_nan=True)
+        assert np.all(np.isneginf(vals[m:]))
+
+
+def check_topk_ties_and_nan():
+    s = np.array([1.0, 5.0, 5.0, np.nan, 5.0, 2.0], dtype=np.float32)
+    idx, _ = O.select_topk(s, 0, 6, 6)
+    assert idx.tolist() == [1, 2, 4, 5, 0, 3]
+    idx, _ = O.select_topk(s, 2, 6, 2)
+    assert idx.tolist() == [2, 4]
+    idx, _ = O.select_topk(s, 0, 2, 4)
+    assert idx.tolist() == [1, 0, -1, -1]
+    # independent library routine on a larger random case with many ties
+    rng = np.random.default_rng(8)
+    s = rng.integers(0, 20, 5000).astype(np.float32)
+    import heapq
+
+    want = heapq.nsmallest(100, range(10, 4990), key=lambda b: (-float(s[b]), b))
+    assert O.select_topk(s, 10, 4990, 100)[0].tolist() == want
+
+
+def check_attention_full_causal():
+    """All blocks retrieved (or window covering all): full causal attention,
+    against torch's scaled_dot_product_attention in float64."""
+    rng = np.random.default_rng(9)
+    for (N, B, S, W, n) in ((37, 4, 2, 5, 1), (64, 8, 0, 8, 6), (50, 50, 0, 50, 50), (33, 4, 1, 3, 3)):
+        d = 16
+        Q, K, V = rng.standard_normal((n, d)), rng.standard_normal((N, d)), rng.standard_normal((N, d))
+        lo, hi = O.eligible_range(N, B, S, W)
+        idx, _ = O.select_topk(rng.standard_normal(N // B + 1).astype(np.float32), lo, hi, N)
+        T = O.attended_mask(N, B, S, W, idx)
+        if N % B and N % B > W:
+            continue  # an unattended tail: not the full-attention case
+        assert T.all()
+        got = O.attention(Q, K, V, T, 1 / math.sqrt(d))
+        mask = torch.arange(N)[None, :] <= (N - n + torch.arange(n))[:, None]
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+            attn_mask=mask[None]).numpy()[0]
+        assert np.max(np.abs(got - want)) < 1e-12
+
+
+def check_attention_set_by_zero_query():
+    """q = 0 gives equal weights, so the output is the plain mean of V over the
+    attended set -- which pins the set itself (sinks, window, blocks, dedup,
+    causal cut)."""
+    rng = np.random.default_rng(10)
+    for trial in range(40):
+        N = int(rng.integers(20, 90))
+        B = int(rng.integers(2, 12))
+        S = int(rng.integers(0, 10))
+        W = int(rng.integers(0, 20))
+        n = int(rng.integers(1, 4))
+        nb = N // B
+        picks = sorted(set(rng.integers(0, max(nb, 1), 3).tolist())) if nb else []
+        idx = np.array(picks + [-1], dtype=np.int32)
+        V = rng.standard_normal((N, 3))
+        T = O.attended_mask(N, B, S, W, idx)
+        got = O.attention(np.zeros((n, 3)), rng.standard_normal((N, 3)), V, T, 0.5)
+        for j in range(n):
+            p = N - n + j
+            toks = set(range(min(S, N))) | set(range(max(N - W, 0), N))
+            for b in picks:
+                toks |= set(range(b * B, (b + 1) * B))
+            toks = sorted(t for t in toks if t <= p)
+            assert np.allclose(got[j], V[toks].mean(axis=0), atol=1e-13, rtol=0), (trial, j)
+
+
+def check_attention_properties():
+    rng = np.random.default_rng(11)
+    N, B, d = 96, 8, 16
+    K, V = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    q = rng.standard_normal((1, d))
+    idx = np.array([3, 7, 1, -1], dtype=np.int32)
+    T = O.attended_mask(N, B, 2, 10, idx)
+    base = O.attention(q, K, V, T, 0.25)
+    # weights sum to one: V = 1 gives 1
+    assert np.allclose(O.attention(q, K, np.ones((N, d)), T, 0.25), 1.0, atol=1e-14)
+    # order of idx does not matter
+    T2 = O.attended_mask(N, B, 2, 10, idx[[2, 0, 3, 1]])
+    assert np.array_equal(O.attention(q, K, V, T2, 0.25), base)
+    # the scale multiplies the logits
+    assert np.allclose(O.attention(q * 0.25, K, V, T, 1.0), base, atol=1e-14)
+    # output is a convex combination of the attended V rows
+    assert np.all(base <= V[T].max(axis=0) + 1e-12) and np.all(base >= V[T].min(axis=0) - 1e-12)
+    # shifting all logits equally leaves the output unchanged: add a constant
+    # key component along a direction orthogonal-complemented by the query
+    with pytest.raises(ValueError):
+        O.attention(q, K, V, np.zeros(N, dtype=bool), 0.25)
+
+
+def check_gqa_is_replicated_mha():
+    rng = np.random.default_rng(12)
+    Bt, Hq, Hkv, N, d, B = 2, 8, 2, 64, 8, 8
+    q = rng.standard_normal((Bt, Hq, 1, d))
+    K, V = rng.standard_normal((Bt, Hkv, N, d)), rng.standard_normal((Bt, Hkv, N, d))
+    reps = np.stack([np.stack([O.reps_topnorm(K[b, g], B, 2) for g in range(Hkv)]) for b in range(Bt)])
+    kw = dict(block=B, k=2, sinks=4, window=8, mode="topnorm")
+    gqa = O.step(q, K, V, reps, **kw)
+    G = Hq // Hkv
+    rep = lambda X: np.repeat(X, G, axis=1)  # noqa: E731  (kv head g serves query heads gG..gG+G-1)
+    mha = O.step(q, rep(K), rep(V), rep(reps), **kw)
+    for key in gqa["out"]:
+        assert np.array_equal(gqa["idx"][key], mha["idx"][key])
+        assert np.array_equal(gqa["out"][key], mha["out"][key])
+    assert O.kv_head_of(5, 32, 8) == 1 and O.kv_head_of(31, 32, 8) == 7 and O.kv_head_of(3, 4, 4) == 3
+
+
+def check_planted_recall():
+    """Blocks whose keys align with the query are retrieved (InfLLM's needle
+    claim, here on synthetic planted blocks)."""
+    from synth import WORKLOADS
+    from synth import inputs as I
+
+    w = WORKLOADS["infllm_gqa_decode_128k"].scaled(n_tokens=8192, window=512, sinks=128, n_q_heads=8,
+                                                   n_kv_heads=2, k=10)
+    x = I.make_all(w, "cpu")
+    f = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    K = f(x["k"])
+    reps = np.stack([np.stack([O.reps_topnorm(K[b, g], w.block, w.reps_per_block)
+                               for g in range(w.n_kv_heads)]) for b in range(w.batch)])
+    res = O.step(f(x["q"]), K, f(x["v"]), reps, block=w.block, k=w.k, sinks=w.sinks,
+                 window=w.window, mode="topnorm")
+    for (b, h), blocks in x["planted"].items():
+        assert set(blocks) <= set(res["idx"][(b, h)].tolist()), (h, blocks, res["idx"][(b, h)])
+
+
+def check_hand_worked_fixture():
+    """The hand-derived decode step in tests/golden/hand_worked_decode.json."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_decode.json")))
+    K, V = np.array(g["K"], float), np.array(g["V"], float)
+    assert O.eligible_range(g["N"], g["B"], g["S"], g["W"]) == tuple(g["eligible"])
+    reps = O.reps_mean(K, g["B"], "f32")
+    assert np.array_equal(reps[:, 0, :], np.array(g["reps"], float))
+    lo, hi = g["eligible"]
+    for j, qv in enumerate(g["q"]):
+        q = np.array(qv, float)
+        s = O.scores_dot_max(q, reps[lo:hi])
+        assert s.tolist() == g["scores"][j]
+        full = np.full(reps.shape[0], np.nan, dtype=np.float32)
+        full[lo:hi] = s
+        idx, _ = O.select_topk(full, lo, hi, g["k"])
+        assert idx.tolist() == g["idx"][j]
+        T = O.attended_mask(g["N"], g["B"], g["S"], g["W"], idx)
+        out = O.attention(q[None], K, V, T, g["scale"])[0]
+        assert np.allclose(out, g["out"][j], atol=1e-15, rtol=0)
+
+
+def check_step_cosine_chunks():
+    """Cosine mode selects per sequence, shared by all heads (MemLong 2.3.2):
+    a stored chunk embedding equal to the query embedding wins, and every head
+    attends the same chunks plus its causal local chunk."""
+    rng = np.random.default_rng(13)
+    Bt, H, n, d, C, nb = 1, 3, 4, 8, 4, 6           # 6 chunks of 4 tokens, last = current chunk
+    N = nb * C
+    E = rng.standard_normal((Bt, 1, nb, 1, 16))
+    rq = E[:, 0, -1, 0, :].copy()
+    E[0, 0, 2, 0, :] = 3.0 * rq[0]                   # chunk 2 points exactly along the query
+    q = np.zeros((Bt, H, n, d))
+    K, V = rng.standard_normal((Bt, H, N, d)), rng.standard_normal((Bt, H, N, d))
+    res = O.step(q, K, V, E, block=C, k=2, sinks=0, window=C, mode="embed", rq=rq)
+    idx = res["idx"][(0, 0)]
+    assert idx[0] == 2 and len(res["idx"]) == 1
+    for h in range(H):
+        for j in range(n):
+            toks = [t for b in idx for t in range(b * C, (b + 1) * C)] + list(range(N - C, N - C + j + 1))
+            assert np.allclose(res["out"][(0, h)][j], V[0, h, toks].mean(axis=0), atol=1e-13)
+
+
+CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_eligible_workloads,
+          check_mean_exact, check_topnorm_bruteforce, check_dot_exact_mips, check_cosine,
+          check_topk_bruteforce, check_topk_ties_and_nan, check_attention_full_causal,
+          check_attention_set_by_zero_query, check_attention_properties, check_gqa_is_replicated_mha,
+          check_planted_recall, check_hand_worked_fixture, check_step_cosine_chunks]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check()
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: every one must be caught by at least one check
+
+
+def _mut_round_trunc(x, dtype):
+    p, emin = O._FMT[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    e = np.maximum(e - 1, emin) - (p - 1)
+    out[fin] = np.ldexp(np.trunc(np.ldexp(x[fin], -e)), e)
+    return out
+
+
+def _mut_round_half_up(x, dtype):
+    p, emin = O._FMT[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    e = np.maximum(e - 1, emin) - (p - 1)
+    out[fin] = np.ldexp(np.floor(np.ldexp(x[fin], -e) + 0.5), e)
+    return out
+
+
+def _mut_elig_floor(N, B, S, W):
+    nb = N // B
+    lo = min(S // B, nb)
+    if N - W <= S:
+        return lo, lo
+    return lo, max(lo, min(nb, (N - W) // B))
+
+
+def _mut_elig_no_guard(N, B, S, W):
+    nb = N // B
+    lo = min(S // B, nb)
+    return lo, max(lo, min(nb, -(-(N - W) // B)))
+
+
+def _mut_mean_div(K, B, dtype):
+    nb = K.shape[0] // B
+    s = K[: nb * B].reshape(nb, B, K.shape[1]).sum(axis=1)
+    return O.round_to_dtype(s / max(B - 1, 1), dtype)[:, None, :]
+
+
+def _mut_mean_unrounded(K, B, dtype):
+    nb = K.shape[0] // B
+    return (K[: nb * B].reshape(nb, B, K.shape[1]).sum(axis=1) / B)[:, None, :]
+
+
+def _mut_topnorm_tie_high(K, B, R):
+    nb = K.shape[0] // B
+    out = np.empty((nb, R, K.shape[1]))
+    for b in range(nb):
+        blk = K[b * B:(b + 1) * B]
+        n2 = (blk * blk).sum(axis=1)
+        order = sorted(range(B), key=lambda t: (-n2[t], -t))
+        out[b] = blk[order[:R]]
+    return out
+
+
+def _mut_topnorm_l1(K, B, R):
+    nb = K.shape[0] // B
+    out = np.empty((nb, R, K.shape[1]))
+    for b in range(nb):
+        blk = K[b * B:(b + 1) * B]
+        n1 = np.abs(blk).sum(axis=1)
+        order = sorted(range(B), key=lambda t: (-n1[t], t))
+        out[b] = blk[order[:R]]
+    return out
+
+
+def _mut_dot_f32_accum(q, reps):
+    return (reps.astype(np.float32) @ q.astype(np.float32)).max(axis=1).astype(np.float32)
+
+
+def _mut_dot_mean_reps(q, reps):
+    return (reps @ q).mean(axis=1).astype(np.float32)
+
+
+def _mut_cos_no_qnorm(rq, E):
+    ne = np.sqrt((E * E).sum(axis=1))
+    s = np.zeros(E.shape[0])
+    ok = ne != 0
+    s[ok] = (E @ rq)[ok] / ne[ok]
+    return s.astype(np.float32)
+
+
+def _mut_topk_tie_high(scores, lo, hi, k):
+    def key(b):
+        s = float(scores[b])
+        return (1, 0.0, -b) if math.isnan(s) else (0, -s, -b)
+
+    order = sorted(range(lo, hi), key=key)[:k]
+    idx = np.full(k, -1, dtype=np.int32)
+    vals = np.full(k, -np.inf, dtype=np.float32)
+    idx[: len(order)] = order
+    vals[: len(order)] = scores[order] if order else []
+    return idx, vals
+
+
+def _mut_topk_nan_first(scores, lo, hi, k):
+    def key(b):
+        s = float(scores[b])
+        return (-1, 0.0, b) if math.isnan(s) else (0, -s, b)
+
+    order = sorted(range(lo, hi), key=key)[:k]
+    idx = np.full(k, -1, dtype=np.int32)
+    vals = np.full(k, -np.inf, dtype=np.float32)
+    idx[: len(order)] = order
+    vals[: len(order)] = scores[order] if order else []
+    return idx, vals
+
+
+def _mut_mask_window_off_by_one(N, B, S, W, idx):
+    T = np.zeros(N, dtype=bool)
+    T[: min(S, N)] = True
+    T[max(N - W + 1, 0):] = True
+    for b in idx:
+        if int(b) >= 0:
+            T[int(b) * B: min((int(b) + 1) * B, N)] = True
+    return T
+
+
+def _mut_mask_block_short(N, B, S, W, idx):
+    T = np.zeros(N, dtype=bool)
+    T[: min(S, N)] = True
+    T[max(N - W, 0):] = True
+    for b in idx:
+        if int(b) >= 0:
+            T[int(b) * B: min((int(b) + 1) * B - 1, N)] = True
+    return T
+
+
+def _mut_attention_no_causal(Q, K, V, T, scale):
+    out = np.empty((Q.shape[0], V.shape[1]))
+    for j in range(Q.shape[0]):
+        if not T.any():
+            raise ValueError
+        z = scale * (K[T] @ Q[j])
+        w = np.exp(z - z.max())
+        out[j] = (w / w.sum()) @ V[T]
+    return out
+
+
+def _mut_attention_no_scale(Q, K, V, T, scale):
+    return _orig_attention(Q, K, V, T, 1.0)
+
+
+def _mut_attention_transposed(Q, K, V, T, scale):
+    n, N = Q.shape[0], K.shape[0]
+    out = np.empty((n, V.shape[1]))
+    pos = np.arange(N)
+    for j in range(n):
+        sel = T & (pos <= N - n + j)
+        if not sel.any():
+            raise ValueError
+        z = scale * (V[sel] @ Q[j])
+        w = np.exp(z - z.max())
+        out[j] = (w / w.sum()) @ K[sel]
+    return out
+
+
+def _mut_attention_query_first(Q, K, V, T, scale):
+    n, N = Q.shape[0], K.shape[0]
+    out = np.empty((n, V.shape[1]))
+    pos = np.arange(N)
+    for j in range(n):
+        sel = T & (pos <= N - 1 - j)  # queries placed in reverse order
+        if not sel.any():
+            raise ValueError
+        z = scale * (K[sel] @ Q[j])
+        w = np.exp(z - z.max())
+        out[j] = (w / w.sum()) @ V[sel]
+    return out
+
+
+def _mut_kv_head_mod(h, Hq, Hkv):
+    return h % Hkv
+
+
+_orig_attention = O.attention
+
+MUTANTS = [
+    ("round_to_dtype", _mut_round_trunc),
+    ("round_to_dtype", _mut_round_half_up),
+    ("eligible_range", _mut_elig_floor),
+    ("eligible_range", _mut_elig_no_guard),
+    ("reps_mean", _mut_mean_div),
+    ("reps_mean", _mut_mean_unrounded),
+    ("reps_topnorm", _mut_topnorm_tie_high),
+    ("reps_topnorm", _mut_topnorm_l1),
+    ("scores_dot_max", _mut_dot_f32_accum),
+    ("scores_dot_max", _mut_dot_mean_reps),
+    ("scores_cosine", _mut_cos_no_qnorm),
+    ("select_topk", _mut_topk_tie_high),
+    ("select_topk", _mut_topk_nan_first),
+    ("attended_mask", _mut_mask_window_off_by_one),
+    ("attended_mask", _mut_mask_block_short),
+    ("attention", _mut_attention_no_causal),
+    ("attention", _mut_attention_no_scale),
+    ("attention", _mut_attention_transposed),
+    ("attention", _mut_attention_query_first),
+    ("kv_head_of", _mut_kv_head_mod),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[f"{n}:{m.__name__}" for n, m in MUTANTS])
+def test_planted_mistakes(monkeypatch, name, mutant):
+    monkeypatch.setattr(O, name, mutant)
+    caught = []
+    for check in CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+    assert caught, f"no check catches the planted mistake {mutant.__name__} in {name}"
