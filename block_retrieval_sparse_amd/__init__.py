@@ -1,0 +1,146 @@
+"""Block-retrieval sparse attention for MI355X (gfx950).
+
+Python face of libbrs: a KV memory with block representatives
+(:class:`KVMemory`), block scoring, exact top-k selection and retrieval
+attention.  Tensors are torch tensors on the GPU; every computation runs in
+the library's HIP kernels on the current torch stream.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import BrsError, REP_MODES, check, lib
+
+__all__ = ["KVMemory", "select_topk", "BrsError", "lib", "version"]
+
+
+def version() -> int:
+    return lib.brs_version()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dt(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return _lib.BRS_F32
+    if dtype == torch.bfloat16:
+        return _lib.BRS_BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class KVMemory:
+    """One layer's block memory: K, V and per-block representatives.
+
+    K and V are ``[batch][n_kv_heads][capacity][row_stride]``; reps are
+    ``[batch][rep_heads][capacity // block][reps_per_block][rep_dim]``.
+    """
+
+    def __init__(self, batch: int, n_kv_heads: int, head_dim: int, capacity: int, block_size: int,
+                 dtype: torch.dtype = torch.bfloat16, rep_mode: str = "mean", reps_per_block: int = 1,
+                 rep_dim: int | None = None, rep_dtype: torch.dtype | None = None,
+                 row_stride: int | None = None, device="cuda"):
+        embed = rep_mode == "embed"
+        rep_dim = rep_dim if rep_dim is not None else head_dim
+        rep_dtype = rep_dtype if rep_dtype is not None else dtype
+        row_stride = row_stride or head_dim
+        rep_heads = 1 if embed else n_kv_heads
+        self.k = torch.zeros((batch, n_kv_heads, capacity, row_stride), dtype=dtype, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.reps = torch.zeros((batch, rep_heads, capacity // block_size, reps_per_block, rep_dim),
+                                dtype=rep_dtype, device=device)
+        self.desc = _lib.brs_memory(
+            dtype=_dt(dtype), batch=batch, n_kv_heads=n_kv_heads, head_dim=head_dim, row_stride=row_stride,
+            block_size=block_size, reps_per_block=reps_per_block, rep_dim=rep_dim, rep_heads=rep_heads,
+            rep_mode=REP_MODES[rep_mode], rep_dtype=_dt(rep_dtype), reserved=0, capacity=capacity, length=0,
+            k=self.k.data_ptr(), v=self.v.data_ptr(), reps=self.reps.data_ptr())
+        check(lib.brs_memory_check(self.desc))
+        self.dtype, self.rep_mode, self.block_size = dtype, rep_mode, block_size
+        self.batch, self.n_kv_heads, self.head_dim = batch, n_kv_heads, head_dim
+
+    @property
+    def length(self) -> int:
+        return self.desc.length
+
+    @property
+    def n_blocks(self) -> int:
+        return self.length // self.block_size
+
+    @property
+    def blocks_stride(self) -> int:
+        return self.reps.shape[2]
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, reps_new: torch.Tensor | None = None,
+               stream=None) -> None:
+        """Append ``[batch][n_kv_heads][n][head_dim]`` K/V rows (contiguous)."""
+        k_new, v_new = k_new.contiguous(), v_new.contiguous()
+        if reps_new is not None:
+            reps_new = reps_new.contiguous()
+        n = k_new.shape[2]
+        check(lib.brs_mem_append(self.desc, k_new.data_ptr(), v_new.data_ptr(), n, _ptr(reps_new),
+                                 _stream(stream)))
+
+    def eligible_range(self, n_sink: int, window: int) -> tuple[int, int]:
+        lo, hi = _lib.c_int64(), _lib.c_int64()
+        check(lib.brs_eligible_range(self.desc, n_sink, window, lo, hi))
+        return lo.value, hi.value
+
+    def score_blocks(self, qrep: torch.Tensor, lo: int, hi: int, scores: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+        """Dot-max scores ``[batch][Hq][blocks]`` from q ``[batch][Hq][d]``, or
+        cosine scores ``[batch][1][blocks]`` from ``[batch][rep_dim]`` (embed mode)."""
+        qrep = qrep.contiguous()
+        hs = 1 if self.rep_mode == "embed" else qrep.shape[1]
+        if scores is None:
+            scores = torch.full((self.batch, hs, self.blocks_stride), float("nan"), dtype=torch.float32,
+                                device=qrep.device)
+        check(lib.brs_score_blocks(self.desc, qrep.data_ptr(), hs, lo, hi, scores.data_ptr(), _stream(stream)))
+        return scores
+
+    def workspace_bytes(self, n_q_heads: int, n_q: int, idx_heads: int, k: int, n_sink: int, window: int) -> int:
+        n = _lib.c_size_t()
+        check(lib.brs_attention_workspace_bytes(self.desc, n_q_heads, n_q, idx_heads, k, n_sink, window, n))
+        return n.value
+
+    def retrieval_attention(self, q: torch.Tensor, idx: torch.Tensor | None, n_sink: int, window: int,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """q ``[batch][Hq][n_q][d]``, idx ``[batch][1 or Hq][k]`` int32 -> fp32 ``[batch][Hq][n_q][d]``."""
+        q = q.contiguous()
+        bt, hq, n_q, d = q.shape
+        if idx is None:
+            idx_heads, k, iptr = 1, 0, None
+        else:
+            idx = idx.contiguous()
+            idx_heads, k, iptr = idx.shape[1], idx.shape[2], idx.data_ptr()
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        nbytes = self.workspace_bytes(hq, n_q, idx_heads, k, n_sink, window)
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty((bt, hq, n_q, d), dtype=torch.float32, device=q.device)
+        check(lib.brs_retrieval_attention(self.desc, q.data_ptr(), hq, n_q, iptr, idx_heads, k, n_sink, window,
+                                          scale, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                          _stream(stream)))
+        return out
+
+
+def select_topk(scores: torch.Tensor, lo: int, hi: int, k: int, want_vals: bool = True, stream=None):
+    """Top-k over columns [lo, hi) of ``[batch][heads][stride]`` fp32 scores.
+
+    Returns (idx int32 ``[batch][heads][k]``, vals or None)."""
+    bt, h, stride = scores.shape
+    idx = torch.empty((bt, h, k), dtype=torch.int32, device=scores.device)
+    vals = torch.empty((bt, h, k), dtype=torch.float32, device=scores.device) if want_vals else None
+    check(lib.brs_select_topk(scores.data_ptr(), bt, h, stride, lo, hi, k, idx.data_ptr(), _ptr(vals),
+                              _stream(stream)))
+    return idx, vals

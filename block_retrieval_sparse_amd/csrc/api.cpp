@@ -1,0 +1,268 @@
+// C-ABI entry points of libbrs: argument validation on the host, then kernel
+// launches on the caller's stream.  No call allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "brs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BRS_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(BRS_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_memory(const brs_memory* m) {
+  if (!m) return fail(BRS_E_INVAL, "memory descriptor is NULL");
+  if (m->dtype != BRS_F32 && m->dtype != BRS_BF16) return fail(BRS_E_INVAL, "dtype %d", m->dtype);
+  if (m->rep_dtype != BRS_F32 && m->rep_dtype != BRS_BF16)
+    return fail(BRS_E_INVAL, "rep_dtype %d", m->rep_dtype);
+  if (m->rep_mode < BRS_REP_MEAN || m->rep_mode > BRS_REP_EMBED)
+    return fail(BRS_E_INVAL, "rep_mode %d", m->rep_mode);
+  if (m->reserved != 0) return fail(BRS_E_INVAL, "reserved field must be 0");
+  if (m->batch < 1 || m->n_kv_heads < 1 || m->head_dim < 1 || m->block_size < 1 ||
+      m->reps_per_block < 1 || m->rep_dim < 1 || m->rep_heads < 1)
+    return fail(BRS_E_INVAL, "sizes must be >= 1");
+  if (m->row_stride < m->head_dim) return fail(BRS_E_INVAL, "row_stride < head_dim");
+  if ((m->row_stride * brs::elem_bytes(m->dtype)) % 4 != 0)
+    return fail(BRS_E_INVAL, "row_stride * element size must be a multiple of 4 bytes");
+  if (m->capacity < 0 || m->capacity > INT32_MAX) return fail(BRS_E_INVAL, "capacity out of range");
+  if (m->length < 0 || m->length > m->capacity) return fail(BRS_E_INVAL, "length out of range");
+  const bool embed = m->rep_mode == BRS_REP_EMBED;
+  if (m->rep_heads != (embed ? 1 : m->n_kv_heads))
+    return fail(BRS_E_INVAL, "rep_heads must be %d for this rep_mode", embed ? 1 : m->n_kv_heads);
+  if (!embed && (m->rep_dim != m->head_dim || m->rep_dtype != m->dtype))
+    return fail(BRS_E_INVAL, "rep_dim/rep_dtype must equal head_dim/dtype unless rep_mode is EMBED");
+  if ((m->rep_mode == BRS_REP_MEAN || embed) && m->reps_per_block != 1)
+    return fail(BRS_E_INVAL, "reps_per_block must be 1 for MEAN and EMBED");
+  if (m->rep_mode == BRS_REP_TOPNORM && (m->reps_per_block > m->block_size || m->reps_per_block > 64))
+    return fail(BRS_E_INVAL, "TOPNORM needs reps_per_block <= min(block_size, 64)");
+  if (m->rep_mode == BRS_REP_TOPNORM && m->block_size > 1024)
+    return fail(BRS_E_UNSUPPORTED, "TOPNORM supports block_size <= 1024");
+  if (!m->k || !m->v || !m->reps) return fail(BRS_E_INVAL, "k, v and reps must be non-NULL");
+  if (!aligned(m->k, 16) || !aligned(m->v, 16) || !aligned(m->reps, 16))
+    return fail(BRS_E_INVAL, "k, v and reps must be 16-byte aligned");
+  return BRS_OK;
+}
+
+void eligible(int64_t N, int64_t B, int64_t S, int64_t W, int64_t* lo, int64_t* hi) {
+  // Tokens outside the sinks and the window are [S, N - W); block b meets
+  // them iff floor(S/B) <= b < ceil((N-W)/B); it must also be complete.
+  const int64_t nb = N / B;
+  int64_t l = S / B;
+  if (l > nb) l = nb;
+  int64_t h = l;
+  if (N - W > S) {
+    h = (N - W + B - 1) / B;
+    if (h > nb) h = nb;
+    if (h < l) h = l;
+  }
+  *lo = l;
+  *hi = h;
+}
+
+}  // namespace
+
+extern "C" {
+
+int brs_version(void) { return BRS_VERSION; }
+
+const char* brs_last_error(void) { return g_err; }
+
+int brs_memory_check(const brs_memory* m) {
+  int rc = check_memory(m);
+  return rc ? rc : ok();
+}
+
+int brs_eligible_range(const brs_memory* m, int64_t n_sink, int64_t window, int64_t* lo,
+                       int64_t* hi) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (n_sink < 0 || window < 0) return fail(BRS_E_INVAL, "n_sink and window must be >= 0");
+  if (!lo || !hi) return fail(BRS_E_INVAL, "lo/hi must be non-NULL");
+  eligible(m->length, m->block_size, n_sink, window, lo, hi);
+  return ok();
+}
+
+int brs_mem_append(brs_memory* m, const void* k_new, const void* v_new, int64_t n_new,
+                   const void* reps_new, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (n_new < 0) return fail(BRS_E_INVAL, "n_new < 0");
+  if (n_new == 0) return ok();
+  if (m->length + n_new > m->capacity)
+    return fail(BRS_E_CAPACITY, "length %lld + n_new %lld > capacity %lld", (long long)m->length,
+                (long long)n_new, (long long)m->capacity);
+  if (!k_new || !v_new) return fail(BRS_E_INVAL, "k_new/v_new must be non-NULL");
+  const int es = brs::elem_bytes(m->dtype);
+  if (!aligned(k_new, es) || !aligned(v_new, es)) return fail(BRS_E_INVAL, "k_new/v_new misaligned");
+  const int64_t b0 = m->length / m->block_size;
+  const int64_t b1 = (m->length + n_new) / m->block_size;
+  const bool given = m->rep_mode == BRS_REP_GIVEN || m->rep_mode == BRS_REP_EMBED;
+  if (given && b1 > b0 && !reps_new)
+    return fail(BRS_E_INVAL, "reps_new required: this append completes %lld block(s)", (long long)(b1 - b0));
+  if (given && b1 > b0 && !aligned(reps_new, brs::elem_bytes(m->rep_dtype)))
+    return fail(BRS_E_INVAL, "reps_new misaligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = brs::launch_kv_append(*m, k_new, v_new, n_new, s);
+  if (e != hipSuccess) return hip_fail(e, "kv_append");
+  if (b1 > b0) {
+    brs_memory after = *m;
+    after.length = m->length + n_new;
+    e = brs::launch_rep_build(after, b0, b1, reps_new, s);
+    if (e != hipSuccess) return hip_fail(e, "rep_build");
+  }
+  m->length += n_new;
+  return ok();
+}
+
+int brs_score_blocks(const brs_memory* m, const void* qrep, int32_t n_score_heads, int64_t lo,
+                     int64_t hi, float* scores, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  const int64_t nb = m->length / m->block_size;
+  if (lo < 0 || hi < lo || hi > nb)
+    return fail(BRS_E_INVAL, "need 0 <= lo <= hi <= %lld (complete blocks)", (long long)nb);
+  if (!qrep || !scores) return fail(BRS_E_INVAL, "qrep/scores must be non-NULL");
+  if (!aligned(scores, 4)) return fail(BRS_E_INVAL, "scores misaligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (m->rep_mode == BRS_REP_EMBED) {
+    if (n_score_heads != 1) return fail(BRS_E_INVAL, "cosine scoring has one score head per sequence");
+    if (!aligned(qrep, brs::elem_bytes(m->rep_dtype))) return fail(BRS_E_INVAL, "qrep misaligned");
+    if (hi == lo) return ok();
+    hipError_t e = brs::launch_score_cosine(*m, qrep, lo, hi, scores, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "score_cosine");
+  }
+  if (n_score_heads < 1 || n_score_heads % m->n_kv_heads != 0)
+    return fail(BRS_E_INVAL, "n_score_heads must be a positive multiple of n_kv_heads");
+  if (n_score_heads / m->n_kv_heads > 32) return fail(BRS_E_UNSUPPORTED, "more than 32 query heads per kv head");
+  if (!aligned(qrep, brs::elem_bytes(m->dtype))) return fail(BRS_E_INVAL, "q misaligned");
+  if (hi == lo) return ok();
+  hipError_t e = brs::launch_score_dot(*m, qrep, n_score_heads, lo, hi, scores, s);
+  return e == hipSuccess ? ok() : hip_fail(e, "score_dot");
+}
+
+int brs_select_topk(const float* scores, int32_t batch, int32_t n_heads, int64_t blocks_stride,
+                    int64_t lo, int64_t hi, int32_t k, int32_t* idx, float* vals, void* stream) {
+  if (!scores || !idx) return fail(BRS_E_INVAL, "scores/idx must be non-NULL");
+  if (batch < 1 || n_heads < 1) return fail(BRS_E_INVAL, "batch and n_heads must be >= 1");
+  if (k < 1 || k > 2048) return fail(BRS_E_UNSUPPORTED, "k must be in [1, 2048]");
+  if (lo < 0 || hi < lo || hi > blocks_stride) return fail(BRS_E_INVAL, "need 0 <= lo <= hi <= blocks_stride");
+  if (hi - lo > (1 << 20)) return fail(BRS_E_UNSUPPORTED, "more than 2^20 candidates");
+  if (!aligned(scores, 4) || !aligned(idx, 4) || (vals && !aligned(vals, 4)))
+    return fail(BRS_E_INVAL, "misaligned pointer");
+  hipError_t e = brs::launch_select_topk(scores, batch, n_heads, blocks_stride, lo, hi, k, idx, vals,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "select_topk");
+}
+
+static int attn_setup(const brs_memory* m, int32_t n_q_heads, int32_t n_q, int32_t idx_heads, int32_t k,
+                      int64_t n_sink, int64_t window, float scale, brs::AttnGeom& g) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (n_q_heads < 1 || n_q_heads % m->n_kv_heads != 0)
+    return fail(BRS_E_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q < 1 || n_q > m->length) return fail(BRS_E_INVAL, "need 1 <= n_q <= length");
+  if (idx_heads != 1 && idx_heads != n_q_heads) return fail(BRS_E_INVAL, "idx_heads must be 1 or n_q_heads");
+  if (k < 0) return fail(BRS_E_INVAL, "k < 0");
+  if (n_sink < 0 || window < 0) return fail(BRS_E_INVAL, "n_sink and window must be >= 0");
+  if (!isfinite(scale)) return fail(BRS_E_INVAL, "scale must be finite");
+  if (n_sink == 0 && window == 0 && k == 0) return fail(BRS_E_EMPTY, "no sinks, no window and k = 0");
+  const int G = n_q_heads / m->n_kv_heads;
+  if (G > 32) return fail(BRS_E_UNSUPPORTED, "more than 32 query heads per kv head");
+  g = brs::AttnGeom{};
+  g.batch = m->batch;
+  g.hq = n_q_heads;
+  g.hkv = m->n_kv_heads;
+  g.group = G;
+  g.n_q = n_q;
+  g.d = m->head_dim;
+  g.row_stride = m->row_stride;
+  g.dtype = m->dtype;
+  g.N = (int)m->length;
+  g.B = m->block_size;
+  g.nb = (int)(m->length / m->block_size);
+  const int64_t S = n_sink < m->length ? n_sink : m->length;
+  g.sink_end = (int)S;
+  const int64_t ws = m->length - window;
+  g.win_start = (int)(ws > S ? ws : S);
+  g.idx_heads = idx_heads;
+  g.k = k;
+  g.head_stride = m->capacity * (int64_t)m->row_stride;
+  g.qscale = scale * 1.4426950408889634f;
+  if (!brs::attn_geometry(g)) return fail(BRS_E_UNSUPPORTED, "attention shape not supported");
+  return BRS_OK;
+}
+
+int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_t n_q,
+                                  int32_t idx_heads, int32_t k, int64_t n_sink, int64_t window,
+                                  size_t* bytes) {
+  if (!bytes) return fail(BRS_E_INVAL, "bytes must be non-NULL");
+  *bytes = 0;
+  brs::AttnGeom g;
+  int rc = attn_setup(m, n_q_heads, n_q, idx_heads, k, n_sink, window, 1.0f, g);
+  if (rc) return rc;
+  *bytes = g.total;
+  return ok();
+}
+
+int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
+                            const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
+                            int64_t window, float scale, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  brs::AttnGeom g;
+  int rc = attn_setup(m, n_q_heads, n_q, idx_heads, k, n_sink, window, scale, g);
+  if (rc) return rc;
+  if (!q || !out) return fail(BRS_E_INVAL, "q/out must be non-NULL");
+  if (k > 0 && !idx) return fail(BRS_E_INVAL, "idx must be non-NULL when k > 0");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(BRS_E_INVAL, "q/out must be 16-byte aligned");
+  if (idx && !aligned(idx, 4)) return fail(BRS_E_INVAL, "idx misaligned");
+  if (!workspace || workspace_bytes < g.total)
+    return fail(BRS_E_WORKSPACE, "workspace of %zu bytes needed", g.total);
+  if (!aligned(workspace, 256)) return fail(BRS_E_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  hipError_t e = brs::launch_attn_plan(g, idx, workspace, s);
+  if (e != hipSuccess) return hip_fail(e, "attn_plan");
+  if (brs::prefill_supported(g)) {
+    e = brs::launch_attn_prefill(g, m->k, m->v, q, idx, out, s, e0, e1);
+    if (e != hipSuccess) return hip_fail(e, "attn_prefill");
+    return ok();
+  }
+  e = brs::launch_attn_split(g, m->k, m->v, q, workspace, s, e0, e1);
+  if (e != hipSuccess) return hip_fail(e, "attn_split");
+  e = brs::launch_attn_merge(g, workspace, out, s);
+  if (e != hipSuccess) return hip_fail(e, "attn_merge");
+  return ok();
+}
+
+int brs_profile_next_attention(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(BRS_E_INVAL, "pass both events or neither");
+  g_prof_start = (hipEvent_t)start_event;
+  g_prof_stop = (hipEvent_t)stop_event;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal declarations shared by the HIP translation units of libbrs.
+// Nothing here crosses the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "brs.h"
+
+namespace brs {
+
+// ---------------------------------------------------------------------------
+// element helpers
+
+__host__ __device__ inline int elem_bytes(int dtype) { return dtype == BRS_F32 ? 4 : 2; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round a float64 to the nearest bfloat16, ties to even, in one step (no
+// intermediate float32 rounding).  Finite, normal-range inputs; values in
+// the subnormal range use the fixed subnormal spacing.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  if (x == 0.0 || !isfinite(x)) {
+    return (uint16_t)(__float_as_uint((float)x) >> 16);
+  }
+  int e;
+  frexp(x, &e);                 // x = m 2^e, 0.5 <= |m| < 1
+  int binade = e - 1;
+  if (binade < -126) binade = -126;
+  const int sp = binade - 7;    // spacing exponent for 8 significant bits
+  double r = ldexp(rint(ldexp(x, -sp)), sp);   // exact, representable in bf16
+  float f = (float)r;           // exact conversion (or overflow to inf)
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// Inclusive prefix sum of one int per thread over the whole workgroup
+// (blockDim.x a multiple of 64, at most 1024).  Contains barriers: every
+// thread of the workgroup must call it.
+__device__ inline int block_inclusive_scan(int v, int* wave_tot /* [16] shared */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += wave_tot[w];
+  __syncthreads();
+  return v + add;
+}
+
+// ---------------------------------------------------------------------------
+// attention plan
+//
+// For every (batch, kv head) the plan kernel writes a list of work items.
+// An item is a contiguous span of token rows that some of the group's query
+// heads attend: (first row, token count, head mask).  Items never overlap,
+// so every attended token is visited once per (batch, kv head) no matter how
+// many query heads selected its block (the K/V bytes of a block shared by
+// several heads are read once).  Item 0 of each list is a header holding the
+// item count.
+
+constexpr int kItemTokens = 128;   // longest item
+constexpr int kMarkBlocks = 8192;  // blocks marked per pass of the plan kernel
+constexpr int kRowsMax = 8;        // query rows one split workgroup handles
+
+struct AttnGeom {
+  int batch, hq, hkv, group, n_q, d, row_stride, dtype;
+  int N, B, nb;
+  int sink_end;           // S' = min(n_sink, N)
+  int win_start;          // max(N - window, S')
+  int idx_heads, k;
+  int64_t head_stride;    // elements between consecutive (batch, kv head) slices of k / v
+  float qscale;           // softmax scale * log2(e)
+  // decomposition
+  int64_t max_items;
+  int nw;                 // waves per split workgroup
+  int ipw;                // items per split workgroup
+  int max_chunks;         // split workgroups per (batch, kv head)
+  int row_groups;         // ceil(group * n_q / kRowsMax)
+  int rows_per_group;
+  // workspace offsets (bytes)
+  size_t plan_off, ml_off, o_off, total;
+};
+
+// Fills the decomposition and workspace layout; returns false if unsupported.
+bool attn_geometry(AttnGeom& g);
+
+hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, hipStream_t s);
+hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
+                             hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q,
+                               const int32_t* idx, float* out, hipStream_t s, hipEvent_t ev0,
+                               hipEvent_t ev1);
+bool prefill_supported(const AttnGeom& g);
+
+// ---------------------------------------------------------------------------
+// memory, scores, selection
+
+hipError_t launch_kv_append(const brs_memory& m, const void* k_new, const void* v_new, int64_t n_new,
+                            hipStream_t s);
+hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new,
+                            hipStream_t s);
+hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi,
+                            float* scores, hipStream_t s);
+hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, int64_t hi,
+                               float* scores, hipStream_t s);
+hipError_t launch_select_topk(const float* scores, int batch, int heads, int64_t stride, int64_t lo,
+                              int64_t hi, int k, int32_t* idx, float* vals, hipStream_t s);
+
+}  // namespace brs

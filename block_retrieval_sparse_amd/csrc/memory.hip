@@ -1,0 +1,201 @@
+// Memory write path: copy new K/V rows into the block-contiguous memory and
+// build the representatives of every block an append completes (MemLong
+// 2.3.2 memorisation: K-V pairs stored with their index-aligned
+// representation; InfLLM "method": a few tokens stand for each memory unit;
+// Landmark Attention "proposed method": one landmark key per block).
+#include "brs_internal.h"
+
+namespace brs {
+namespace {
+
+// ---------------------------------------------------------------------------
+// K/V append: rows of head_dim elements into rows of row_stride elements,
+// padding columns set to zero.  U is the copy unit (16, 4 or 2 bytes).
+
+template <typename U>
+__global__ __launch_bounds__(256) void kv_append_kernel(const U* __restrict__ ksrc, const U* __restrict__ vsrc,
+                                                        U* __restrict__ kdst, U* __restrict__ vdst,
+                                                        int64_t rows, int hkv, int64_t n_new, int64_t cap,
+                                                        int64_t len, int src_units, int dst_units) {
+  const int64_t total = rows * dst_units;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / dst_units;
+    const int u = (int)(i - r * dst_units);
+    const int64_t t = r % n_new;
+    const int64_t bg = r / n_new;  // batch * hkv + head
+    const int64_t dst = ((bg * cap) + len + t) * dst_units + u;
+    U kv{}, vv{};
+    if (u < src_units) {
+      kv = ksrc[r * src_units + u];
+      vv = vsrc[r * src_units + u];
+    }
+    kdst[dst] = kv;
+    vdst[dst] = vv;
+  }
+  (void)hkv;
+}
+
+// ---------------------------------------------------------------------------
+// MEAN: rep = RNE_dtype( (sum of the block's keys in float64) / B ).
+
+template <typename T>
+__device__ __forceinline__ double load_as_f64(const T* p);
+template <>
+__device__ __forceinline__ double load_as_f64<float>(const float* p) { return (double)*p; }
+template <>
+__device__ __forceinline__ double load_as_f64<uint16_t>(const uint16_t* p) { return (double)bf16_to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ void store_rounded(T* p, double x);
+template <>
+__device__ __forceinline__ void store_rounded<float>(float* p, double x) { *p = (float)x; }
+template <>
+__device__ __forceinline__ void store_rounded<uint16_t>(uint16_t* p, double x) { *p = f64_to_bf16_rne(x); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void rep_mean_kernel(const T* __restrict__ K, T* __restrict__ reps, int64_t b0,
+                                                       int B, int d, int rs, int64_t cap, int64_t capB) {
+  const int64_t blk = b0 + blockIdx.x;
+  const int64_t bg = blockIdx.y;
+  const T* base = K + (bg * cap + blk * B) * (int64_t)rs;
+  T* dst = reps + (bg * capB + blk) * (int64_t)d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    double s = 0.0;
+    for (int t = 0; t < B; ++t) s += load_as_f64(base + (int64_t)t * rs + c);
+    store_rounded(dst + c, s / (double)B);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// TOPNORM: the R keys with the largest squared norm (float64 sums), ties to
+// the lower token, copied unchanged in that order.
+
+template <typename T>
+__global__ __launch_bounds__(256) void rep_topnorm_kernel(const T* __restrict__ K, T* __restrict__ reps,
+                                                          int64_t b0, int B, int R, int d, int rs, int64_t cap,
+                                                          int64_t capB) {
+  __shared__ double n2[1024];
+  __shared__ int chosen[64];
+  const int64_t blk = b0 + blockIdx.x;
+  const int64_t bg = blockIdx.y;
+  const T* base = K + (bg * cap + blk * B) * (int64_t)rs;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  if (threadIdx.x < R) chosen[threadIdx.x] = threadIdx.x;  // every slot names a valid token even for NaN norms
+  for (int t = wave; t < B; t += nwaves) {
+    double s = 0.0;
+    for (int c = lane; c < d; c += 64) {
+      const double x = load_as_f64(base + (int64_t)t * rs + c);
+      s = fma(x, x, s);
+    }
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) n2[t] = s;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += blockDim.x) {
+    const double mine = n2[t];
+    int rank = 0;
+    for (int u = 0; u < B; ++u) {
+      const double o = n2[u];
+      rank += (o > mine) || (o == mine && u < t);
+    }
+    if (rank < R) chosen[rank] = t;  // ranks are distinct for finite norms
+  }
+  __syncthreads();
+  T* dst = reps + (bg * capB + blk) * (int64_t)R * d;
+  for (int i = threadIdx.x; i < R * d; i += blockDim.x) {
+    const int r = i / d, c = i - r * d;
+    dst[i] = base[(int64_t)chosen[r] * rs + c];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GIVEN / EMBED: copy the caller's vectors into the block slots.
+
+template <typename T>
+__global__ __launch_bounds__(256) void rep_copy_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t per_head,
+                                                       int64_t heads, int64_t head_stride, int64_t dst_off) {
+  const int64_t total = per_head * heads;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t h = i / per_head, e = i - h * per_head;
+    dst[h * head_stride + dst_off + e] = src[i];
+  }
+}
+
+int grid_for(int64_t work) {
+  int64_t g = (work + 255) / 256;
+  if (g > 65536) g = 65536;
+  return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const brs_memory& m, const void* k_new, const void* v_new, int64_t n_new,
+                            hipStream_t s) {
+  const int es = elem_bytes(m.dtype);
+  const int64_t rows = (int64_t)m.batch * m.n_kv_heads * n_new;
+  const int src_bytes = m.head_dim * es, dst_bytes = m.row_stride * es;
+  auto al = [](const void* p, int a) { return ((uintptr_t)p % a) == 0; };
+  if (src_bytes % 16 == 0 && dst_bytes % 16 == 0 && al(k_new, 16) && al(v_new, 16)) {
+    hipLaunchKernelGGL(kv_append_kernel<uint4>, dim3(grid_for(rows * (dst_bytes / 16))), dim3(256), 0, s,
+                       (const uint4*)k_new, (const uint4*)v_new, (uint4*)m.k, (uint4*)m.v, rows, m.n_kv_heads,
+                       n_new, m.capacity, m.length, src_bytes / 16, dst_bytes / 16);
+  } else if (src_bytes % 4 == 0 && al(k_new, 4) && al(v_new, 4)) {
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3(grid_for(rows * (dst_bytes / 4))), dim3(256), 0, s,
+                       (const uint32_t*)k_new, (const uint32_t*)v_new, (uint32_t*)m.k, (uint32_t*)m.v, rows,
+                       m.n_kv_heads, n_new, m.capacity, m.length, src_bytes / 4, dst_bytes / 4);
+  } else {
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(grid_for(rows * (dst_bytes / 2))), dim3(256), 0, s,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)m.k, (uint16_t*)m.v, rows,
+                       m.n_kv_heads, n_new, m.capacity, m.length, src_bytes / 2, dst_bytes / 2);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new, hipStream_t s) {
+  const int64_t nblk = b1 - b0;
+  const int64_t capB = m.capacity / m.block_size;
+  const int64_t heads = (int64_t)m.batch * m.rep_heads;
+  if (m.rep_mode == BRS_REP_GIVEN || m.rep_mode == BRS_REP_EMBED) {
+    const int64_t per_block = (int64_t)m.reps_per_block * m.rep_dim;
+    const int64_t per_head = nblk * per_block;
+    if (m.rep_dtype == BRS_F32)
+      hipLaunchKernelGGL(rep_copy_kernel<float>, dim3(grid_for(per_head * heads)), dim3(256), 0, s,
+                         (const float*)reps_new, (float*)m.reps, per_head, heads, capB * per_block,
+                         b0 * per_block);
+    else
+      hipLaunchKernelGGL(rep_copy_kernel<uint16_t>, dim3(grid_for(per_head * heads)), dim3(256), 0, s,
+                         (const uint16_t*)reps_new, (uint16_t*)m.reps, per_head, heads, capB * per_block,
+                         b0 * per_block);
+    return hipGetLastError();
+  }
+  // the grid's y dimension covers (batch, kv head); x covers the new blocks
+  for (int64_t done = 0; done < nblk; done += 65535) {
+    const int64_t n = nblk - done < 65535 ? nblk - done : 65535;
+    const dim3 grid((unsigned)n, (unsigned)heads);
+    if (m.rep_mode == BRS_REP_MEAN) {
+      if (m.dtype == BRS_F32)
+        hipLaunchKernelGGL(rep_mean_kernel<float>, grid, dim3(128), 0, s, (const float*)m.k, (float*)m.reps,
+                           b0 + done, m.block_size, m.head_dim, m.row_stride, m.capacity, capB);
+      else
+        hipLaunchKernelGGL(rep_mean_kernel<uint16_t>, grid, dim3(128), 0, s, (const uint16_t*)m.k,
+                           (uint16_t*)m.reps, b0 + done, m.block_size, m.head_dim, m.row_stride, m.capacity,
+                           capB);
+    } else {
+      if (m.dtype == BRS_F32)
+        hipLaunchKernelGGL(rep_topnorm_kernel<float>, grid, dim3(256), 0, s, (const float*)m.k, (float*)m.reps,
+                           b0 + done, m.block_size, m.reps_per_block, m.head_dim, m.row_stride, m.capacity,
+                           capB);
+      else
+        hipLaunchKernelGGL(rep_topnorm_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)m.k,
+                           (uint16_t*)m.reps, b0 + done, m.block_size, m.reps_per_block, m.head_dim,
+                           m.row_stride, m.capacity, capB);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace brs

@@ -1,0 +1,250 @@
+// Block scoring (Landmark Attention "proposed method": query-landmark
+// similarity; InfLLM "method": block-level relevance instead of token-level;
+// MemLong 2.3.2: cosine similarity of chunk embeddings).
+//
+// Scores are exact: every product of two stored values is exact in float64
+// and the sums are float64, rounded once to float32 at the end, so the
+// result does not depend on how lanes split the sum.
+//
+// Dot-max layout: one workgroup streams a range of blocks of one
+// (batch, kv head); each block's R representatives are contiguous rows, read
+// once and dotted with all G query heads of the group (grouped-query sharing:
+// the representative bytes are read once per kv head, not once per query
+// head).  L lanes share one row (16-byte loads, coalesced); each lane holds
+// its slice of the G queries in float64 registers.
+#include "brs_internal.h"
+
+namespace brs {
+namespace {
+
+template <typename T>
+struct Vec;  // 16-byte unit of T
+template <>
+struct Vec<uint16_t> {
+  static constexpr int n = 8;
+  __device__ static void to_f64(const uint4& u, double* out) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = (double)bf16_lo(w[i]);
+      out[2 * i + 1] = (double)bf16_hi(w[i]);
+    }
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int n = 4;
+  __device__ static void to_f64(const uint4& u, double* out) {
+    out[0] = (double)__uint_as_float(u.x);
+    out[1] = (double)__uint_as_float(u.y);
+    out[2] = (double)__uint_as_float(u.z);
+    out[3] = (double)__uint_as_float(u.w);
+  }
+};
+
+__device__ __forceinline__ double nan_max(double a, double b) {
+  // max that keeps NaN (a NaN representative dot makes the block score NaN)
+  return (b > a || b != b) ? b : a;
+}
+
+template <typename T>
+__device__ __forceinline__ double elem_f64(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ double elem_f64<float>(const float* p, int64_t i) { return (double)p[i]; }
+template <>
+__device__ __forceinline__ double elem_f64<uint16_t>(const uint16_t* p, int64_t i) {
+  return (double)bf16_to_f32(p[i]);
+}
+
+// EPL: elements per lane (EPL * sizeof(T) is a multiple of 16 bytes).
+// L = d / EPL lanes per row.  G: query heads per kv head.
+template <typename T, int EPL, int G>
+__global__ __launch_bounds__(256) void score_dot_kernel(const T* __restrict__ q, const T* __restrict__ reps,
+                                                        float* __restrict__ scores, int d, int R, int hkv,
+                                                        int64_t capB, int64_t lo, int64_t hi, int bps) {
+  constexpr int UPL = EPL / Vec<T>::n;  // 16-byte units per lane
+  const int L = d / EPL;
+  const int lane = threadIdx.x & 63;
+  const int slot_in_wave = lane / L, sub = lane - slot_in_wave * L;
+  const int slots_per_wave = 64 / L;
+  const int slot = (threadIdx.x >> 6) * slots_per_wave + slot_in_wave;
+  const int slots = (blockDim.x >> 6) * slots_per_wave;
+  const int bg = blockIdx.y;
+  const int b = bg / hkv, g = bg - b * hkv;
+  const int hq = hkv * G;
+
+  double qd[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const T* qrow = q + ((int64_t)b * hq + g * G + j) * d + sub * EPL;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + u * Vec<T>::n);
+      Vec<T>::to_f64(raw, &qd[j][u * Vec<T>::n]);
+    }
+  }
+
+  const T* rbase = reps + ((int64_t)bg * capB) * R * d + sub * EPL;
+  float* sbase = scores + ((int64_t)b * hq + g * G) * capB;
+  const int64_t tile0 = lo + (int64_t)blockIdx.x * slots * bps;
+  for (int i = 0; i < bps; ++i) {
+    const int64_t blk = tile0 + (int64_t)i * slots + slot;
+    const bool valid = blk < hi;
+    double best[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) best[j] = -INFINITY;
+    for (int r = 0; r < R; ++r) {
+      uint4 raw[UPL];
+#pragma unroll
+      for (int u = 0; u < UPL; ++u)
+        raw[u] = valid ? *reinterpret_cast<const uint4*>(rbase + (blk * R + r) * d + u * Vec<T>::n)
+                       : make_uint4(0, 0, 0, 0);
+      double x[EPL];
+#pragma unroll
+      for (int u = 0; u < UPL; ++u) Vec<T>::to_f64(raw[u], &x[u * Vec<T>::n]);
+      double acc[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        double a = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fma(qd[j][e], x[e], a);
+        acc[j] = a;
+      }
+      for (int off = 1; off < L; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc[j] += __shfl_xor(acc[j], off);
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) best[j] = nan_max(best[j], acc[j]);
+    }
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)best[j];
+    }
+  }
+}
+
+// Any shape: one wave per block, lanes stride over the elements, up to 32
+// query heads per kv head.
+template <typename T>
+__global__ __launch_bounds__(256) void score_dot_generic_kernel(const T* __restrict__ q, const T* __restrict__ reps,
+                                                                float* __restrict__ scores, int d, int R, int hkv,
+                                                                int G, int64_t capB, int64_t lo, int64_t hi) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = lo + (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (blk >= hi) return;
+  const int bg = blockIdx.y;
+  const int b = bg / hkv, g = bg - b * hkv;
+  const int hq = hkv * G;
+  const T* rrow = reps + ((int64_t)bg * capB + blk) * R * d;
+  for (int j = 0; j < G; ++j) {
+    const T* qrow = q + ((int64_t)b * hq + g * G + j) * d;
+    double best = -INFINITY;
+    for (int r = 0; r < R; ++r) {
+      double a = 0.0;
+      for (int e = lane; e < d; e += 64) a = fma(elem_f64(qrow, e), elem_f64(rrow + (int64_t)r * d, e), a);
+      for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off);
+      best = nan_max(best, a);
+    }
+    if (lane == 0) scores[((int64_t)b * hq + g * G + j) * capB + blk] = (float)best;
+  }
+}
+
+// Cosine (one score head per sequence): s = q.e / (sqrt(q.q) sqrt(e.e)),
+// float64 throughout, 0 if either norm is 0.
+template <typename T>
+__global__ __launch_bounds__(256) void score_cosine_kernel(const T* __restrict__ rq, const T* __restrict__ emb,
+                                                           float* __restrict__ scores, int D, int64_t capB,
+                                                           int64_t lo, int64_t hi) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = lo + (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (blk >= hi) return;
+  const int b = blockIdx.y;
+  const T* qv = rq + (int64_t)b * D;
+  const T* ev = emb + ((int64_t)b * capB + blk) * D;
+  double dot = 0.0, qq = 0.0, ee = 0.0;
+  for (int e = lane; e < D; e += 64) {
+    const double x = elem_f64(qv, e), y = elem_f64(ev, e);
+    dot = fma(x, y, dot);
+    qq = fma(x, x, qq);
+    ee = fma(y, y, ee);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    dot += __shfl_xor(dot, off);
+    qq += __shfl_xor(qq, off);
+    ee += __shfl_xor(ee, off);
+  }
+  if (lane == 0) {
+    const double den = sqrt(qq) * sqrt(ee);
+    scores[(int64_t)b * capB + blk] = den != 0.0 ? (float)(dot / den) : 0.0f;
+  }
+}
+
+template <typename T, int EPL, int G>
+hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
+  const int L = m.head_dim / EPL;
+  const int slots = 4 * (64 / L);
+  const int64_t nblk = hi - lo;
+  const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
+  // blocks per slot: enough workgroups to fill the chip, a few rows per lane
+  int bps = (int)((nblk * bg) / (slots * 2048));
+  bps = bps < 1 ? 1 : (bps > 8 ? 8 : bps);
+  const int64_t gx = (nblk + (int64_t)slots * bps - 1) / ((int64_t)slots * bps);
+  hipLaunchKernelGGL((score_dot_kernel<T, EPL, G>), dim3((unsigned)gx, (unsigned)bg), dim3(256), 0, s,
+                     (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads,
+                     m.capacity / m.block_size, lo, hi, bps);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_dot(const brs_memory& m, const void* q, int G, int64_t lo, int64_t hi, float* scores,
+                        hipStream_t s) {
+  constexpr int E16 = 16 / sizeof(T);  // elements per 16 bytes
+  const int d = m.head_dim;
+  auto fits = [&](int epl) {
+    if (d % epl) return false;
+    const int L = d / epl;
+    return L >= 1 && L <= 64 && (L & (L - 1)) == 0;
+  };
+  auto qal = ((uintptr_t)q % 16) == 0;
+  if (qal && (d * (int)sizeof(T)) % 16 == 0) {
+    if (G <= 4 && fits(2 * E16)) {
+      if (G == 1) return run_dot<T, 2 * E16, 1>(m, q, lo, hi, scores, s);
+      if (G == 2) return run_dot<T, 2 * E16, 2>(m, q, lo, hi, scores, s);
+      if (G == 4) return run_dot<T, 2 * E16, 4>(m, q, lo, hi, scores, s);
+    }
+    if (G == 8 && fits(E16)) return run_dot<T, E16, 8>(m, q, lo, hi, scores, s);
+  }
+  const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
+  const int64_t gx = (hi - lo + 3) / 4;
+  hipLaunchKernelGGL(score_dot_generic_kernel<T>, dim3((unsigned)gx, (unsigned)bg), dim3(256), 0, s, (const T*)q,
+                     (const T*)m.reps, scores, d, m.reps_per_block, m.n_kv_heads, G, m.capacity / m.block_size,
+                     lo, hi);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi, float* scores,
+                            hipStream_t s) {
+  const int G = hq / m.n_kv_heads;
+  if (m.dtype == BRS_F32) return dispatch_dot<float>(m, q, G, lo, hi, scores, s);
+  return dispatch_dot<uint16_t>(m, q, G, lo, hi, scores, s);
+}
+
+hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, int64_t hi, float* scores,
+                               hipStream_t s) {
+  const int64_t gx = (hi - lo + 3) / 4;
+  if (m.rep_dtype == BRS_F32)
+    hipLaunchKernelGGL(score_cosine_kernel<float>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), 0, s,
+                       (const float*)rq, (const float*)m.reps, scores, m.rep_dim, m.capacity / m.block_size, lo,
+                       hi);
+  else
+    hipLaunchKernelGGL(score_cosine_kernel<uint16_t>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), 0, s,
+                       (const uint16_t*)rq, (const uint16_t*)m.reps, scores, m.rep_dim,
+                       m.capacity / m.block_size, lo, hi);
+  return hipGetLastError();
+}
+
+}  // namespace brs

@@ -1,0 +1,168 @@
+// Exact top-k block selection per score head (MemLong 2.3.2: the top-k
+// indices of the similarity scores, found with an exact search, 2.4.2).
+//
+// Order: score descending, then block index ascending; NaN below every
+// number; -0 equal to +0.  One workgroup per (batch, head):
+//   1. map each score to a 32-bit key whose unsigned order is that score
+//      order (NaN -> 0);
+//   2. radix-select the k-th largest key, 8 bits per pass, with a 256-bin
+//      histogram in LDS;
+//   3. keep every key above it and, among keys equal to it, the lowest block
+//      indices (a prefix count over the workgroup in index order);
+//   4. sort the k winners by counting, on the 64-bit key (score key, ~index).
+#include "brs_internal.h"
+
+namespace brs {
+namespace {
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+  if (s != s) return 0u;
+  uint32_t u = __float_as_uint(s);
+  if (s == 0.0f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NT, int KPT>  // KPT = 0: keys re-read from global memory each pass
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
+                                                  int64_t hi, int k, int32_t* __restrict__ idx,
+                                                  float* __restrict__ vals) {
+  __shared__ uint32_t hist[256];
+  __shared__ int wave_tot[16];
+  __shared__ uint32_t sh_digit;
+  __shared__ int sh_above;
+  __shared__ int sel_count;
+  __shared__ uint64_t sel_key[2048];
+
+  const int64_t row = blockIdx.x;
+  const float* s = scores + row * stride;
+  const int64_t n = hi - lo;
+  const int tid = threadIdx.x;
+  const int64_t c = (n + NT - 1) / NT;  // candidates per thread, contiguous
+  const int64_t my0 = lo + tid * c;
+  const int64_t my1 = (my0 + c < hi) ? my0 + c : hi;
+
+  uint32_t keys[KPT > 0 ? KPT : 1];
+  if (KPT > 0) {
+#pragma unroll
+    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) keys[i] = (my0 + i < my1) ? order_key(s[my0 + i]) : 0u;
+  }
+  auto key_at = [&](int64_t i) -> uint32_t {  // i relative to my0
+    if (KPT > 0) {
+      uint32_t r = 0;
+#pragma unroll
+      for (int j = 0; j < (KPT > 0 ? KPT : 1); ++j)
+        if (j == i) r = keys[j];
+      return r;
+    }
+    return order_key(s[my0 + i]);
+  };
+  const int64_t mine = my1 > my0 ? my1 - my0 : 0;
+
+  if (tid == 0) sel_count = 0;
+  uint32_t thresh = 0;
+  int take_eq = 0;
+  const bool all = n <= k;
+  if (!all) {
+    uint32_t prefix = 0, mask = 0;
+    int kk = k;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+      for (int64_t i = 0; i < mine; ++i) {
+        const uint32_t x = key_at(i);
+        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds reversed positions p = 4l..4l+3, i.e. digits 255-p
+        int h[4], run = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = (int)hist[255 - (4 * tid + i)];
+          run += h[i];
+        }
+        int incl = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (tid >= off) incl += o;
+        }
+        int before = incl - run;  // keys with a larger digit than my first position
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (before < kk && before + h[i] >= kk) {
+            sh_digit = 255u - (uint32_t)(4 * tid + i);
+            sh_above = before;
+          }
+          before += h[i];
+        }
+      }
+      __syncthreads();
+      kk -= sh_above;
+      prefix |= sh_digit << shift;
+      mask |= 0xffu << shift;
+      __syncthreads();
+    }
+    thresh = prefix;
+    take_eq = kk;
+  }
+
+  // count my keys equal to the threshold, in index order
+  int eq = 0;
+  if (!all)
+    for (int64_t i = 0; i < mine; ++i) eq += key_at(i) == thresh;
+  const int eq_incl = block_inclusive_scan(all ? 0 : eq, wave_tot);
+  int rank_eq = eq_incl - eq;
+  for (int64_t i = 0; i < mine; ++i) {
+    const uint32_t x = key_at(i);
+    bool take = all || x > thresh;
+    if (!all && x == thresh) {
+      take = rank_eq < take_eq;
+      ++rank_eq;
+    }
+    if (take) {
+      const int p = atomicAdd(&sel_count, 1);
+      const uint32_t b = (uint32_t)(my0 + i);
+      if (p < k) sel_key[p] = ((uint64_t)x << 32) | (uint64_t)(0xffffffffu - b);
+    }
+  }
+  __syncthreads();
+  const int cnt = min(sel_count, k);
+  int32_t* orow = idx + row * k;
+  float* vrow = vals ? vals + row * k : nullptr;
+  for (int i = tid; i < cnt; i += NT) {
+    const uint64_t me = sel_key[i];
+    int rank = 0;
+    for (int j = 0; j < cnt; ++j) rank += sel_key[j] > me;
+    const int64_t b = (int64_t)(0xffffffffu - (uint32_t)(me & 0xffffffffu));
+    if (rank < k) {
+      orow[rank] = (int32_t)b;
+      if (vrow) vrow[rank] = s[b];
+    }
+  }
+  for (int i = cnt + tid; i < k; i += NT) {
+    orow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select_topk(const float* scores, int batch, int heads, int64_t stride, int64_t lo, int64_t hi,
+                              int k, int32_t* idx, float* vals, hipStream_t s) {
+  const int64_t rows = (int64_t)batch * heads;
+  const int64_t n = hi - lo;
+  if (n <= 256 * 4)
+    hipLaunchKernelGGL((topk_kernel<256, 4>), dim3((unsigned)rows), dim3(256), 0, s, scores, stride, lo, hi, k, idx,
+                       vals);
+  else if (n <= 1024 * 16)
+    hipLaunchKernelGGL((topk_kernel<1024, 16>), dim3((unsigned)rows), dim3(1024), 0, s, scores, stride, lo, hi, k,
+                       idx, vals);
+  else
+    hipLaunchKernelGGL((topk_kernel<1024, 0>), dim3((unsigned)rows), dim3(1024), 0, s, scores, stride, lo, hi, k,
+                       idx, vals);
+  return hipGetLastError();
+}
+
+}  // namespace brs

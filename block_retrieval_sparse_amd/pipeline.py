@@ -1,0 +1,66 @@
+"""One retrieval-attention step over a KVMemory, with its buffers preallocated.
+
+``RetrievalStep.run`` enqueues score_blocks -> select_topk ->
+retrieval_attention on the current stream and returns the output tensor; no
+allocation happens inside ``run``.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import KVMemory, _lib, _stream, check, lib
+
+
+class RetrievalStep:
+    def __init__(self, mem: KVMemory, n_q_heads: int, n_q: int, k: int, n_sink: int, window: int,
+                 scale: float | None = None):
+        self.mem = mem
+        self.n_q_heads, self.n_q, self.k = n_q_heads, n_q, k
+        self.n_sink, self.window = n_sink, window
+        self.scale = 1.0 / math.sqrt(mem.head_dim) if scale is None else scale
+        dev = mem.k.device
+        self.cosine = mem.rep_mode == "embed"
+        self.score_heads = 1 if self.cosine else n_q_heads
+        self.scores = torch.full((mem.batch, self.score_heads, mem.blocks_stride), float("nan"),
+                                 dtype=torch.float32, device=dev)
+        self.idx = torch.full((mem.batch, self.score_heads, k), -1, dtype=torch.int32, device=dev)
+        self.vals = torch.empty((mem.batch, self.score_heads, k), dtype=torch.float32, device=dev)
+        self.out = torch.empty((mem.batch, n_q_heads, n_q, mem.head_dim), dtype=torch.float32, device=dev)
+        nbytes = mem.workspace_bytes(n_q_heads, n_q, self.score_heads, k, n_sink, window)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.lo, self.hi = mem.eligible_range(n_sink, window)
+
+    def score(self, qrep: torch.Tensor, stream=None) -> None:
+        hs = self.score_heads
+        check(lib.brs_score_blocks(self.mem.desc, qrep.data_ptr(), hs, self.lo, self.hi, self.scores.data_ptr(),
+                                   _stream(stream)))
+
+    def select(self, stream=None) -> None:
+        if self.k == 0:
+            return
+        check(lib.brs_select_topk(self.scores.data_ptr(), self.mem.batch, self.score_heads, self.mem.blocks_stride,
+                                  self.lo, self.hi, self.k, self.idx.data_ptr(), self.vals.data_ptr(),
+                                  _stream(stream)))
+
+    def attend(self, q: torch.Tensor, stream=None, profile_events=None) -> torch.Tensor:
+        if profile_events is not None:
+            check(lib.brs_profile_next_attention(profile_events[0], profile_events[1]))
+        check(lib.brs_retrieval_attention(self.mem.desc, q.data_ptr(), self.n_q_heads, self.n_q,
+                                          self.idx.data_ptr() if self.k else None, self.score_heads, self.k,
+                                          self.n_sink, self.window, self.scale, self.out.data_ptr(),
+                                          self.workspace.data_ptr(), self.workspace.numel(), _stream(stream)))
+        return self.out
+
+    def run(self, q: torch.Tensor, qrep: torch.Tensor | None = None, stream=None, profile_events=None):
+        """q ``[batch][Hq][n_q][d]`` (contiguous); qrep is q's last query
+        ``[batch][Hq][d]`` for dot scoring or the chunk embedding
+        ``[batch][rep_dim]`` for cosine scoring."""
+        if qrep is None:
+            qrep = q[:, :, -1, :]
+            if not qrep.is_contiguous():
+                raise ValueError("pass a contiguous qrep")
+        self.score(qrep, stream)
+        self.select(stream)
+        return self.attend(q, stream, profile_events)

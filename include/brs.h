@@ -1,0 +1,225 @@
+/*
+ * brs.h -- block-retrieval sparse attention over a long key/value memory.
+ *
+ * The library implements one decode/prefill step of the method shared by
+ * MemLong (arXiv 2408.16967), InfLLM (arXiv 2402.04617), Landmark Attention
+ * (Mohtashami & Jaggi, 2023) and RetrievalAttention (arXiv 2409.10516):
+ *
+ *   1. brs_mem_append      -- store new K/V rows and, for every block the
+ *                             append completes, its representative vectors;
+ *   2. brs_score_blocks    -- relevance of every candidate block to the query;
+ *   3. brs_select_topk     -- the k best blocks per score head;
+ *   4. brs_retrieval_attention -- exact softmax attention over the sinks,
+ *                             the local window and the selected blocks.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers to tensors are DEVICE pointers (HIP device memory) unless a
+ *   parameter says "host".  The caller allocates and owns all of them; the
+ *   library never allocates, frees or retains device memory, and never
+ *   creates streams.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   device work is enqueued on it; results are ready once the caller has
+ *   synchronised that stream.
+ * - Every call validates its arguments on the host before it enqueues
+ *   anything; a call that returns an error has enqueued nothing and changed
+ *   nothing (brs_mem_append leaves m->length unchanged).
+ * - Return value: BRS_OK (0) or a negative BRS_E_* code; brs_last_error()
+ *   then gives a message (thread-local, valid until the next call on the
+ *   same thread).
+ * - Tensors are dense, row-major, with the shapes given below ([a][b][c]
+ *   means c varies fastest).  "dtype" is the memory's brs_dtype.
+ *
+ * Memory layout (caller-owned, described by brs_memory)
+ * -------------------------------------------------------
+ *   k, v : [batch][n_kv_heads][capacity][row_stride]  dtype
+ *          token t of (batch, head) is row t; columns [head_dim, row_stride)
+ *          are padding that brs_mem_append sets to zero.
+ *   reps : [batch][rep_heads][capacity / block_size][reps_per_block][rep_dim]
+ *          rep_dtype; block b of a head covers tokens [b*B, (b+1)*B), B =
+ *          block_size, and its representatives are written when the block
+ *          is complete.
+ * A block is the memory unit that is scored and retrieved as a whole (the
+ * pages' "chunk", "memory unit", "block"); its tokens are one contiguous span
+ * of rows, so a retrieved block is read with contiguous loads.
+ */
+#ifndef BRS_H_
+#define BRS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BRS_VERSION 1
+
+/* Storage types. */
+typedef enum { BRS_F32 = 0, BRS_BF16 = 1 } brs_dtype;
+
+/* How a block's representatives are obtained (MemLong 2.3.2, InfLLM
+ * "method", Landmark Attention "proposed method"):
+ *   BRS_REP_MEAN    R = 1: the mean of the block's keys, summed in float64
+ *                   and rounded once (nearest-even) to dtype;
+ *   BRS_REP_TOPNORM the R keys of the block with the largest L2 norm (squared
+ *                   norms summed in float64; ties to the lower token), copied
+ *                   unchanged, largest first -- a stand-in for InfLLM's
+ *                   "tokens that received the most attention";
+ *   BRS_REP_GIVEN   caller-supplied vectors of head_dim (Landmark keys);
+ *   BRS_REP_EMBED   caller-supplied chunk embeddings of rep_dim, one per block
+ *                   for the whole sequence (rep_heads = 1), scored by cosine
+ *                   (MemLong's retriever embeddings). */
+typedef enum {
+  BRS_REP_MEAN = 0,
+  BRS_REP_TOPNORM = 1,
+  BRS_REP_GIVEN = 2,
+  BRS_REP_EMBED = 3
+} brs_rep_mode;
+
+enum {
+  BRS_OK = 0,
+  BRS_E_INVAL = -1,        /* bad shape, pointer, mode, alignment or range  */
+  BRS_E_CAPACITY = -2,     /* append would exceed capacity                   */
+  BRS_E_UNSUPPORTED = -3,  /* valid but outside what the kernels implement   */
+  BRS_E_HIP = -4,          /* a HIP launch failed                            */
+  BRS_E_EMPTY = -5,        /* some query would attend no token at all        */
+  BRS_E_WORKSPACE = -6     /* workspace missing or too small                 */
+};
+
+/* Descriptor of one layer's memory.  All enums are stored as int32_t so the
+ * layout is fixed for foreign-function callers.  Constraints (checked by
+ * every call): batch, n_kv_heads, head_dim, block_size, reps_per_block,
+ * rep_dim >= 1; row_stride >= head_dim; 0 <= length <= capacity;
+ * rep_heads = n_kv_heads for MEAN/TOPNORM/GIVEN and 1 for EMBED; rep_dim =
+ * head_dim and rep_dtype = dtype unless rep_mode is EMBED; reps_per_block = 1
+ * for MEAN and EMBED; row_stride * element size is a multiple of 4 bytes;
+ * k, v, reps non-NULL and 16-byte aligned. */
+typedef struct brs_memory {
+  int32_t dtype;           /* brs_dtype of k, v and the queries            */
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t row_stride;      /* elements between consecutive token rows      */
+  int32_t block_size;      /* B, tokens per block                          */
+  int32_t reps_per_block;  /* R                                            */
+  int32_t rep_dim;
+  int32_t rep_heads;
+  int32_t rep_mode;        /* brs_rep_mode                                 */
+  int32_t rep_dtype;       /* brs_dtype of reps                            */
+  int32_t reserved;        /* must be 0                                    */
+  int64_t capacity;        /* token rows per (batch, kv head)              */
+  int64_t length;          /* tokens stored, equal for every batch row     */
+  void* k;
+  void* v;
+  void* reps;
+} brs_memory;
+
+int brs_version(void);
+
+/* Message for the last error on this thread ("" after success). */
+const char* brs_last_error(void);
+
+/* Host-only check of a descriptor (no device access). */
+int brs_memory_check(const brs_memory* m);
+
+/* Append n_new tokens (MemLong 2.3.2, "memorisation": K-V pairs are stored
+ * together with the index-aligned representation of their chunk).
+ *   k_new, v_new : [batch][n_kv_heads][n_new][head_dim] dtype, contiguous.
+ *   reps_new     : for GIVEN/EMBED, the representatives of the blocks this
+ *                  append completes, [batch][rep_heads][n_done][R][rep_dim]
+ *                  rep_dtype, n_done = (length+n_new)/B - length/B; may be
+ *                  NULL when n_done = 0; ignored for MEAN/TOPNORM, whose
+ *                  representatives are computed from the stored keys.
+ * On success enqueues the copies and representative builds and sets
+ * m->length += n_new (host side).  BRS_E_CAPACITY if length + n_new >
+ * capacity.  n_new = 0 is a no-op. */
+int brs_mem_append(brs_memory* m, const void* k_new, const void* v_new, int64_t n_new,
+                   const void* reps_new, void* stream);
+
+/* Candidate blocks for a step with n_sink sinks and a window of the last
+ * `window` tokens (InfLLM "method": the memory units hold what lies outside
+ * the local window).  Host only.  Writes *lo, *hi such that block b is a
+ * candidate iff lo <= b < hi: b is complete (b < length/B) and holds a token
+ * outside [0, n_sink) and [length - window, length).  hi = lo means none. */
+int brs_eligible_range(const brs_memory* m, int64_t n_sink, int64_t window, int64_t* lo,
+                       int64_t* hi);
+
+/* Score blocks [lo, hi) (Landmark Attention "proposed method": similarity of
+ * the query with each block's landmark key; InfLLM "method": block-level
+ * relevance; MemLong 2.3.2: cosine of the chunk embeddings).
+ *   MEAN/TOPNORM/GIVEN (dot-max): qrep = q [batch][n_score_heads][head_dim]
+ *     dtype, n_score_heads = the query heads Hq (a multiple of n_kv_heads;
+ *     query head h reads kv head h / (Hq / n_kv_heads));
+ *     score = max over the block's R representatives of q . rep.
+ *   EMBED (cosine): qrep = [batch][rep_dim] rep_dtype, n_score_heads = 1;
+ *     score = q.e / (|q| |e|), 0 if either norm is 0.
+ * Products are exact and summed in float64, then rounded once to float32, so
+ * the result does not depend on summation order.  No softmax scale.
+ *   scores : [batch][n_score_heads][capacity / block_size] float32; only
+ *            columns [lo, hi) are written.
+ * Requires 0 <= lo <= hi <= length / block_size. */
+int brs_score_blocks(const brs_memory* m, const void* qrep, int32_t n_score_heads, int64_t lo,
+                     int64_t hi, float* scores, void* stream);
+
+/* Exact top-k per row of scores (MemLong 2.3.2: TopK of the scores, computed
+ * exactly, 2.4.2).
+ *   scores : [batch][n_heads][blocks_stride] float32, columns [lo, hi) read.
+ *   idx    : [batch][n_heads][k] int32 -- the first min(k, hi-lo) blocks
+ *            ordered by (score descending, block index ascending); NaN ranks
+ *            below every number; -0 and +0 are equal; unused slots are -1.
+ *   vals   : [batch][n_heads][k] float32 scores of idx (-inf in unused
+ *            slots), or NULL.
+ * Limits: 1 <= k <= 2048; hi - lo <= 1048576. */
+int brs_select_topk(const float* scores, int32_t batch, int32_t n_heads, int64_t blocks_stride,
+                    int64_t lo, int64_t hi, int32_t k, int32_t* idx, float* vals, void* stream);
+
+/* Writes to *bytes (host) the workspace size brs_retrieval_attention needs
+ * for these arguments -- a bound that does not depend on the contents of
+ * idx.  Validates exactly as brs_retrieval_attention does and returns the
+ * same error code for the same arguments. */
+int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_t n_q,
+                                  int32_t idx_heads, int32_t k, int64_t n_sink, int64_t window,
+                                  size_t* bytes);
+
+/* Exact softmax attention over the attended set (InfLLM "method": local
+ * tokens plus a few relevant memory units; MemLong Figure 3 and 2.3.4: the
+ * retrieved chunks are visible in full, the local context causally;
+ * RetrievalAttention "proposed method": attention restricted to the tokens
+ * that matter).
+ *   q    : [batch][n_q_heads][n_q][head_dim] dtype; query j sits at position
+ *          N - n_q + j (N = m->length: the queries' own tokens are already
+ *          appended).
+ *   idx  : [batch][idx_heads][k] int32 block indices; idx_heads = n_q_heads
+ *          (one list per query head) or 1 (one list for all heads of a
+ *          sequence).  Entries < 0 or >= N / block_size are skipped;
+ *          duplicates count once.
+ *   For query j of head h the attended set is the SET
+ *      [0, n_sink) u [N - window, N) u  U_{b in idx} [bB, bB + B)
+ *   restricted to positions <= N - n_q + j; head h reads kv head
+ *   h / (n_q_heads / n_kv_heads).  Logits are scale * q.k; softmax and the
+ *   weighted sum of V are accumulated in float32.
+ *   out  : [batch][n_q_heads][n_q][head_dim] float32.  A query whose set is
+ *          empty at run time (possible only when n_sink = window = 0 and
+ *          every idx entry is skipped) gets zeros; when that is certain
+ *          from the arguments alone the call returns BRS_E_EMPTY.
+ *   workspace : device scratch of at least brs_attention_workspace_bytes()
+ *          bytes, 256-byte aligned; its contents on entry do not matter.
+ * n_q = 1 (decode) runs a split-K flash-decode; n_q > 1 with bf16 runs the
+ * matrix-core prefill kernel. */
+int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
+                            const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
+                            int64_t window, float scale, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Measurement hook: the next brs_retrieval_attention call on this thread
+ * records `start_event` and `stop_event` (hipEvent_t, passed as void*) at the
+ * begin and end of its main attention kernel on its stream, then forgets
+ * them.  Pass NULLs to cancel. */
+int brs_profile_next_attention(void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRS_H_ */

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/brs.h declares, and rejects bad arguments on the host
+before any device work; brs_eligible_range matches the oracle's brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "brs.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_retrieval_sparse_amd import _lib
+
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(brs_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_are_exported(L):
+    names = declared_functions()
+    assert "brs_retrieval_attention" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L.lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def test_version(L):
+    assert L.lib.brs_version() == 1
+
+
+def desc(L, **kw):
+    d = dict(dtype=L.BRS_BF16, batch=1, n_kv_heads=2, head_dim=128, row_stride=128, block_size=64,
+             reps_per_block=1, rep_dim=128, rep_heads=2, rep_mode=L.REP_MEAN, rep_dtype=L.BRS_BF16, reserved=0,
+             capacity=4096, length=4096, k=0x10000, v=0x20000, reps=0x30000)
+    d.update(kw)
+    return L.brs_memory(**d)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(dtype=7), dict(rep_mode=9), dict(batch=0), dict(row_stride=64), dict(length=5000),
+    dict(rep_heads=1), dict(rep_dim=64), dict(reps_per_block=2), dict(k=0), dict(v=0x20004),
+    dict(reserved=1), dict(rep_mode=3, rep_heads=2), dict(capacity=1 << 40, length=0),
+    dict(rep_mode=1, reps_per_block=100), dict(row_stride=127, head_dim=127, rep_dim=127),
+])
+def test_memory_check_rejects(L, bad):
+    assert L.lib.brs_memory_check(desc(L, **bad)) == -1
+    assert L.lib.brs_last_error()
+
+
+def test_memory_check_accepts(L):
+    assert L.lib.brs_memory_check(desc(L)) == 0
+    assert L.lib.brs_memory_check(desc(L, rep_mode=L.REP_EMBED, rep_heads=1, rep_dim=768)) == 0
+    assert L.lib.brs_memory_check(desc(L, rep_mode=L.REP_TOPNORM, reps_per_block=4)) == 0
+
+
+def test_eligible_range_matches_oracle(L):
+    import oracle.brs_oracle as O
+
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    for N in (0, 1, 63, 64, 65, 500, 4096, 4100):
+        for B in (1, 7, 64, 128):
+            for S in (0, 4, 100, 5000):
+                for Wn in (0, 1, 256, 4095, 10000):
+                    m = desc(L, block_size=B, capacity=max(N, 1), length=N)
+                    assert L.lib.brs_eligible_range(m, S, Wn, ctypes.byref(lo), ctypes.byref(hi)) == 0
+                    assert (lo.value, hi.value) == O.eligible_range(N, B, S, Wn), (N, B, S, Wn)
+    assert L.lib.brs_eligible_range(desc(L), -1, 0, ctypes.byref(lo), ctypes.byref(hi)) == -1
+
+
+def test_append_rejects_before_device_work(L):
+    m = desc(L, length=4000)
+    assert L.lib.brs_mem_append(m, 0x1000, 0x2000, 97, None, None) == -2   # capacity
+    assert m.length == 4000
+    assert L.lib.brs_mem_append(m, 0x1000, 0x2000, -1, None, None) == -1
+    assert L.lib.brs_mem_append(m, None, 0x2000, 5, None, None) == -1
+    g = desc(L, rep_mode=L.REP_GIVEN, length=4000)
+    assert L.lib.brs_mem_append(g, 0x1000, 0x2000, 90, None, None) == -1   # completes a block, no reps
+    assert L.lib.brs_mem_append(m, 0x1000, 0x2000, 0, None, None) == 0     # no-op
+    assert m.length == 4000
+
+
+def test_score_select_attention_reject(L):
+    m = desc(L)
+    s = 0x40000
+    assert L.lib.brs_score_blocks(m, 0x1000, 3, 0, 10, s, None) == -1          # heads not a multiple
+    assert L.lib.brs_score_blocks(m, 0x1000, 4, 10, 5, s, None) == -1          # lo > hi
+    assert L.lib.brs_score_blocks(m, 0x1000, 4, 0, 65, s, None) == -1          # beyond complete blocks
+    e = desc(L, rep_mode=L.REP_EMBED, rep_heads=1, rep_dim=768)
+    assert L.lib.brs_score_blocks(e, 0x1000, 2, 0, 10, s, None) == -1          # cosine has one head
+    assert L.lib.brs_select_topk(s, 1, 4, 64, 0, 64, 0, 0x5000, None, None) == -3
+    assert L.lib.brs_select_topk(s, 1, 4, 64, 0, 64, 4096, 0x5000, None, None) == -3
+    assert L.lib.brs_select_topk(s, 1, 4, 64, 10, 5, 4, 0x5000, None, None) == -1
+    assert L.lib.brs_select_topk(s, 1, 4, 64, 0, 65, 4, 0x5000, None, None) == -1
+    n = ctypes.c_size_t()
+    assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 32, 128, 1024, ctypes.byref(n)) == 0
+    ws = n.value
+    assert ws > 0
+    assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 64, 128, 1024, ctypes.byref(n)) == 0
+    assert n.value >= ws
+    assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 0, 0, 0, ctypes.byref(n)) == -5
+    assert L.lib.brs_attention_workspace_bytes(m, 7, 1, 7, 4, 0, 0, ctypes.byref(n)) == -1
+    args = dict(q=0x1000, hq=8, nq=1, idx=0x2000, ih=8, k=32, S=128, Wn=1024, sc=0.1, out=0x3000)
+
+    def call(ws_ptr=0x100000, ws_bytes=ws, **kw):
+        a = dict(args)
+        a.update(kw)
+        return L.lib.brs_retrieval_attention(m, a["q"], a["hq"], a["nq"], a["idx"], a["ih"], a["k"], a["S"],
+                                             a["Wn"], a["sc"], a["out"], ws_ptr, ws_bytes, None)
+
+    assert call(hq=7) == -1
+    assert call(ih=3) == -1
+    assert call(nq=5000) == -1
+    assert call(k=0, S=0, Wn=0) == -5
+    assert call(ws_bytes=ws - 1) == -6
+    assert call(ws_ptr=0x100010) == -6
+    assert call(sc=float("inf")) == -1
+    assert call(idx=None) == -1
+    assert call(q=0x1004) == -1

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Cases span several tiles and ragged tails at oracle-friendly sizes, the five
+workloads at full size (sampled outputs where the oracle would be slow), and
+the edge cases of the method: k above the candidate count, no candidates,
+caller-made selections with duplicates / -1 / out-of-range entries, several
+queries per call, 8 query heads per kv head, head dims served by the generic
+kernels, ties and NaN in selection, and run-to-run determinism.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_cases as C
+import oracle.brs_oracle as O
+from synth import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+W = WORKLOADS
+SMALL = {
+    "tiny": W["tiny_decode"],
+    "landmark": W["landmark_decode_32k"].scaled(n_q_heads=4, n_kv_heads=4, n_tokens=3018),
+    "infllm": W["infllm_gqa_decode_128k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=8192 + 37, window=512,
+                                                  k=8, planted_per_head=2),
+    "retrieval": W["retrievalattn_gqa_decode_1m_b8"].scaled(batch=2, n_q_heads=8, n_kv_heads=2, n_tokens=16384,
+                                                             k=32),
+    "memlong": W["memlong_chunk_prefill_80k"].scaled(n_q_heads=4, n_kv_heads=4, n_tokens=8 * 512 + 512),
+    "gqa8": W["infllm_gqa_decode_128k"].scaled(n_q_heads=16, n_kv_heads=2, n_tokens=4096 + 100, window=256,
+                                                sinks=64, k=6, planted_per_head=1),
+    "multi_q": W["infllm_gqa_decode_128k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=6000, window=300, k=5,
+                                                   n_q=3, planted_per_head=0),
+    "bf16_d64": W["retrievalattn_gqa_decode_1m_b8"].scaled(batch=1, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                                                            rep_dim=64, n_tokens=5000, k=12, window=100, sinks=3),
+    "bf16_d96_generic": W["retrievalattn_gqa_decode_1m_b8"].scaled(batch=1, n_q_heads=6, n_kv_heads=2,
+                                                                    head_dim=96, rep_dim=96, n_tokens=3333, k=7,
+                                                                    window=200, sinks=5, block=32),
+    "f32_d48_generic": W["tiny_decode"].scaled(n_q_heads=2, n_kv_heads=1, head_dim=48, rep_dim=48, n_tokens=2500,
+                                                block=40, k=6),
+    "f32_topnorm": W["tiny_decode"].scaled(n_q_heads=4, n_kv_heads=2, rep_mode="topnorm", reps_per_block=3,
+                                            n_tokens=3000, block=50, k=5, window=64, sinks=10),
+}
+
+
+def run_step(mem, w, x, k=None, sinks=None, window=None):
+    from block_retrieval_sparse_amd.pipeline import RetrievalStep
+
+    step = RetrievalStep(mem, w.n_q_heads, w.n_q, w.k if k is None else k, w.sinks if sinks is None else sinks,
+                         w.window if window is None else window)
+    qrep = x["rq"] if w.rep_mode == "embed" else x["q"][:, :, -1, :].contiguous()
+    step.run(x["q"], qrep)
+    return step
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_append_and_reps(name):
+    w = SMALL[name]
+    mem, x = C.load(w, pieces=3)
+    torch.cuda.synchronize()
+    N, d = w.n_tokens, w.head_dim
+    assert mem.length == N
+    assert torch.equal(mem.k[:, :, :N, :d], x["k"]) and torch.equal(mem.v[:, :, :N, :d], x["v"])
+    if w.stride > d:
+        assert not mem.k[:, :, :N, d:].any() and not mem.v[:, :, :N, d:].any()
+    C.check_reps(w, mem, C.oracle_reps(w, x))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step(name):
+    w = SMALL[name]
+    mem, x = C.load(w)
+    step = run_step(mem, w, x)
+    res = C.check_step(w, mem, x, step)
+    print(f"{name}: max |err| {res['max_abs_err']:.3g}")
+    if w.planted_per_head:
+        idx = step.idx.cpu().numpy()
+        for (b, h), blocks in x["planted"].items():
+            assert set(blocks) <= set(idx[b, h].tolist()), (b, h)
+
+
+def test_determinism():
+    w = SMALL["retrieval"]
+    mem, x = C.load(w)
+    a = run_step(mem, w, x)
+    outs = (a.scores.clone(), a.idx.clone(), a.out.clone())
+    b = run_step(mem, w, x)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].nan_to_num(0), b.scores.nan_to_num(0))
+    assert torch.equal(outs[1], b.idx)
+    assert torch.equal(outs[2], b.out)
+
+
+def test_k_above_candidates_and_no_candidates():
+    w = SMALL["landmark"]
+    mem, x = C.load(w)
+    lo, hi = mem.eligible_range(w.sinks, w.window)
+    wk = w.scaled(k=hi - lo + 9)
+    step = run_step(mem, wk, x)
+    C.check_step(wk, mem, x, step)
+    assert (step.idx[:, :, hi - lo:] == -1).all()
+    # a window covering all tokens leaves no candidate: plain causal attention
+    wn = w.scaled(window=w.n_tokens)
+    step = run_step(mem, wn, x)
+    assert step.lo == step.hi
+    C.check_step(wn, mem, x, step)
+
+
+def test_caller_selection_with_duplicates_and_skips():
+    """Selections from the caller: duplicates count once, -1 and out-of-range
+    entries are skipped, blocks overlapping sinks/window are deduplicated."""
+    w = SMALL["infllm"]
+    mem, x = C.load(w)
+    nb = w.n_blocks
+    idx = torch.tensor([[[5, 5, -1, nb, nb + 100, 0, nb - 1, 3]] * w.n_q_heads] * w.batch, dtype=torch.int32,
+                       device="cuda")
+    out = mem.retrieval_attention(x["q"], idx, w.sinks, w.window)
+    torch.cuda.synchronize()
+    q, K, V = C.host(x["q"]), C.host(x["k"]), C.host(x["v"])
+    for h in range(w.n_q_heads):
+        g = h // w.group
+        T = O.attended_mask(w.n_tokens, w.block, w.sinks, w.window, [b for b in idx[0, h].tolist() if b < nb])
+        ref = O.attention(q[0, h], K[0, g], V[0, g], T, C.scale_of(w))
+        assert np.max(np.abs(out[0, h].cpu().numpy() - ref)) <= C.TOL[w.dtype]
+
+
+def test_empty_set_gives_zeros_and_static_empty_is_an_error():
+    import block_retrieval_sparse_amd as brs
+
+    w = SMALL["retrieval"]
+    mem, x = C.load(w)
+    idx = torch.full((w.batch, w.n_q_heads, 4), -1, dtype=torch.int32, device="cuda")
+    out = mem.retrieval_attention(x["q"], idx, 0, 0)
+    torch.cuda.synchronize()
+    assert not out.any()
+    with pytest.raises(brs.BrsError) as e:
+        mem.retrieval_attention(x["q"], None, 0, 0)
+    assert e.value.code == -5
+
+
+def test_broadcast_selection_dot_mode():
+    """One selection per sequence (idx_heads = 1) in dot mode."""
+    w = SMALL["infllm"]
+    mem, x = C.load(w)
+    idx = torch.tensor([[[7, 2, 40, 11]]] * w.batch, dtype=torch.int32, device="cuda")
+    out = mem.retrieval_attention(x["q"], idx, w.sinks, w.window)
+    torch.cuda.synchronize()
+    q, K, V = C.host(x["q"]), C.host(x["k"]), C.host(x["v"])
+    T = O.attended_mask(w.n_tokens, w.block, w.sinks, w.window, [7, 2, 40, 11])
+    for h in range(w.n_q_heads):
+        ref = O.attention(q[0, h], K[0, h // w.group], V[0, h // w.group], T, C.scale_of(w))
+        assert np.max(np.abs(out[0, h].cpu().numpy() - ref)) <= C.TOL[w.dtype]
+
+
+@pytest.mark.parametrize("n,k,kind", [(1, 1, "normal"), (60, 4, "ties"), (991, 32, "ties"), (991, 32, "nan"),
+                                      (5000, 2048, "normal"), (16384, 320, "ties"), (16384, 320, "zeros"),
+                                      (20000, 100, "ties"), (700, 700, "normal"), (50, 64, "normal")])
+def test_select_topk(n, k, kind):
+    import block_retrieval_sparse_amd as brs
+
+    rng = np.random.default_rng(n + k)
+    rows, stride, lo = 3, n + 11, 5
+    s = rng.standard_normal((rows, stride)).astype(np.float32)
+    if kind == "ties":
+        s = np.round(s * 4) / 4
+    if kind == "nan":
+        s[:, rng.integers(0, stride, 40)] = np.nan
+    if kind == "zeros":
+        s = np.where(rng.random((rows, stride)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        s[rng.random((rows, stride)) < 0.01] = 1.0
+    hi = lo + n
+    st = torch.from_numpy(s).cuda()[None].reshape(1, rows, stride).contiguous()
+    idx, vals = brs.select_topk(st, lo, hi, k)
+    torch.cuda.synchronize()
+    for r in range(rows):
+        oi, ov = O.select_topk(s[r], lo, hi, k)
+        assert np.array_equal(idx[0, r].cpu().numpy(), oi), (r, idx[0, r][:10], oi[:10])
+        gv = vals[0, r].cpu().numpy()
+        assert np.array_equal(gv.view(np.uint32), ov.view(np.uint32)) or np.array_equal(gv, ov, equal_nan=True)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "landmark_decode_32k", "infllm_gqa_decode_128k"])
+def test_full_size_decode(name):
+    w = W[name]
+    mem, x = C.load(w)
+    step = run_step(mem, w, x)
+    res = C.check_step(w, mem, x, step)
+    print(f"{name}: max |err| {res['max_abs_err']:.3g}")
+    for (b, h), blocks in x["planted"].items():
+        assert set(blocks) <= set(step.idx[b, h].cpu().tolist())
+
+
+def test_full_size_retrievalattn_sampled():
+    w = W["retrievalattn_gqa_decode_1m_b8"]
+    mem, x = C.load(w)
+    step = run_step(mem, w, x)
+    pairs = [(0, 0), (3, 13), (7, 31), (5, 22)]
+    res = C.check_step(w, mem, x, step, pairs=pairs)
+    print(f"retrievalattn: max |err| {res['max_abs_err']:.3g}")
+
+
+def test_full_size_memlong_prefill_sampled():
+    w = W["memlong_chunk_prefill_80k"]
+    mem, x = C.load(w)
+    step = run_step(mem, w, x)
+    res = C.check_step(w, mem, x, step, pairs=[(0, 0), (0, 17), (0, 31)], query_rows=[0, 1, 255, 510, 511])
+    print(f"memlong: max |err| {res['max_abs_err']:.3g}")
