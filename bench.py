@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of one block-retrieval attention step on one MI355X.
+
+A step is the whole hot path for one attention layer: score_blocks ->
+select_topk -> retrieval_attention, on inputs resident in HBM.  Steps rotate
+over ``--layers`` independent layer memories (each with its own K, V,
+representatives and query), as successive layers of a model would, so that a
+step's data has been evicted from the 256 MB Infinity Cache by the other
+layers' traffic before it is read again.
+
+Prints one JSON line (stdout).  Progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime (for per-launch kernel timing)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def attended_tokens(N, B, S, W, rows) -> int:
+    """Distinct tokens of one (batch, kv head): sinks, window and the selected
+    blocks of all its query heads (each token counted once)."""
+    import numpy as np
+
+    T = np.zeros(N, dtype=bool)
+    T[:min(S, N)] = True
+    T[max(N - W, 0):] = True
+    nb = N // B
+    for b in np.unique(rows):
+        if 0 <= b < nb:
+            T[b * B:(b + 1) * B] = True
+    return int(T.sum())
+
+
+def build_layers(w, n_layers, dev):
+    import torch
+
+    import block_retrieval_sparse_amd as brs
+    from block_retrieval_sparse_amd.pipeline import RetrievalStep
+    from synth import inputs as I
+
+    layers = []
+    t_build, built_bytes = 0.0, 0
+    for i in range(n_layers):
+        wl = w.scaled(seed=w.seed + 7919 * i)
+        x = I.make_all(wl, dev)
+        rep_dtype = torch.bfloat16 if w.rep_mode == "embed" else I.torch_dtype(w)
+        mem = brs.KVMemory(w.batch, w.n_kv_heads, w.head_dim, w.n_tokens, w.block, dtype=I.torch_dtype(w),
+                           rep_mode=w.rep_mode, reps_per_block=w.reps_per_block, rep_dim=w.rep_dim,
+                           rep_dtype=rep_dtype, row_stride=w.stride, device=dev)
+        given = x.get("given_reps", x.get("embeds"))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        mem.append(x["k"], x["v"], given)
+        torch.cuda.synchronize()
+        t_build += time.perf_counter() - t0
+        built_bytes += 2 * x["k"].numel() * x["k"].element_size()
+        step = RetrievalStep(mem, w.n_q_heads, w.n_q, w.k, w.sinks, w.window)
+        qrep = x["rq"].reshape(w.batch, -1).contiguous() if w.rep_mode == "embed" else \
+            x["q"][:, :, -1, :].contiguous()
+        keep = {"q": x["q"], "qrep": qrep}
+        if i == 0:
+            keep.update(host_inputs=x)
+        else:
+            del x
+        layers.append((mem, step, keep))
+        log(f"layer {i}: built {w.n_tokens} tokens x {w.batch * w.n_kv_heads} kv heads")
+    return layers, t_build, built_bytes
+
+
+def step_bytes(w, step) -> dict:
+    """Algorithmic bytes of one executed step, from its own selection."""
+    es = 4 if w.dtype == "f32" else 2
+    idx = step.idx.cpu().numpy()
+    N = step.mem.length
+    kv = 0
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            rows = idx[b, 0] if w.rep_mode == "embed" else idx[b, g * w.group:(g + 1) * w.group]
+            kv += attended_tokens(N, w.block, w.sinks, w.window, rows) * w.head_dim * es * 2
+    nelig = step.hi - step.lo
+    if w.rep_mode == "embed":
+        reps = w.batch * nelig * w.rep_dim * 2 + w.batch * w.rep_dim * 2
+    else:
+        reps = w.batch * w.n_kv_heads * nelig * w.reps_per_block * w.rep_dim * es
+    q = w.batch * w.n_q_heads * w.n_q * w.head_dim * es
+    out = w.batch * w.n_q_heads * w.n_q * w.head_dim * 4
+    return {"reps": reps, "kv": kv, "q": q, "out": out, "total": reps + kv + q + out}
+
+
+def cpu_baseline(w, layer0, budget_s: float) -> dict:
+    """The oracle (as it stands) on a bounded sample of layer 0's step."""
+    import numpy as np
+    import torch
+
+    import oracle.brs_oracle as O
+
+    x = layer0["host_inputs"]
+    f = lambda t: t.to(torch.float64).cpu().numpy()  # noqa: E731
+    q = f(x["q"])
+    pairs_all = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)]
+    # one (batch, kv head) slice at a time keeps host memory bounded
+    done, elapsed = 0, 0.0
+    for (b0, g0) in [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]:
+        K = f(x["k"][b0:b0 + 1, g0:g0 + 1])
+        V = f(x["v"][b0:b0 + 1, g0:g0 + 1])
+        if w.rep_mode in ("given", "embed"):
+            src = x["given_reps"] if w.rep_mode == "given" else x["embeds"]
+            reps = f(src[b0:b0 + 1, :1] if w.rep_mode == "embed" else src[b0:b0 + 1, g0:g0 + 1])
+        else:
+            reps = O.build_reps(K[0, 0], w.rep_mode, w.block, w.reps_per_block, w.dtype)[None, None]
+        rq = f(x["rq"]).reshape(w.batch, -1)[b0:b0 + 1] if w.rep_mode == "embed" else None
+        heads = [h for (b, h) in pairs_all if b == b0 and (w.rep_mode == "embed" or h // w.group == g0)]
+        for h in heads:
+            t0 = time.perf_counter()
+            O.step(q[b0:b0 + 1, h:h + 1], K, V, reps, block=w.block, k=w.k, sinks=w.sinks, window=w.window,
+                   mode=w.rep_mode, rq=rq)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= budget_s:
+                break
+        del K, V
+        if elapsed >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    frac = done / len(pairs_all)
+    return {"value": w.batch * frac / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(pairs_all)} (batch, query head) decode problems of one layer "
+                      f"(scores, top-k, attention; representatives prebuilt, untimed), {elapsed:.1f} s of CPU "
+                      f"work, scaled to whole steps"}
+
+
+def run(args):
+    import torch
+
+    from block_retrieval_sparse_amd import _lib
+    from synth import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if w.n_q > 1:
+        raise SystemExit("bench.py times decode workloads; the chunked-prefill workload is timed by "
+                         "--workload with n_q == 1 only in this version")
+    es = 4 if w.dtype == "f32" else 2
+    est = (w.batch * w.n_kv_heads * (w.sinks + w.window + w.k * w.group * w.block) * w.head_dim * es * 2)
+    n_layers = args.layers or max(1, min(8, math.ceil(1.5e9 / max(est, 1))))
+    layers, t_build, built_bytes = build_layers(w, n_layers, dev)
+
+    def one(i, ev=None):
+        mem, step, keep = layers[i % n_layers]
+        step.run(keep["q"], keep["qrep"], profile_events=ev)
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    per_layer = [step_bytes(w, st) for (_, st, _) in layers]
+    avg = {k: sum(p[k] for p in per_layer) / n_layers for k in per_layer[0]}
+
+    # pass A: the timed region
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s0.record()
+    for i in range(args.steps):
+        one(i)
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = s0.elapsed_time(s1)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step (host wall {wall * 1e3 / args.steps:.2f} us/step)")
+
+    # pass B: the same steps with the attention kernel's own begin/end timestamps
+    he = HipEvents()
+    evs = [(he.create(), he.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        one(i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [he.elapsed_ms(a, b) for (a, b) in evs]
+    for a, b in evs:
+        he.destroy(a)
+        he.destroy(b)
+    kern_avg = sum(kern_ms) / len(kern_ms)
+
+    # pass C: per-stage breakdown (events on the library's stream = torch's current stream)
+    stage = {"score": 0.0, "select": 0.0, "attend": 0.0}
+    n_c = min(args.steps, 100)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n_c)]
+    for i in range(n_c):
+        mem, step, keep = layers[i % n_layers]
+        ev[4 * i].record()
+        step.score(keep["qrep"])
+        ev[4 * i + 1].record()
+        step.select()
+        ev[4 * i + 2].record()
+        step.attend(keep["q"])
+        ev[4 * i + 3].record()
+    torch.cuda.synchronize()
+    for i in range(n_c):
+        stage["score"] += ev[4 * i].elapsed_time(ev[4 * i + 1]) / n_c
+        stage["select"] += ev[4 * i + 1].elapsed_time(ev[4 * i + 2]) / n_c
+        stage["attend"] += ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) / n_c
+
+    split_bytes = avg["kv"] + avg["q"]
+    achieved = split_bytes / (kern_avg * 1e-3) / 1e9
+    res = {
+        "metric": "retrieval-attn decode tokens/s @128K ctx; achieved HBM GB/s vs peak",
+        "value": w.batch / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q with planted blocks; no dataset or weights)",
+        "config": {"workload": w.name, "batch": w.batch, "context_tokens": w.n_tokens, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block,
+                   "reps_per_block": w.reps_per_block, "rep_mode": w.rep_mode, "top_k": w.k,
+                   "window": w.window, "sinks": w.sinks, "layers_rotated": n_layers, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "attn_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": split_bytes, "avg_launch_us": kern_avg * 1e3},
+        "step_hbm": {"algorithmic_bytes": avg["total"], "GB/s": avg["total"] / (ms_step * 1e-3) / 1e9,
+                     "frac": avg["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, "parts": avg},
+        "stage_us": {k: v * 1e3 for k, v in stage.items()},
+        "append_build": {"bytes": built_bytes, "s": t_build, "GB/s": built_bytes / max(t_build, 1e-9) / 1e9},
+        "lib_version": _lib.lib.brs_version(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        res["cpu_baseline"] = cpu_baseline(w, layers[0][2], args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="infllm_gqa_decode_128k")
+    ap.add_argument("--layers", type=int, default=0, help="layer memories to rotate over (0 = enough to exceed the cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the path has no multi-GPU part (each (batch, kv head) is "
+              "independent; see the sharding notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    res = run(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -243,14 +243,14 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
-  hipError_t e = brs::launch_attn_plan(g, idx, workspace, s);
+  hipError_t e = brs::launch_attn_plan(g, idx, workspace, out, s);
   if (e != hipSuccess) return hip_fail(e, "attn_plan");
   if (brs::prefill_supported(g)) {
     e = brs::launch_attn_prefill(g, m->k, m->v, q, idx, out, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "attn_prefill");
     return ok();
   }
-  e = brs::launch_attn_split(g, m->k, m->v, q, workspace, s, e0, e1);
+  e = brs::launch_attn_split(g, m->k, m->v, q, workspace, out, s, e0, e1);
   if (e != hipSuccess) return hip_fail(e, "attn_split");
   e = brs::launch_attn_merge(g, workspace, out, s);
   if (e != hipSuccess) return hip_fail(e, "attn_merge");

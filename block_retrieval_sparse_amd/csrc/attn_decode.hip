@@ -7,16 +7,22 @@
 //   plan   one workgroup per (batch, kv head): marks the blocks any query
 //          head of the group selected (a head bitmask per block, in LDS),
 //          clips them against sinks and window so every token appears once,
-//          and writes work items (first row, length <= 128, head mask):
-//          sinks, window, then the selected blocks in index order.
-//   split  one workgroup per (batch, kv head, run of items): streams each
-//          item's K and V rows once for all query rows of the group, with an
-//          online softmax in float32 (log2 domain), and writes a partial
-//          (max, sum, weighted V) per query row.
-//   merge  one wave per query row: combines the partials by log-sum-exp in
-//          a fixed order (deterministic).
+//          and writes the segments of the attended set with their offsets in
+//          the flattened token list, plus the segment that starts each chunk.
+//   split  one workgroup per (batch, kv head, row group, chunk of
+//          chunk_tokens flattened tokens); each wave takes an equal run of
+//          the chunk, so work is balanced whatever the segment lengths.  K and
+//          V rows are streamed once for all query rows of the group, with an
+//          online softmax in float32 (log2 domain); the workgroup writes a
+//          partial (max, sum, weighted V) per query row.
+//   merge  one workgroup per query row combines the partials by log-sum-exp
+//          in a fixed order (deterministic).  A kernel of its own: merging in
+//          the last split workgroup would need an agent-scope release/acquire
+//          per workgroup, which on this GPU writes back and invalidates the
+//          whole L2 of the XCD each time.
 #include <hip/hip_ext.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include "brs_internal.h"
 
@@ -24,49 +30,95 @@ namespace brs {
 namespace {
 
 constexpr float kNegInf = -INFINITY;
+constexpr int kMergeC = 256;   // chunk weights cached in LDS by the merging workgroup
+constexpr int kItemsLds = 256;  // segments of one chunk staged in LDS
+constexpr int kTargetWaves = 2048;
+
+// Tuning knobs (shape of the decomposition only; results do not depend on
+// them beyond float32 summation order): BRS_TARGET_WAVES, BRS_NW, BRS_U.
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Sum over aligned groups of L lanes (L a power of two).  Within a 16-lane
+// row the exchanges are DPP moves (quad permutes, then half-row and row
+// mirrors: each pairs lanes so that every lane ends with the group total);
+// wider groups fall back to cross-row shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (L >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  if constexpr (L >= 32) v += __shfl_xor(v, 16);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// 2^x with the hardware instruction (about 1 ulp; tiny results flush to 0,
+// which only drops softmax weights below 2^-126).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct PlanArgs {
   const int32_t* idx;
-  int4* plan;
+  int4* hdr;          // [bg]: (segments, tokens)
+  int4* items;        // [bg][max_items]: (first row, length, head mask, flattened offset)
+  int* chunk_first;   // [bg][max_chunks]: segment holding the chunk's first token
+  int4* chunks;       // [bg][max_chunks]: (first segment, end segment, end token, 0)
+  float* out;
   int64_t max_items;
-  int hq, hkv, G, k, idx_heads;
-  int N, B, nb, sink_end, win_start;
+  int max_chunks;
+  int hq, hkv, G, k, idx_heads, n_q, d, row_groups;
+  int N, B, nb, sink_end, win_start, chunk_tokens;
 };
 
 // ---------------------------------------------------------------------------
 // plan
 
+__device__ __forceinline__ void mark_chunks(int* first, int item, int off, int len, int CH) {
+  for (int c = (off + CH - 1) / CH; c * CH < off + len; ++c) first[c] = item;
+}
+
 __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
   __shared__ uint32_t marks[kMarkBlocks];
   __shared__ int wave_tot[16];
-  __shared__ int sh_total;
+  __shared__ int sh_items, sh_tokens;
   const int bg = blockIdx.x;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
-  int4* plan = a.plan + (int64_t)bg * (1 + a.max_items);
+  int4* items = a.items + (int64_t)bg * a.max_items;
+  int* first = a.chunk_first + (int64_t)bg * a.max_chunks;
   const int tid = threadIdx.x, nt = blockDim.x;
+  const int CH = a.chunk_tokens;
   const uint32_t full = a.G >= 32 ? 0xffffffffu : ((1u << a.G) - 1u);
 
-  // shared part: sinks [0, S') and window [ws, N), in pieces of <= kItemTokens
-  const int n_sink_items = (a.sink_end + kItemTokens - 1) / kItemTokens;
-  const int n_win_items = (a.N - a.win_start + kItemTokens - 1) / kItemTokens;
-  for (int i = tid; i < n_sink_items + n_win_items; i += nt) {
-    int p0, end;
-    if (i < n_sink_items) {
-      p0 = i * kItemTokens;
-      end = a.sink_end;
-    } else {
-      p0 = a.win_start + (i - n_sink_items) * kItemTokens;
-      end = a.N;
+  // shared part: sinks [0, S') then window [ws, N)
+  const int S = a.sink_end, Wn = a.N - a.win_start;
+  if (tid == 0) {
+    int i = 0;
+    if (S > 0) {
+      items[i] = make_int4(0, S, (int)full, 0);
+      mark_chunks(first, i, 0, S, CH);
+      ++i;
     }
-    plan[1 + i] = make_int4(p0, min(kItemTokens, end - p0), (int)full, 0);
+    if (Wn > 0) {
+      items[i] = make_int4(a.win_start, Wn, (int)full, S);
+      mark_chunks(first, i, S, Wn, CH);
+    }
   }
+  int n_items = (S > 0) + (Wn > 0), n_tokens = S + Wn;
 
   const int E = a.idx_heads == 1 ? a.k : a.G * a.k;
-  int written = n_sink_items + n_win_items;
   for (int base = 0; base < a.nb; base += kMarkBlocks) {
-    for (int i = tid; i < kMarkBlocks; i += nt) marks[i] = 0u;
-    __syncthreads();
     const int top = min(a.nb, base + kMarkBlocks);
+    for (int i = tid; i < top - base; i += nt) marks[i] = 0u;
+    __syncthreads();
     for (int e = tid; e < E; e += nt) {
       int blk;
       uint32_t bit;
@@ -79,7 +131,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
         bit = 1u << j;
       }
       if (blk >= base && blk < top) {
-        const int lo_t = max(blk * a.B, a.sink_end);
+        const int lo_t = max(blk * a.B, S);
         const int hi_t = min((blk + 1) * a.B, a.win_start);
         if (lo_t < hi_t) atomicOr(&marks[blk - base], bit);
       }
@@ -88,28 +140,52 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
     // each thread owns a contiguous run of blocks
     const int per = (kMarkBlocks + nt - 1) / nt;
     const int r0 = base + tid * per, r1 = min(top, r0 + per);
-    int cnt = 0;
+    int ci = 0, ct = 0;
     for (int blk = r0; blk < r1; ++blk) {
       if (marks[blk - base]) {
-        const int len = min((blk + 1) * a.B, a.win_start) - max(blk * a.B, a.sink_end);
-        cnt += (len + kItemTokens - 1) / kItemTokens;
+        ++ci;
+        ct += min((blk + 1) * a.B, a.win_start) - max(blk * a.B, S);
       }
     }
-    const int incl = block_inclusive_scan(cnt, wave_tot);
-    int off = written + incl - cnt;
+    const int inc_i = block_inclusive_scan(ci, wave_tot);
+    const int inc_t = block_inclusive_scan(ct, wave_tot);
+    int oi = n_items + inc_i - ci, ot = n_tokens + inc_t - ct;
     for (int blk = r0; blk < r1; ++blk) {
       const uint32_t mk = marks[blk - base];
       if (!mk) continue;
-      const int lo_t = max(blk * a.B, a.sink_end);
-      const int hi_t = min((blk + 1) * a.B, a.win_start);
-      for (int p = lo_t; p < hi_t; p += kItemTokens) plan[1 + off++] = make_int4(p, min(kItemTokens, hi_t - p), (int)mk, 0);
+      const int lo_t = max(blk * a.B, S);
+      const int len = min((blk + 1) * a.B, a.win_start) - lo_t;
+      items[oi] = make_int4(lo_t, len, (int)mk, ot);
+      mark_chunks(first, oi, ot, len, CH);
+      ++oi;
+      ot += len;
     }
-    if (tid == nt - 1) sh_total = incl;
+    if (tid == nt - 1) {
+      sh_items = inc_i;
+      sh_tokens = inc_t;
+    }
     __syncthreads();
-    written += sh_total;
+    n_items += sh_items;
+    n_tokens += sh_tokens;
     __syncthreads();
   }
-  if (tid == 0) plan[0] = make_int4(written, 0, 0, 0);
+  if (tid == 0) a.hdr[bg] = make_int4(n_items, n_tokens, 0, 0);
+  // chunk descriptors: every chunk c < max_chunks gets one (empty beyond the last)
+  __syncthreads();
+  const int n_chunks = (n_tokens + CH - 1) / CH;
+  int4* chunks = a.chunks + (int64_t)bg * a.max_chunks;
+  for (int c = tid; c < a.max_chunks; c += nt) {
+    if (c < n_chunks)
+      chunks[c] = make_int4(first[c], c + 1 < n_chunks ? first[c + 1] + 1 : n_items, min((c + 1) * CH, n_tokens), 0);
+    else
+      chunks[c] = make_int4(0, 0, 0, 0);
+  }
+  if (n_tokens == 0) {
+    // nothing to attend for this (batch, kv head): its rows are zeros
+    const int rows = a.G * a.n_q;
+    float* o = a.out + (((int64_t)b * a.hq + g * a.G) * a.n_q) * a.d;
+    for (int i = tid; i < rows * a.d; i += nt) o[i] = 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -119,16 +195,19 @@ struct SplitArgs {
   const void* k;
   const void* v;
   const void* q;
-  const int4* plan;
+  const int4* hdr;
+  const int4* items;
+  const int4* chunks;
   float2* ml;
   float* o;
   int64_t max_items;
+  int max_chunks;
   int64_t head_stride;
   int row_stride;
   int hq, hkv, G, n_q, N, d;
   float qscale;
-  int ipw, nw, max_chunks;
-  int rows, rows_per_group;
+  int chunk_tokens, wave_tokens, nw;
+  int rows, rows_per_group, row_groups;
 };
 
 template <typename T>
@@ -158,73 +237,149 @@ struct Elt<float> {
   __device__ static float load(const float* p) { return *p; }
 };
 
-// Writes the workgroup's combined partial for each active row.  o_lane holds
-// this lane's DPL dims [sub*DPL, sub*DPL+DPL) for each row; rows beyond
-// `rows` are ignored.
-template <int D, int DPL, int ROWS>
-__device__ void write_partials(const SplitArgs& a, int bg, int c, int rg, int rows_here, float (&m)[ROWS],
-                               float (&l)[ROWS], float (&o)[ROWS][DPL], int slot, int sub, int wave, int nw) {
-  __shared__ float s_o[4][ROWS][D];
-  __shared__ float s_m[4][ROWS];
-  __shared__ float s_l[4][ROWS];
-  if (slot == 0) {
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) s_o[wave][r][sub * DPL + e] = o[r][e];
-      if (sub == 0) {
-        s_m[wave][r] = m[r];
-        s_l[wave][r] = l[r];
-      }
-    }
+__device__ __forceinline__ int64_t row_index(const SplitArgs& a, int b, int g, int gr) {
+  const int j = gr / a.n_q, i = gr - j * a.n_q;
+  return ((int64_t)b * a.hq + g * a.G + j) * a.n_q + i;
+}
+
+// The segments of one chunk, staged in LDS (the chunk size is capped so that
+// they always fit).  A cursor walks them as the flattened token index grows.
+__device__ __forceinline__ int stage_items(const SplitArgs& a, int bg, const int4& desc, int4* lds) {
+  const int4* g = a.items + (int64_t)bg * a.max_items;
+  const int ns = min(desc.y - desc.x, kItemsLds);
+  for (int j = threadIdx.x; j < ns; j += blockDim.x) lds[j] = g[desc.x + j];
+  __syncthreads();
+  return ns;
+}
+
+// ---------------------------------------------------------------------------
+// merge: one workgroup per query row.
+//   out = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  M = max_c m_c.
+// Chunks are split into `slices` interleaved runs whose loads are all in
+// flight; runs are summed in increasing slice order (deterministic).
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
   }
   __syncthreads();
-  const int b = bg / a.hkv, g = bg - b * a.hkv;
-  for (int t = threadIdx.x; t < rows_here * D; t += blockDim.x) {
-    const int r = t / D, e = t - r * D;
-    float M = kNegInf;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][r]);
-    float Ls = 0.f, Os = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float mw = s_m[w][r];
-      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - M);
-      Ls += s_l[w][r] * f;
-      Os += s_o[w][r][e] * f;
+  if (lane == 0) tmp[wave] = v;
+  __syncthreads();
+  v = tmp[0];
+  for (int w = 1; w < nwaves; ++w) v = is_max ? fmaxf(v, tmp[w]) : v + tmp[w];
+  return v;
+}
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict__ hdr, const float2* __restrict__ ml,
+                                                        const float* __restrict__ o, float* __restrict__ out, int hq,
+                                                        int hkv, int n_q, int d, int chunk_tokens, int max_chunks) {
+  __shared__ float tmp[16];
+  __shared__ float sh_w[kMergeC];
+  __shared__ float4 red[256];
+  const int64_t row = blockIdx.x;  // ((b * hq + h) * n_q + i)
+  const int64_t bh = row / n_q;
+  const int b = (int)(bh / hq), h = (int)(bh - (int64_t)b * hq);
+  const int bg = b * hkv + h / (hq / hkv);
+  const int n_tokens = hdr[bg].y;
+  if (n_tokens == 0) return;  // the plan kernel wrote zeros
+  const int n_chunks = min((n_tokens + chunk_tokens - 1) / chunk_tokens, max_chunks);
+  const float2* mlr = ml + row * max_chunks;
+  float M = kNegInf;
+  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) M = fmaxf(M, mlr[c].x);
+  M = block_reduce(M, true, tmp);
+  float L = 0.f;
+  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
+    const float2 v = mlr[c];
+    if (v.x != kNegInf) L += v.y * exp2f(v.x - M);
+  }
+  L = block_reduce(L, false, tmp);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int c = threadIdx.x; c < min(n_chunks, kMergeC); c += blockDim.x) {
+    const float mc = mlr[c].x;
+    sh_w[c] = (mc == kNegInf) ? 0.f : exp2f(mc - M) * inv;
+  }
+  __syncthreads();
+  auto weight = [&](int c) -> float {
+    if (c < kMergeC) return sh_w[c];
+    const float mc = mlr[c].x;
+    return (mc == kNegInf) ? 0.f : exp2f(mc - M) * inv;
+  };
+  const float* ob = o + row * max_chunks * (int64_t)d;
+  if ((d & 3) == 0 && d / 4 <= (int)blockDim.x) {
+    const int D4 = d >> 2;
+    const int slices = blockDim.x / D4;
+    const int e4 = threadIdx.x % D4, sl = threadIdx.x / D4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sl < slices) {
+      const float4* p = reinterpret_cast<const float4*>(ob) + e4;
+#pragma unroll 8
+      for (int c = sl; c < n_chunks; c += slices) {
+        const float w = weight(c);
+        const float4 v = p[(int64_t)c * D4];
+        acc.x = fmaf(v.x, w, acc.x);
+        acc.y = fmaf(v.y, w, acc.y);
+        acc.z = fmaf(v.z, w, acc.z);
+        acc.w = fmaf(v.w, w, acc.w);
+      }
     }
-    const int gr = rg * a.rows_per_group + r;
-    const int j = gr / a.n_q, i = gr - j * a.n_q;
-    const int64_t row = ((int64_t)b * a.hq + g * a.G + j) * a.n_q + i;
-    const int64_t pidx = row * a.max_chunks + c;
-    a.o[pidx * D + e] = Os;
-    if (e == 0) a.ml[pidx] = make_float2(M, Ls);
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < D4) {
+      float4 t = red[threadIdx.x];
+      for (int s2 = 1; s2 < slices; ++s2) {
+        const float4 v = red[s2 * D4 + threadIdx.x];
+        t.x += v.x;
+        t.y += v.y;
+        t.z += v.z;
+        t.w += v.w;
+      }
+      reinterpret_cast<float4*>(out + row * d)[threadIdx.x] = t;
+    }
+    return;
+  }
+  for (int e = threadIdx.x; e < d; e += blockDim.x) {
+    float acc = 0.f;
+    for (int c = 0; c < n_chunks; ++c) acc = fmaf(ob[(int64_t)c * d + e], weight(c), acc);
+    out[row * d + e] = acc;
   }
 }
 
 // Fast path: D = head_dim, rows 16-byte aligned.  L = D / DPL lanes share a
-// token (each loads DPL contiguous elements of the K row and of the V row),
-// TPS = 64 / L tokens per wave step, U steps in flight.
-template <typename T, int D, int DPL, int ROWS>
-__global__ __launch_bounds__(256) void attn_split_kernel(SplitArgs a) {
+// token; lane `sub` holds the 16-byte units sub, sub + L, ... of the row, so
+// each load instruction reads whole cache lines of every token.  TPS = 64 / L
+// tokens per wave step; steps are taken in groups of U and two groups are in
+// flight (one computed while the next loads).  Query logits use bf16 pair
+// dot products (exact products, float32 sums) for bfloat16 data.
+template <typename T, int DPL, int U>
+struct Group {
+  static constexpr int NU = DPL / Elt<T>::per16;
+  uint4 k[U][NU], v[U][NU];
+  int pos[U];
+  uint32_t msk[U];
+};
+
+template <typename T, int D, int DPL, int ROWS, int U, int NWMAX>
+__global__ __launch_bounds__(64 * NWMAX) void attn_split_kernel(SplitArgs a) {
   constexpr int L = D / DPL;
   constexpr int TPS = 64 / L;
-  constexpr int NU = DPL / Elt<T>::per16;  // 16-byte units per lane per row
-  constexpr int U = 2;
+  constexpr int E16 = Elt<T>::per16;        // elements per 16-byte unit
+  constexpr int NU = DPL / E16;             // units per lane per row
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int QW = BF ? DPL / 2 : DPL;    // query registers per row
   static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "lanes per token");
-  static_assert(NU >= 1 && NU * Elt<T>::per16 == DPL, "16-byte units");
+  static_assert(NU >= 1 && NU * E16 == DPL, "16-byte units");
+  __shared__ int4 s_items[kItemsLds];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / L, sub = lane % L;
   const int c = blockIdx.x, bg = blockIdx.y, rg = blockIdx.z;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
-  const int4* plan = a.plan + (int64_t)bg * (1 + a.max_items);
-  const int n_items = min((int64_t)plan[0].x, a.max_items);
-  const int it0 = c * a.ipw;
-  if (it0 >= n_items) return;
-  const int it1 = min(it0 + a.ipw, n_items);
   const int rows_here = min(a.rows_per_group, a.rows - rg * a.rows_per_group);
 
-  // query rows of this group, pre-multiplied by scale * log2(e)
-  float qf[ROWS][DPL];
+  // query rows of this group (independent of the plan: issued first)
+  uint32_t qw[ROWS][QW];
   uint32_t rowbit[ROWS];
   int plim[ROWS];
 #pragma unroll
@@ -234,15 +389,21 @@ __global__ __launch_bounds__(256) void attn_split_kernel(SplitArgs a) {
     const int j = act ? gr / a.n_q : 0, i = act ? gr - j * a.n_q : 0;
     rowbit[r] = act ? (1u << j) : 0u;
     plim[r] = a.N - a.n_q + i;
-    const T* qrow = (const T*)a.q + (((int64_t)b * a.hq + g * a.G + j) * a.n_q + i) * D + sub * DPL;
+    const T* qrow = (const T*)a.q + (((int64_t)b * a.hq + g * a.G + j) * a.n_q + i) * D + sub * E16;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      uint4 raw = act ? *reinterpret_cast<const uint4*>(qrow + u * Elt<T>::per16) : make_uint4(0, 0, 0, 0);
-      Elt<T>::unpack(raw, &qf[r][u * Elt<T>::per16]);
+      const uint4 raw = act ? *reinterpret_cast<const uint4*>(qrow + u * L * E16) : make_uint4(0, 0, 0, 0);
+      qw[r][4 * u] = raw.x;
+      qw[r][4 * u + 1] = raw.y;
+      qw[r][4 * u + 2] = raw.z;
+      qw[r][4 * u + 3] = raw.w;
     }
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) qf[r][e] *= a.qscale;
   }
+
+  const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
+  if (desc.x >= desc.y) return;  // past the end of this (batch, kv head)'s tokens
+  const int ns = stage_items(a, bg, desc, s_items);
+  const int t0 = c * a.chunk_tokens;
 
   float m[ROWS], l[ROWS], o[ROWS][DPL];
 #pragma unroll
@@ -253,79 +414,111 @@ __global__ __launch_bounds__(256) void attn_split_kernel(SplitArgs a) {
     for (int e = 0; e < DPL; ++e) o[r][e] = 0.f;
   }
 
-  const T* kb = (const T*)a.k + (int64_t)bg * a.head_stride + sub * DPL;
-  const T* vb = (const T*)a.v + (int64_t)bg * a.head_stride + sub * DPL;
+  const T* kb = (const T*)a.k + (int64_t)bg * a.head_stride + sub * E16;
+  const T* vb = (const T*)a.v + (int64_t)bg * a.head_stride + sub * E16;
+  const float qs = a.qscale;
 
-  for (int it = it0 + wave; it < it1; it += a.nw) {
-    const int4 item = plan[1 + it];
-    const int pos0 = item.x, len = item.y;
-    const uint32_t mask = (uint32_t)item.z;
-    for (int t0 = 0; t0 < len; t0 += TPS * U) {
-      uint4 kr[U][NU], vr[U][NU];
-      int pos[U];
-      bool val[U];
+  // this wave's run of the flattened token list
+  const int w0 = t0 + wave * a.wave_tokens;
+  const int w1 = min(w0 + a.wave_tokens, desc.z);
+  int cur = 0;
+  int4 it = s_items[0];
+
+  auto load = [&](Group<T, DPL, U>& gr, int tb) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = t0 + u * TPS + slot;
-        val[u] = t < len;
-        pos[u] = pos0 + t;
-        const int64_t off = (int64_t)(val[u] ? pos[u] : pos0) * a.row_stride;
-#pragma unroll
-        for (int w = 0; w < NU; ++w) {
-          kr[u][w] = *reinterpret_cast<const uint4*>(kb + off + w * Elt<T>::per16);
-          vr[u][w] = *reinterpret_cast<const uint4*>(vb + off + w * Elt<T>::per16);
-        }
+    for (int u = 0; u < U; ++u) {
+      const int tau = tb + u * TPS + slot;
+      bool val = tau < w1;
+      if (val) {
+        while (tau >= it.w + it.y && cur + 1 < ns) it = s_items[++cur];
+        val = tau >= it.w && tau < it.w + it.y;
       }
-      float s[U][ROWS];
+      gr.pos[u] = it.x + (tau - it.w);
+      gr.msk[u] = val ? (uint32_t)it.z : 0u;
+      const int64_t off = (int64_t)(val ? gr.pos[u] : it.x) * a.row_stride;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float kf[DPL];
+      for (int w = 0; w < NU; ++w) gr.k[u][w] = *reinterpret_cast<const uint4*>(kb + off + w * L * E16);
 #pragma unroll
-        for (int w = 0; w < NU; ++w) Elt<T>::unpack(kr[u][w], &kf[w * Elt<T>::per16]);
+      for (int w = 0; w < NU; ++w) gr.v[u][w] = *reinterpret_cast<const uint4*>(vb + off + w * L * E16);
+    }
+  };
+
+  auto compute = [&](const Group<T, DPL, U>& gr) {
+    float s[U][ROWS];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          float acc = 0.f;
+    for (int u = 0; u < U; ++u) {
+      uint32_t kw[4 * NU];
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc = fmaf(qf[r][e], kf[e], acc);
-#pragma unroll
-          for (int off = 1; off < L; off <<= 1) acc += __shfl_xor(acc, off);
-          const bool pass = val[u] && (mask & rowbit[r]) && pos[u] <= plim[r];
-          s[u][r] = pass ? acc : kNegInf;
-        }
+      for (int w = 0; w < NU; ++w) {
+        kw[4 * w] = gr.k[u][w].x;
+        kw[4 * w + 1] = gr.k[u][w].y;
+        kw[4 * w + 2] = gr.k[u][w].z;
+        kw[4 * w + 3] = gr.k[u][w].w;
       }
-      bool grow = false;
-      float mt[ROWS];
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
-        mt[r] = m[r];
+        float acc = 0.f;
+        if constexpr (BF) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) mt[r] = fmaxf(mt[r], s[u][r]);
-        grow |= mt[r] > m[r];
-      }
-      if (__ballot(grow)) {
+          for (int e = 0; e < QW; ++e)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[r][e]),
+                                                  __builtin_bit_cast(bf16x2_t, kw[e]), acc, false);
+        } else {
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          const float al = (mt[r] == m[r]) ? 1.f : exp2f(m[r] - mt[r]);
-          l[r] *= al;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[r][e] *= al;
-          m[r] = mt[r];
+          for (int e = 0; e < QW; ++e) acc = fmaf(__uint_as_float(qw[r][e]), __uint_as_float(kw[e]), acc);
         }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float vf[DPL];
-#pragma unroll
-        for (int w = 0; w < NU; ++w) Elt<T>::unpack(vr[u][w], &vf[w * Elt<T>::per16]);
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          const float p = (s[u][r] == kNegInf) ? 0.f : exp2f(s[u][r] - m[r]);
-          l[r] += p;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
-        }
+        acc = group_sum<L>(acc);
+        const bool pass = (gr.msk[u] & rowbit[r]) && gr.pos[u] <= plim[r];
+        s[u][r] = pass ? acc * qs : kNegInf;
       }
     }
+    bool grow = false;
+    float mt[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      mt[r] = m[r];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mt[r] = fmaxf(mt[r], s[u][r]);
+      grow |= mt[r] > m[r];
+    }
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const float al = (mt[r] == m[r]) ? 1.f : fast_exp2(m[r] - mt[r]);
+        l[r] *= al;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[r][e] *= al;
+        m[r] = mt[r];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[DPL];
+#pragma unroll
+      for (int w = 0; w < NU; ++w) Elt<T>::unpack(gr.v[u][w], &vf[w * E16]);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const float p = (s[u][r] == kNegInf) ? 0.f : fast_exp2(s[u][r] - m[r]);
+        l[r] += p;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+      }
+    }
+  };
+
+  constexpr int GT = TPS * U;  // tokens per group
+  Group<T, DPL, U> ga, gb;
+  int tb = w0;
+  if (tb < w1) load(ga, tb);
+  if (tb + GT < w1) load(gb, tb + GT);
+  while (tb < w1) {
+    compute(ga);
+    tb += GT;
+    if (tb + GT < w1) load(ga, tb + GT);
+    if (tb >= w1) break;
+    compute(gb);
+    tb += GT;
+    if (tb + GT < w1) load(gb, tb + GT);
   }
 
   // combine the TPS token slots of the wave (lanes with equal `sub`)
@@ -347,7 +540,40 @@ __global__ __launch_bounds__(256) void attn_split_kernel(SplitArgs a) {
       m[r] = M;
     }
   }
-  write_partials<D, DPL, ROWS>(a, bg, c, rg, rows_here, m, l, o, slot, sub, wave, a.nw);
+
+  // combine the waves of the workgroup in LDS and write this chunk's partials
+  __shared__ float s_o[NWMAX][ROWS][D];
+  __shared__ float s_m[NWMAX][ROWS];
+  __shared__ float s_l[NWMAX][ROWS];
+  if (slot == 0) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+#pragma unroll
+      for (int w = 0; w < NU; ++w)
+#pragma unroll
+        for (int e = 0; e < E16; ++e) s_o[wave][r][(w * L + sub) * E16 + e] = o[r][w * E16 + e];
+      if (sub == 0) {
+        s_m[wave][r] = m[r];
+        s_l[wave][r] = l[r];
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < rows_here * D; t += blockDim.x) {
+    const int r = t / D, e = t - r * D;
+    float M = kNegInf;
+    for (int w = 0; w < a.nw; ++w) M = fmaxf(M, s_m[w][r]);
+    float Ls = 0.f, Os = 0.f;
+    for (int w = 0; w < a.nw; ++w) {
+      const float mw = s_m[w][r];
+      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - M);
+      Ls += s_l[w][r] * f;
+      Os += s_o[w][r][e] * f;
+    }
+    const int64_t pidx = row_index(a, b, g, rg * a.rows_per_group + r) * a.max_chunks + c;
+    a.o[pidx * D + e] = Os;
+    if (e == 0) a.ml[pidx] = make_float2(M, Ls);
+  }
 }
 
 // Any head_dim <= 512 and any row stride: one token at a time per wave,
@@ -355,16 +581,17 @@ __global__ __launch_bounds__(256) void attn_split_kernel(SplitArgs a) {
 template <typename T>
 __global__ __launch_bounds__(64) void attn_split_generic_kernel(SplitArgs a) {
   constexpr int NE = 8;  // dims per lane, head_dim <= 512
+  __shared__ int4 s_items[kItemsLds];
   const int lane = threadIdx.x;
   const int c = blockIdx.x, bg = blockIdx.y, rg = blockIdx.z;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
-  const int4* plan = a.plan + (int64_t)bg * (1 + a.max_items);
-  const int n_items = min((int64_t)plan[0].x, a.max_items);
-  const int it0 = c * a.ipw;
-  if (it0 >= n_items) return;
-  const int it1 = min(it0 + a.ipw, n_items);
+  const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
+  if (desc.x >= desc.y) return;  // past the end of this (batch, kv head)'s tokens
+  const int t0 = c * a.chunk_tokens;
+  const int t1 = desc.z;
   const int rows_here = min(a.rows_per_group, a.rows - rg * a.rows_per_group);
   const int D = a.d;
+  const int ns = stage_items(a, bg, desc, s_items);
 
   float qf[kRowsMax][NE], m[kRowsMax], l[kRowsMax], o[kRowsMax][NE];
   uint32_t rowbit[kRowsMax];
@@ -380,7 +607,7 @@ __global__ __launch_bounds__(64) void attn_split_generic_kernel(SplitArgs a) {
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
       const int e = lane + 64 * u;
-      qf[r][u] = (act && e < D) ? Elt<T>::load(qrow + e) * a.qscale : 0.f;
+      qf[r][u] = (act && e < D) ? Elt<T>::load(qrow + e) : 0.f;
       o[r][u] = 0.f;
     }
     m[r] = kNegInf;
@@ -388,40 +615,38 @@ __global__ __launch_bounds__(64) void attn_split_generic_kernel(SplitArgs a) {
   }
   const T* kb = (const T*)a.k + (int64_t)bg * a.head_stride;
   const T* vb = (const T*)a.v + (int64_t)bg * a.head_stride;
-  for (int it = it0; it < it1; ++it) {
-    const int4 item = plan[1 + it];
-    const uint32_t mask = (uint32_t)item.z;
-    for (int t = 0; t < item.y; ++t) {
-      const int pos = item.x + t;
-      float kf[NE], vf[NE];
+  int cur = 0;
+  int4 it = s_items[0];
+  for (int tau = t0; tau < t1; ++tau) {
+    while (tau >= it.w + it.y && cur + 1 < ns) it = s_items[++cur];
+    const bool val = tau >= it.w && tau < it.w + it.y;
+    const int pos = val ? it.x + (tau - it.w) : it.x;
+    const uint32_t mask = val ? (uint32_t)it.z : 0u;
+    float kf[NE], vf[NE];
 #pragma unroll
-      for (int u = 0; u < NE; ++u) {
-        const int e = lane + 64 * u;
-        kf[u] = e < D ? Elt<T>::load(kb + (int64_t)pos * a.row_stride + e) : 0.f;
-        vf[u] = e < D ? Elt<T>::load(vb + (int64_t)pos * a.row_stride + e) : 0.f;
-      }
+    for (int u = 0; u < NE; ++u) {
+      const int e = lane + 64 * u;
+      kf[u] = e < D ? Elt<T>::load(kb + (int64_t)pos * a.row_stride + e) : 0.f;
+      vf[u] = e < D ? Elt<T>::load(vb + (int64_t)pos * a.row_stride + e) : 0.f;
+    }
 #pragma unroll
-      for (int r = 0; r < kRowsMax; ++r) {
-        float acc = 0.f;
+    for (int r = 0; r < kRowsMax; ++r) {
+      float acc = 0.f;
 #pragma unroll
-        for (int u = 0; u < NE; ++u) acc = fmaf(qf[r][u], kf[u], acc);
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        const float sc = ((mask & rowbit[r]) && pos <= plim[r]) ? acc : kNegInf;
-        const float mn = fmaxf(m[r], sc);
-        const float al = (mn == m[r]) ? 1.f : exp2f(m[r] - mn);
-        const float p = (sc == kNegInf) ? 0.f : exp2f(sc - mn);
-        l[r] = l[r] * al + p;
+      for (int u = 0; u < NE; ++u) acc = fmaf(qf[r][u], kf[u], acc);
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      const float sc = ((mask & rowbit[r]) && pos <= plim[r]) ? acc * a.qscale : kNegInf;
+      const float mn = fmaxf(m[r], sc);
+      const float al = (mn == m[r]) ? 1.f : exp2f(m[r] - mn);
+      const float p = (sc == kNegInf) ? 0.f : exp2f(sc - mn);
+      l[r] = l[r] * al + p;
 #pragma unroll
-        for (int u = 0; u < NE; ++u) o[r][u] = o[r][u] * al + p * vf[u];
-        m[r] = mn;
-      }
+      for (int u = 0; u < NE; ++u) o[r][u] = o[r][u] * al + p * vf[u];
+      m[r] = mn;
     }
   }
   for (int r = 0; r < rows_here; ++r) {
-    const int gr = rg * a.rows_per_group + r;
-    const int j = gr / a.n_q, i = gr - j * a.n_q;
-    const int64_t row = ((int64_t)b * a.hq + g * a.G + j) * a.n_q + i;
-    const int64_t pidx = row * a.max_chunks + c;
+    const int64_t pidx = row_index(a, b, g, rg * a.rows_per_group + r) * a.max_chunks + c;
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
       const int e = lane + 64 * u;
@@ -432,65 +657,76 @@ __global__ __launch_bounds__(64) void attn_split_generic_kernel(SplitArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// merge: out = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M)
-
-__global__ __launch_bounds__(64) void attn_merge_kernel(const int4* __restrict__ plan, const float2* __restrict__ ml,
-                                                        const float* __restrict__ o, float* __restrict__ out,
-                                                        int64_t max_items, int hq, int hkv, int n_q, int d,
-                                                        int ipw, int max_chunks) {
-  const int64_t row = blockIdx.x;  // ((b * hq + h) * n_q + i)
-  const int lane = threadIdx.x;
-  const int64_t bh = row / n_q;
-  const int b = (int)(bh / hq), h = (int)(bh - (int64_t)b * hq);
-  const int G = hq / hkv;
-  const int bg = b * hkv + h / G;
-  const int n_items = (int)min((int64_t)plan[(int64_t)bg * (1 + max_items)].x, max_items);
-  const int nch = (n_items + ipw - 1) / ipw;
-  const float2* mlr = ml + row * max_chunks;
-  float M = kNegInf;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, mlr[c].x);
-  float Ls = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float2 v = mlr[c];
-    if (v.x != kNegInf) Ls += v.y * exp2f(v.x - M);
-  }
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  for (int e = lane; e < d; e += 64) {
-    float acc = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float mc = mlr[c].x;
-      if (mc != kNegInf) acc += o[(row * max_chunks + c) * d + e] * exp2f(mc - M);
-    }
-    out[row * d + e] = acc * inv;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dispatch
 
-template <typename T, int D, int ROWS>
+template <typename T, int ROWS>
 constexpr int dpl_for() {
   return ROWS <= 4 ? 32 / (int)sizeof(T) : 16 / (int)sizeof(T);
+}
+
+template <int D, int ROWS>
+constexpr int nwmax_for() {
+  return ROWS * D <= 1024 ? 8 : 4;
+}
+
+// elements per lane for <= 4 rows: 16 bytes (16 lanes per 128-dim bf16 row:
+// fewer registers, more waves) by default; BRS_NARROW=0 uses 32 bytes
+bool split_narrow() { return env_int("BRS_NARROW", 1) == 1; }
+
+int split_u() {
+  const int u = env_int("BRS_U", 2);
+  return (u == 1 || u == 4) ? u : 2;
+}
+
+// tokens of one group of the vector kernel (TPS * U)
+int step_tokens(const AttnGeom& g) {
+  const int es = elem_bytes(g.dtype);
+  const int rows = g.rows_per_group;
+  const int dpl = (rows <= 4 && !split_narrow()) ? 32 / es : 16 / es;
+  const int L = g.d / dpl;
+  return (64 / L) * split_u();
+}
+
+int nw_max(const AttnGeom& g) {
+  const int R = g.rows_per_group <= 1 ? 1 : g.rows_per_group <= 2 ? 2 : g.rows_per_group <= 4 ? 4 : 8;
+  return R * g.d <= 1024 ? 8 : 4;
 }
 
 template <typename T, int D>
 bool launch_fast_d(const AttnGeom& g, dim3 grid, dim3 block, hipStream_t s, const SplitArgs& a, hipEvent_t ev0,
                    hipEvent_t ev1) {
   const int rows = g.rows_per_group;
+  const int u = split_u();
+#define BRS_LAUNCH_U(R, UU)                                                                                   \
+  if (R <= 4 && split_narrow()) {                                                                             \
+    constexpr int DPL = 16 / (int)sizeof(T);                                                                  \
+    constexpr int NWM = nwmax_for<D, R>();                                                                    \
+    if (ev0)                                                                                                  \
+      hipExtLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, ev0, ev1, 0, a);   \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, a);                   \
+    return true;                                                                                              \
+  } else {                                                                                                    \
+    constexpr int DPL = dpl_for<T, R>();                                                                      \
+    constexpr int NWM = nwmax_for<D, R>();                                                                    \
+    if (ev0)                                                                                                  \
+      hipExtLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, ev0, ev1, 0, a);   \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, a);                   \
+    return true;                                                                                              \
+  }
 #define BRS_LAUNCH_ROWS(R)                                                                                    \
   if (rows <= R) {                                                                                            \
-    constexpr int DPL = dpl_for<T, D, R>();                                                                   \
-    if (ev0)                                                                                                  \
-      hipExtLaunchKernelGGL((attn_split_kernel<T, D, DPL, R>), grid, block, 0, s, ev0, ev1, 0, a);            \
-    else                                                                                                      \
-      hipLaunchKernelGGL((attn_split_kernel<T, D, DPL, R>), grid, block, 0, s, a);                            \
-    return true;                                                                                              \
+    if (u == 1) BRS_LAUNCH_U(R, 1)                                                                            \
+    if (u == 4) BRS_LAUNCH_U(R, 4)                                                                            \
+    BRS_LAUNCH_U(R, 2)                                                                                        \
   }
   BRS_LAUNCH_ROWS(1)
   BRS_LAUNCH_ROWS(2)
   BRS_LAUNCH_ROWS(4)
   BRS_LAUNCH_ROWS(8)
 #undef BRS_LAUNCH_ROWS
+#undef BRS_LAUNCH_U
   return false;
 }
 
@@ -506,64 +742,92 @@ bool fast_supported(const AttnGeom& g) {
 bool attn_geometry(AttnGeom& g) {
   if (g.d > 512) return false;
   const int64_t E = g.idx_heads == 1 ? (int64_t)g.k : (int64_t)g.group * g.k;
-  const int64_t n_sh = (g.sink_end + kItemTokens - 1) / kItemTokens + (g.N - g.win_start + kItemTokens - 1) / kItemTokens;
-  const int64_t per_block = (g.B + kItemTokens - 1) / kItemTokens;
   const int64_t uniq = E < g.nb ? E : g.nb;
-  g.max_items = n_sh + uniq * per_block;
   const int rows = g.group * g.n_q;
   g.row_groups = (rows + kRowsMax - 1) / kRowsMax;
   g.rows_per_group = rows < kRowsMax ? rows : kRowsMax;
   const int64_t bg = (int64_t)g.batch * g.hkv;
-  const int64_t work = g.max_items * bg * g.row_groups;  // items over all workgroups
-  if (!fast_supported(g)) {
-    g.nw = 1;
-    g.ipw = 1;
-  } else {
-    int64_t per_wave = work / 2048;
-    per_wave = per_wave < 1 ? 1 : (per_wave > 8 ? 8 : per_wave);
-    g.nw = (work / per_wave >= 4096) ? 4 : 1;
-    g.ipw = (int)(per_wave * g.nw);
+  g.fast = fast_supported(g);
+  g.max_items = 2 + uniq;
+  g.max_tokens = (int64_t)g.sink_end + (g.N - g.win_start) + uniq * g.B;
+  if (g.max_tokens > INT32_MAX) return false;
+  // tokens per wave: about kTargetWaves waves over the whole problem, in whole steps
+  const int64_t total = g.max_tokens * bg * g.row_groups;
+  const int st = g.fast ? step_tokens(g) : 1;
+  const int target = env_int("BRS_TARGET_WAVES", kTargetWaves);
+  int64_t wt = (total + target - 1) / target;
+  wt = ((wt + st - 1) / st) * st;
+  const int64_t wmin = g.fast ? 2 * st : 16;
+  wt = wt < wmin ? wmin : (wt > 4096 ? 4096 : wt);
+  g.wave_tokens = (int)wt;
+  const int64_t waves = (total + wt - 1) / wt;
+  g.nw = !g.fast ? 1 : (waves >= 2048 ? nw_max(g) : (waves >= 1024 ? 4 : 1));
+  if (g.fast) {
+    const int nw_env = env_int("BRS_NW", 0);
+    if (nw_env == 1 || nw_env == 2 || nw_env == 4 || (nw_env == 8 && nw_max(g) == 8)) g.nw = nw_env;
   }
-  g.max_chunks = (int)((g.max_items + g.ipw - 1) / g.ipw);
-  if (g.max_chunks < 1) g.max_chunks = 1;
+  // a chunk meets at most chunk_tokens / B + 6 segments (sinks, window, the two
+  // blocks cut by them, whole blocks, one more at each end): keep them in LDS
+  const int64_t cap = (int64_t)(kItemsLds - 8) * g.B;
+  while ((int64_t)g.nw * g.wave_tokens > cap && g.wave_tokens > st) g.wave_tokens -= st;
+  while ((int64_t)g.nw * g.wave_tokens > cap && g.nw > 1) g.nw >>= 1;
+  if ((int64_t)g.nw * g.wave_tokens > cap) return false;
+  g.chunk_tokens = g.nw * g.wave_tokens;
+  int64_t mc = (g.max_tokens + g.chunk_tokens - 1) / g.chunk_tokens;
+  g.max_chunks = (int)(mc < 1 ? 1 : mc);
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows_total = (size_t)g.batch * g.hq * g.n_q;
-  g.plan_off = 0;
-  g.ml_off = up((size_t)bg * (1 + g.max_items) * sizeof(int4));
+  g.hdr_off = 0;
+  g.items_off = up((size_t)bg * sizeof(int4));
+  g.first_off = g.items_off + up((size_t)bg * g.max_items * sizeof(int4));
+  g.chunks_off = g.first_off + up((size_t)bg * g.max_chunks * sizeof(int));
+  g.ml_off = g.chunks_off + up((size_t)bg * g.max_chunks * sizeof(int4));
   g.o_off = g.ml_off + up(rows_total * g.max_chunks * sizeof(float2));
   g.total = g.o_off + up(rows_total * g.max_chunks * (size_t)g.d * sizeof(float));
   return true;
 }
 
-hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, hipStream_t s) {
+hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, float* out, hipStream_t s) {
   PlanArgs a;
   a.idx = idx;
-  a.plan = (int4*)((char*)ws + g.plan_off);
+  a.hdr = (int4*)((char*)ws + g.hdr_off);
+  a.items = (int4*)((char*)ws + g.items_off);
+  a.chunk_first = (int*)((char*)ws + g.first_off);
+  a.chunks = (int4*)((char*)ws + g.chunks_off);
+  a.out = out;
   a.max_items = g.max_items;
+  a.max_chunks = g.max_chunks;
   a.hq = g.hq;
   a.hkv = g.hkv;
   a.G = g.group;
   a.k = idx ? g.k : 0;
   a.idx_heads = g.idx_heads;
+  a.n_q = g.n_q;
+  a.d = g.d;
+  a.row_groups = g.row_groups;
   a.N = g.N;
   a.B = g.B;
   a.nb = g.nb;
   a.sink_end = g.sink_end;
   a.win_start = g.win_start;
+  a.chunk_tokens = g.chunk_tokens;
   hipLaunchKernelGGL(attn_plan_kernel, dim3((unsigned)(g.batch * g.hkv)), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
+hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws, float* out,
                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   SplitArgs a;
   a.k = k;
   a.v = v;
   a.q = q;
-  a.plan = (const int4*)((char*)ws + g.plan_off);
+  a.hdr = (const int4*)((char*)ws + g.hdr_off);
+  a.items = (const int4*)((char*)ws + g.items_off);
+  a.chunks = (const int4*)((char*)ws + g.chunks_off);
   a.ml = (float2*)((char*)ws + g.ml_off);
   a.o = (float*)((char*)ws + g.o_off);
   a.max_items = g.max_items;
+  a.max_chunks = g.max_chunks;
   a.head_stride = g.head_stride;
   a.row_stride = g.row_stride;
   a.hq = g.hq;
@@ -573,13 +837,14 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   a.N = g.N;
   a.d = g.d;
   a.qscale = g.qscale;
-  a.ipw = g.ipw;
+  a.chunk_tokens = g.chunk_tokens;
+  a.wave_tokens = g.wave_tokens;
   a.nw = g.nw;
-  a.max_chunks = g.max_chunks;
   a.rows = g.group * g.n_q;
   a.rows_per_group = g.rows_per_group;
+  a.row_groups = g.row_groups;
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
-  if (fast_supported(g)) {
+  if (g.fast) {
     const dim3 block(64 * g.nw);
     bool done = false;
     if (g.dtype == BRS_BF16) {
@@ -608,10 +873,9 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
 
 hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s) {
   const int64_t rows = (int64_t)g.batch * g.hq * g.n_q;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows), dim3(64), 0, s,
-                     (const int4*)((char*)ws + g.plan_off), (const float2*)((char*)ws + g.ml_off),
-                     (const float*)((char*)ws + g.o_off), out, g.max_items, g.hq, g.hkv, g.n_q, g.d, g.ipw,
-                     g.max_chunks);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows), dim3(256), 0, s, (const int4*)((char*)ws + g.hdr_off),
+                     (const float2*)((char*)ws + g.ml_off), (const float*)((char*)ws + g.o_off), out, g.hq, g.hkv,
+                     g.n_q, g.d, g.chunk_tokens, g.max_chunks);
   return hipGetLastError();
 }
 

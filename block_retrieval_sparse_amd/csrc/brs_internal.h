@@ -56,15 +56,15 @@ __device__ inline int block_inclusive_scan(int v, int* wave_tot /* [16] shared *
 // ---------------------------------------------------------------------------
 // attention plan
 //
-// For every (batch, kv head) the plan kernel writes a list of work items.
-// An item is a contiguous span of token rows that some of the group's query
-// heads attend: (first row, token count, head mask).  Items never overlap,
-// so every attended token is visited once per (batch, kv head) no matter how
-// many query heads selected its block (the K/V bytes of a block shared by
-// several heads are read once).  Item 0 of each list is a header holding the
-// item count.
+// For every (batch, kv head) the plan kernel writes the attended token set as
+// a list of disjoint segments (first row, length, head mask, offset in the
+// flattened list): the sinks, the window, then every selected block clipped
+// against both, in block order.  Each token appears once per (batch, kv
+// head) however many query heads selected its block, so the K/V bytes of a
+// block shared by several heads are read once.  The flattened list is cut
+// into equal chunks of chunk_tokens; chunk_first[c] names the segment that
+// holds the first token of chunk c.
 
-constexpr int kItemTokens = 128;   // longest item
 constexpr int kMarkBlocks = 8192;  // blocks marked per pass of the plan kernel
 constexpr int kRowsMax = 8;        // query rows one split workgroup handles
 
@@ -77,22 +77,25 @@ struct AttnGeom {
   int64_t head_stride;    // elements between consecutive (batch, kv head) slices of k / v
   float qscale;           // softmax scale * log2(e)
   // decomposition
-  int64_t max_items;
+  bool fast;              // head_dim and row layout served by the vector kernel
+  int64_t max_items;      // segments per (batch, kv head)
+  int64_t max_tokens;     // bound on attended tokens per (batch, kv head)
   int nw;                 // waves per split workgroup
-  int ipw;                // items per split workgroup
-  int max_chunks;         // split workgroups per (batch, kv head)
+  int wave_tokens;        // tokens per wave
+  int chunk_tokens;       // nw * wave_tokens
+  int max_chunks;         // split workgroups per (batch, kv head, row group)
   int row_groups;         // ceil(group * n_q / kRowsMax)
   int rows_per_group;
   // workspace offsets (bytes)
-  size_t plan_off, ml_off, o_off, total;
+  size_t hdr_off, items_off, first_off, chunks_off, ml_off, o_off, total;
 };
 
 // Fills the decomposition and workspace layout; returns false if unsupported.
 bool attn_geometry(AttnGeom& g);
 
-hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, hipStream_t s);
+hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, float* out, hipStream_t s);
 hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
-                             hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+                             float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q,
                                const int32_t* idx, float* out, hipStream_t s, hipEvent_t ev0,

@@ -125,6 +125,80 @@ __global__ __launch_bounds__(256) void score_dot_kernel(const T* __restrict__ q,
   }
 }
 
+// Row-granular variant, used when R divides the slots of a wave: each slot
+// (L lanes) takes one representative row, RPS rows in flight per slot, and a
+// block's R rows sit in R adjacent slots, so the max over representatives is
+// a shuffle.  Rows of one (batch, kv head) are contiguous in memory.
+template <typename T, int EPL, int G, int L, int RPS>
+__global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict__ q, const T* __restrict__ reps,
+                                                             float* __restrict__ scores, int d, int R, int hkv,
+                                                             int64_t capB, int64_t lo, int64_t hi) {
+  constexpr int UPL = EPL / Vec<T>::n;
+  constexpr int SPW = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int sw = lane / L, sub = lane % L;
+  const int slot = (threadIdx.x >> 6) * SPW + sw;
+  const int slots = (blockDim.x >> 6) * SPW;
+  const int bg = blockIdx.y;
+  const int b = bg / hkv, g = bg - b * hkv;
+  const int hq = hkv * G;
+
+  double qd[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const T* qrow = q + ((int64_t)b * hq + g * G + j) * d + sub * EPL;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + u * Vec<T>::n);
+      Vec<T>::to_f64(raw, &qd[j][u * Vec<T>::n]);
+    }
+  }
+  const int64_t row_lo = lo * R, row_hi = hi * R;
+  const int64_t row0 = row_lo + (int64_t)blockIdx.x * slots * RPS;
+  const T* rbase = reps + (int64_t)bg * capB * R * d + sub * EPL;
+  float* sbase = scores + ((int64_t)b * hq + g * G) * capB;
+
+  uint4 raw[RPS][UPL];
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    const int64_t row = row0 + (int64_t)i * slots + slot;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u)
+      raw[i][u] = row < row_hi ? *reinterpret_cast<const uint4*>(rbase + row * d + u * Vec<T>::n)
+                               : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    const int64_t row = row0 + (int64_t)i * slots + slot;
+    double x[EPL];
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) Vec<T>::to_f64(raw[i][u], &x[u * Vec<T>::n]);
+    double acc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      double a = 0.0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = fma(qd[j][e], x[e], a);
+      acc[j] = a;
+    }
+#pragma unroll
+    for (int off = 1; off < L; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] += __shfl_xor(acc[j], off);
+    }
+    for (int off = L; off < L * R; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] = nan_max(acc[j], __shfl_xor(acc[j], off));
+    }
+    if (row < row_hi && (row % R) == 0) {
+      const int64_t blk = row / R;
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)acc[j];
+    }
+  }
+}
+
 // Any shape: one wave per block, lanes stride over the elements, up to 32
 // query heads per kv head.
 template <typename T>
@@ -197,6 +271,47 @@ hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, f
   return hipGetLastError();
 }
 
+template <typename T, int EPL, int G, int L>
+hipError_t run_rows(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
+  constexpr int slots = 4 * (64 / L);
+  const int64_t rows = (hi - lo) * m.reps_per_block;
+  const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
+  const int64_t want = rows * bg / (slots * 2048);
+  const dim3 block(256);
+  const int64_t capB = m.capacity / m.block_size;
+  if (want >= 4) {
+    const int64_t gx = (rows + slots * 4 - 1) / (slots * 4);
+    hipLaunchKernelGGL((score_dot_rows_kernel<T, EPL, G, L, 4>), dim3((unsigned)gx, (unsigned)bg), block, 0, s,
+                       (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
+                       hi);
+  } else if (want >= 2) {
+    const int64_t gx = (rows + slots * 2 - 1) / (slots * 2);
+    hipLaunchKernelGGL((score_dot_rows_kernel<T, EPL, G, L, 2>), dim3((unsigned)gx, (unsigned)bg), block, 0, s,
+                       (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
+                       hi);
+  } else {
+    const int64_t gx = (rows + slots - 1) / slots;
+    hipLaunchKernelGGL((score_dot_rows_kernel<T, EPL, G, L, 1>), dim3((unsigned)gx, (unsigned)bg), block, 0, s,
+                       (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
+                       hi);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int EPL, int G>
+hipError_t run_dot_any(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
+  // the row kernel needs R to divide the slots of a wave (64 / L of them)
+  const int L = m.head_dim / EPL;
+  const int R = m.reps_per_block;
+  const bool rows_ok = (R & (R - 1)) == 0 && R <= 64 / L;
+  if (rows_ok) {
+    if (L == 4) return run_rows<T, EPL, G, 4>(m, q, lo, hi, scores, s);
+    if (L == 8) return run_rows<T, EPL, G, 8>(m, q, lo, hi, scores, s);
+    if (L == 16) return run_rows<T, EPL, G, 16>(m, q, lo, hi, scores, s);
+  }
+  return run_dot<T, EPL, G>(m, q, lo, hi, scores, s);
+}
+
 template <typename T>
 hipError_t dispatch_dot(const brs_memory& m, const void* q, int G, int64_t lo, int64_t hi, float* scores,
                         hipStream_t s) {
@@ -210,11 +325,11 @@ hipError_t dispatch_dot(const brs_memory& m, const void* q, int G, int64_t lo, i
   auto qal = ((uintptr_t)q % 16) == 0;
   if (qal && (d * (int)sizeof(T)) % 16 == 0) {
     if (G <= 4 && fits(2 * E16)) {
-      if (G == 1) return run_dot<T, 2 * E16, 1>(m, q, lo, hi, scores, s);
-      if (G == 2) return run_dot<T, 2 * E16, 2>(m, q, lo, hi, scores, s);
-      if (G == 4) return run_dot<T, 2 * E16, 4>(m, q, lo, hi, scores, s);
+      if (G == 1) return run_dot_any<T, 2 * E16, 1>(m, q, lo, hi, scores, s);
+      if (G == 2) return run_dot_any<T, 2 * E16, 2>(m, q, lo, hi, scores, s);
+      if (G == 4) return run_dot_any<T, 2 * E16, 4>(m, q, lo, hi, scores, s);
     }
-    if (G == 8 && fits(E16)) return run_dot<T, E16, 8>(m, q, lo, hi, scores, s);
+    if (G == 8 && fits(E16)) return run_dot_any<T, E16, 8>(m, q, lo, hi, scores, s);
   }
   const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
   const int64_t gx = (hi - lo + 3) / 4;

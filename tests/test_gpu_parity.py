@@ -155,7 +155,9 @@ def test_broadcast_selection_dot_mode():
 
 @pytest.mark.parametrize("n,k,kind", [(1, 1, "normal"), (60, 4, "ties"), (991, 32, "ties"), (991, 32, "nan"),
                                       (5000, 2048, "normal"), (16384, 320, "ties"), (16384, 320, "zeros"),
-                                      (20000, 100, "ties"), (700, 700, "normal"), (50, 64, "normal")])
+                                      (20000, 100, "ties"), (700, 700, "normal"), (50, 64, "normal"),
+                                      (1500, 100, "ties"), (2048, 512, "normal"), (2048, 513, "ties"),
+                                      (130, 33, "nan")])
 def test_select_topk(n, k, kind):
     import block_retrieval_sparse_amd as brs
 
