@@ -576,6 +576,235 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_kernel(SplitArgs a) {
   }
 }
 
+// Matrix-core path (bfloat16, head_dim 64/128/256, up to 16 query rows per
+// group).  Per wave, tiles of 32 tokens:
+//   S^T = K Q^T  with v_mfma_f32_16x16x32_bf16: A = 16 token rows of K (each
+//                lane loads 16 contiguous bytes of a row), B = the query rows
+//                (zero beyond the group), accumulator lane l = tokens
+//                4(l/16)+i of the 16, query row l%16;
+//   O  += P V    with the same instruction: that accumulator layout is already
+//                the A operand (query row l%16, 8 tokens), and V is read back
+//                from LDS with the transposing ds_read_b64_tr_b16 into the B
+//                operand.  P is split into bf16 high and low parts (two MFMAs),
+//                so the weights keep about 16 significant bits.
+// Softmax is online with a lazy reference: the row reference only moves when
+// a tile's maximum exceeds it by more than 2^8, so rescaling is rare and
+// weights stay below 256.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kLazy = 8.0f;      // log2 headroom before the reference moves
+constexpr float kFarNeg = -1e30f;  // initial reference (finite: keeps 2^(s - ref) NaN-free)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // round to nearest even, two values into one register
+  auto rne = [](float f) -> uint32_t {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  };
+  return rne(lo) | (rne(hi) << 16);
+}
+
+template <int D, int NWMAX>
+__global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a) {
+  constexpr int KC = D / 32;  // 32-wide k chunks of the head dim
+  constexpr int NJ = D / 16;  // 16-wide output column tiles
+  __shared__ int4 s_items[kItemsLds];
+  // V tiles, rows padded by 32 bytes: the four rows one transposed read
+  // gathers then fall on disjoint banks.  Reused to combine the waves.
+  constexpr int VS = D + 16;
+  __shared__ __align__(16) uint16_t s_v[NWMAX][32][VS];
+  __shared__ int2 s_meta[NWMAX][32];
+  __shared__ float s_m[NWMAX][16], s_l[NWMAX][16];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, n = lane & 15;
+  const int c = blockIdx.x, bg = blockIdx.y, rg = blockIdx.z;
+  const int b = bg / a.hkv, g = bg - b * a.hkv;
+  const int rows_here = min(a.rows_per_group, a.rows - rg * a.rows_per_group);
+
+  // query row n of this group as the B operand
+  const bool act = n < rows_here;
+  const int gr = rg * a.rows_per_group + n;
+  const int jh = act ? gr / a.n_q : 0, qi = act ? gr - jh * a.n_q : 0;
+  const uint32_t rowbit = act ? (1u << jh) : 0u;
+  const int plim = a.N - a.n_q + qi;
+  uint4 qb[KC];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.hq + g * a.G + jh) * a.n_q + qi) * D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+      qb[kk] = act ? *reinterpret_cast<const uint4*>(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
+  }
+
+  const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
+  if (desc.x >= desc.y) return;
+  const int ns = stage_items(a, bg, desc, s_items);
+  const int t0 = c * a.chunk_tokens;
+  const int w0 = t0 + wave * a.wave_tokens;
+  const int w1 = min(w0 + a.wave_tokens, desc.z);
+
+  const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bg * a.head_stride + 8 * g4;
+  const uint16_t* vb = (const uint16_t*)a.v + (int64_t)bg * a.head_stride + 8 * g4;
+  const float qs = a.qscale;
+
+  f32x4_t o[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) o[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mref = kFarNeg, lpart = 0.f;
+
+  // cursor over the chunk's segments (each lane follows tokens tile + n and tile + 16 + n)
+  int cur = 0;
+  int4 it = s_items[0];
+  auto locate = [&](int tau, int& pos, uint32_t& msk) {
+    bool val = tau < w1;
+    if (val) {
+      while (tau >= it.w + it.y && cur + 1 < ns) it = s_items[++cur];
+      val = tau >= it.w && tau < it.w + it.y;
+    }
+    pos = it.x + (tau - it.w);
+    msk = val ? (uint32_t)it.z : 0u;
+    return val;
+  };
+
+  struct Tile {
+    uint4 k[2][KC], v[2][KC];
+    int pos[2];
+    uint32_t msk[2];
+  };
+  auto load = [&](Tile& tl, int tb) {
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      const bool val = locate(tb + 16 * sidx + n, tl.pos[sidx], tl.msk[sidx]);
+      const int64_t off = (int64_t)(val ? tl.pos[sidx] : it.x) * a.row_stride;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) tl.k[sidx][kk] = *reinterpret_cast<const uint4*>(kb + off + 32 * kk);
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) tl.v[sidx][kk] = *reinterpret_cast<const uint4*>(vb + off + 32 * kk);
+    }
+  };
+
+  // One tile of registers: its K feeds the S^T MFMAs and its V goes to LDS,
+  // then the next tile's loads are issued into the same registers while the
+  // softmax and the P V products of this tile run.
+  Tile tl;
+  if (w0 < w1) load(tl, w0);
+  for (int tb = w0; tb < w1; tb += 32) {
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        *reinterpret_cast<uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]) = tl.v[sidx][kk];
+    if (g4 == 0) {
+      s_meta[wave][n] = make_int2(tl.pos[0], (int)tl.msk[0]);
+      s_meta[wave][16 + n] = make_int2(tl.pos[1], (int)tl.msk[1]);
+    }
+    f32x4_t st[2];
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      st[sidx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        st[sidx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[sidx][kk]), as_bf16x8(qb[kk]), st[sidx], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (tb + 32 < w1) load(tl, tb + 32);
+    // logits of this lane: tokens 4*g4 + i (first half) and 16 + 4*g4 + i, query row n
+    float sv[8];
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int2 md = s_meta[wave][16 * sidx + 4 * g4 + i];
+        const bool pass = ((uint32_t)md.y & rowbit) && md.x <= plim;
+        sv[4 * sidx + i] = pass ? st[sidx][i] * qs : kNegInf;
+      }
+    float tm = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, sv[i]);
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    if (__ballot(tm > mref + kLazy)) {
+      const float nm = fmaxf(mref, tm);
+      const float al = fast_exp2(mref - nm);
+      mref = nm;
+      lpart *= al;
+      // accumulator rows are 4*g4 + i: fetch their factors from lanes 4*g4 + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(al, 4 * g4 + i);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) o[jj][i] *= ai;
+      }
+    }
+    // weights: high and low bf16 parts
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(sv[i] - mref);
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
+      const float h0 = __uint_as_float(ph[i] << 16), h1 = __uint_as_float(ph[i] & 0xffff0000u);
+      pl[i] = pack_bf16x2(pv[2 * i] - h0, pv[2 * i + 1] - h1);
+      lpart += pv[2 * i] + pv[2 * i + 1];
+    }
+    const bf16x8_t pa_hi = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8_t pa_lo = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    // O += P V, V columns 16*jj..16*jj+15 read transposed from LDS
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int col = 16 * jj + 4 * (n & 3);
+      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&s_v[wave][4 * g4 + (n >> 2)][col]);
+      const i16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&s_v[wave][16 + 4 * g4 + (n >> 2)][col]);
+      const bf16x8_t vbv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vbv, o[jj], 0, 0, 0);
+      o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vbv, o[jj], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // row sums over the four lanes that share a query row
+  lpart += __shfl_xor(lpart, 16);
+  lpart += __shfl_xor(lpart, 32);
+
+  // combine the waves: O rows 4*g4 + i, columns 16*jj + n; V tiles' LDS reused
+  __syncthreads();
+  float* s_o = reinterpret_cast<float*>(&s_v[0][0][0]);  // [NWMAX][16][D] floats fit in [NWMAX][32][VS] halves
+  if (lane < 16) {
+    s_m[wave][lane] = mref;
+    s_l[wave][lane] = lpart;
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[((int64_t)wave * 16 + 4 * g4 + i) * D + 16 * jj + n] = o[jj][i];
+  __syncthreads();
+  for (int t = threadIdx.x; t < rows_here * D; t += blockDim.x) {
+    const int r = t / D, e = t - r * D;
+    float M = kFarNeg;
+    for (int w = 0; w < a.nw; ++w) M = fmaxf(M, s_m[w][r]);
+    float Ls = 0.f, Os = 0.f;
+    for (int w = 0; w < a.nw; ++w) {
+      const float f = fast_exp2(s_m[w][r] - M);
+      Ls += s_l[w][r] * f;
+      Os += s_o[((int64_t)w * 16 + r) * D + e] * f;
+    }
+    const int64_t pidx = row_index(a, b, g, rg * a.rows_per_group + r) * a.max_chunks + c;
+    a.o[pidx * D + e] = Os;
+    if (e == 0) a.ml[pidx] = make_float2(M, Ls);
+  }
+}
+
 // Any head_dim <= 512 and any row stride: one token at a time per wave,
 // lanes across the dims.  One wave per workgroup.
 template <typename T>
@@ -744,27 +973,30 @@ bool attn_geometry(AttnGeom& g) {
   const int64_t E = g.idx_heads == 1 ? (int64_t)g.k : (int64_t)g.group * g.k;
   const int64_t uniq = E < g.nb ? E : g.nb;
   const int rows = g.group * g.n_q;
-  g.row_groups = (rows + kRowsMax - 1) / kRowsMax;
-  g.rows_per_group = rows < kRowsMax ? rows : kRowsMax;
-  const int64_t bg = (int64_t)g.batch * g.hkv;
   g.fast = fast_supported(g);
+  g.mfma = g.fast && g.dtype == BRS_BF16 && g.d <= 128 && env_int("BRS_MFMA", 1) != 0;
+  const int rmax = g.mfma ? 16 : kRowsMax;
+  g.row_groups = (rows + rmax - 1) / rmax;
+  g.rows_per_group = rows < rmax ? rows : rmax;
+  const int64_t bg = (int64_t)g.batch * g.hkv;
   g.max_items = 2 + uniq;
   g.max_tokens = (int64_t)g.sink_end + (g.N - g.win_start) + uniq * g.B;
   if (g.max_tokens > INT32_MAX) return false;
   // tokens per wave: about kTargetWaves waves over the whole problem, in whole steps
   const int64_t total = g.max_tokens * bg * g.row_groups;
-  const int st = g.fast ? step_tokens(g) : 1;
+  const int st = g.mfma ? 32 : (g.fast ? step_tokens(g) : 1);
   const int target = env_int("BRS_TARGET_WAVES", kTargetWaves);
   int64_t wt = (total + target - 1) / target;
   wt = ((wt + st - 1) / st) * st;
-  const int64_t wmin = g.fast ? 2 * st : 16;
+  const int64_t wmin = g.mfma ? 32 : (g.fast ? 2 * st : 16);
   wt = wt < wmin ? wmin : (wt > 4096 ? 4096 : wt);
   g.wave_tokens = (int)wt;
   const int64_t waves = (total + wt - 1) / wt;
-  g.nw = !g.fast ? 1 : (waves >= 2048 ? nw_max(g) : (waves >= 1024 ? 4 : 1));
+  const int nwm = g.mfma ? (g.d <= 128 ? 8 : 4) : nw_max(g);
+  g.nw = !g.fast ? 1 : (waves >= 2048 ? nwm : (waves >= 1024 ? 4 : 1));
   if (g.fast) {
     const int nw_env = env_int("BRS_NW", 0);
-    if (nw_env == 1 || nw_env == 2 || nw_env == 4 || (nw_env == 8 && nw_max(g) == 8)) g.nw = nw_env;
+    if (nw_env == 1 || nw_env == 2 || nw_env == 4 || (nw_env == 8 && nwm == 8)) g.nw = nw_env;
   }
   // a chunk meets at most chunk_tokens / B + 6 segments (sinks, window, the two
   // blocks cut by them, whole blocks, one more at each end): keep them in LDS
@@ -844,6 +1076,21 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   a.rows_per_group = g.rows_per_group;
   a.row_groups = g.row_groups;
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
+  if (g.mfma) {
+    const dim3 block(64 * g.nw);
+#define BRS_LAUNCH_MFMA(DD, NWM)                                                                            \
+  if (g.d == DD) {                                                                                          \
+    if (ev0)                                                                                                \
+      hipExtLaunchKernelGGL((attn_split_mfma_kernel<DD, NWM>), grid, block, 0, s, ev0, ev1, 0, a);         \
+    else                                                                                                    \
+      hipLaunchKernelGGL((attn_split_mfma_kernel<DD, NWM>), grid, block, 0, s, a);                         \
+    return hipGetLastError();                                                                               \
+  }
+    BRS_LAUNCH_MFMA(64, 8)
+    BRS_LAUNCH_MFMA(128, 8)
+#undef BRS_LAUNCH_MFMA
+    return hipErrorInvalidValue;
+  }
   if (g.fast) {
     const dim3 block(64 * g.nw);
     bool done = false;

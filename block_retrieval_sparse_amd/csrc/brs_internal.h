@@ -78,6 +78,7 @@ struct AttnGeom {
   float qscale;           // softmax scale * log2(e)
   // decomposition
   bool fast;              // head_dim and row layout served by the vector kernel
+  bool mfma;              // bfloat16 served by the matrix-core kernel
   int64_t max_items;      // segments per (batch, kv head)
   int64_t max_tokens;     // bound on attended tokens per (batch, kv head)
   int nw;                 // waves per split workgroup
