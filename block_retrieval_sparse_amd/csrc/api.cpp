@@ -245,8 +245,8 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
   g_prof_start = g_prof_stop = nullptr;
   hipError_t e = brs::launch_attn_plan(g, idx, workspace, out, s);
   if (e != hipSuccess) return hip_fail(e, "attn_plan");
-  if (brs::prefill_supported(g)) {
-    e = brs::launch_attn_prefill(g, m->k, m->v, q, idx, out, s, e0, e1);
+  if (g.prefill) {
+    e = brs::launch_attn_prefill(g, m->k, m->v, q, workspace, out, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "attn_prefill");
     return ok();
   }

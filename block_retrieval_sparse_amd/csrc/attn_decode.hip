@@ -1014,8 +1014,11 @@ bool attn_geometry(AttnGeom& g) {
   g.first_off = g.items_off + up((size_t)bg * g.max_items * sizeof(int4));
   g.chunks_off = g.first_off + up((size_t)bg * g.max_chunks * sizeof(int));
   g.ml_off = g.chunks_off + up((size_t)bg * g.max_chunks * sizeof(int4));
-  g.o_off = g.ml_off + up(rows_total * g.max_chunks * sizeof(float2));
-  g.total = g.o_off + up(rows_total * g.max_chunks * (size_t)g.d * sizeof(float));
+  // the prefill kernel needs only the plan; the split path also keeps partials
+  g.prefill = prefill_supported(g);
+  const size_t parts = g.prefill ? 0 : rows_total * g.max_chunks;
+  g.o_off = g.ml_off + up(parts * sizeof(float2));
+  g.total = g.o_off + up(parts * (size_t)g.d * sizeof(float));
   return true;
 }
 
@@ -1126,11 +1129,5 @@ hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_
   return hipGetLastError();
 }
 
-bool prefill_supported(const AttnGeom&) { return false; }
-
-hipError_t launch_attn_prefill(const AttnGeom&, const void*, const void*, const void*, const int32_t*, float*,
-                               hipStream_t, hipEvent_t, hipEvent_t) {
-  return hipErrorNotSupported;
-}
 
 }  // namespace brs

@@ -79,6 +79,7 @@ struct AttnGeom {
   // decomposition
   bool fast;              // head_dim and row layout served by the vector kernel
   bool mfma;              // bfloat16 served by the matrix-core kernel
+  bool prefill;           // chunk of queries served by the matrix-core prefill kernel
   int64_t max_items;      // segments per (batch, kv head)
   int64_t max_tokens;     // bound on attended tokens per (batch, kv head)
   int nw;                 // waves per split workgroup
@@ -98,9 +99,9 @@ hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, flo
 hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
                              float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);
-hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q,
-                               const int32_t* idx, float* out, hipStream_t s, hipEvent_t ev0,
-                               hipEvent_t ev1);
+// Chunked prefill on the matrix cores (reads the plan's segments from ws).
+hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
+                               float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 bool prefill_supported(const AttnGeom& g);
 
 // ---------------------------------------------------------------------------

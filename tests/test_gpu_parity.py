@@ -41,6 +41,12 @@ SMALL = {
                                                 block=40, k=6),
     "f32_topnorm": W["tiny_decode"].scaled(n_q_heads=4, n_kv_heads=2, rep_mode="topnorm", reps_per_block=3,
                                             n_tokens=3000, block=50, k=5, window=64, sinks=10),
+    # chunks of queries on the matrix-core prefill kernel (n_q >= 64, bf16, head_dim <= 128)
+    "prefill_gqa": W["infllm_gqa_decode_128k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=6000 + 11, block=64,
+                                                       window=200, sinks=16, k=5, n_q=100, planted_per_head=0),
+    "prefill_d64_short_window": W["retrievalattn_gqa_decode_1m_b8"].scaled(
+        batch=2, n_q_heads=4, n_kv_heads=4, head_dim=64, rep_dim=64, n_tokens=4000, block=32, k=10, window=40,
+        n_q=150),
 }
 
 
@@ -210,5 +216,6 @@ def test_full_size_memlong_prefill_sampled():
     w = W["memlong_chunk_prefill_80k"]
     mem, x = C.load(w)
     step = run_step(mem, w, x)
-    res = C.check_step(w, mem, x, step, pairs=[(0, 0), (0, 17), (0, 31)], query_rows=[0, 1, 255, 510, 511])
+    res = C.check_step(w, mem, x, step, pairs=[(0, 0), (0, 17), (0, 31)],
+                       query_rows=[0, 1, 63, 64, 255, 448, 510, 511])
     print(f"memlong: max |err| {res['max_abs_err']:.3g}")
