@@ -61,10 +61,14 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
-KERNEL_SOURCES = ("block_retrieval_sparse_amd/csrc/attn_decode.hip", "block_retrieval_sparse_amd/csrc/brs_internal.h")
+KERNEL_SOURCES = {
+    "attn_split": ("block_retrieval_sparse_amd/csrc/attn_decode.hip", "block_retrieval_sparse_amd/csrc/brs_internal.h"),
+    "attn_prefill": ("block_retrieval_sparse_amd/csrc/attn_prefill.hip",
+                     "block_retrieval_sparse_amd/csrc/brs_internal.h"),
+}
 
 
-def sources_sha256(paths=KERNEL_SOURCES) -> str:
+def sources_sha256(paths=KERNEL_SOURCES["attn_split"]) -> str:
     import hashlib
 
     h = hashlib.sha256()
@@ -74,11 +78,11 @@ def sources_sha256(paths=KERNEL_SOURCES) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the split kernel from the committed counter
-    summary for this workload, or None when there is none or the kernel's
-    sources have changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"attn_split_{workload}_traffic.txt")
+def measured_traffic(workload: str, kernel: str = "attn_split"):
+    """HBM bytes per launch of the main attention kernel from the committed
+    counter summary for this workload, or None when there is none or the
+    kernel's sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -87,7 +91,7 @@ def measured_traffic(workload: str):
             if ":" in line and not line.startswith(" "):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    if fields.get("source_sha256") != sources_sha256():
+    if fields.get("source_sha256") != sources_sha256(KERNEL_SOURCES[kernel]):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -181,6 +185,30 @@ def step_bytes(w, step) -> dict:
     return {"reps": reps, "kv": kv, "q": q, "out": out, "total": reps + kv + q + out}
 
 
+def step_flops(w, step) -> float:
+    """Algorithmic flops of the attention of one executed step: 2 d for
+    q.k and 2 d for p.v per (query, visible attended token)."""
+    import numpy as np
+
+    idx = step.idx.cpu().numpy()
+    N = step.mem.length
+    pos = np.arange(N)
+    total = 0
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            rows = idx[b, 0] if w.rep_mode == "embed" else idx[b, h]
+            T = np.zeros(N, dtype=bool)
+            T[:min(w.sinks, N)] = True
+            T[max(N - w.window, 0):] = True
+            for blk in np.unique(rows):
+                if 0 <= blk < N // w.block:
+                    T[blk * w.block:(blk + 1) * w.block] = True
+            cum = np.cumsum(T)
+            qpos = N - w.n_q + np.arange(w.n_q)
+            total += int(cum[qpos].sum())
+    return 4.0 * w.head_dim * total
+
+
 def cpu_baseline(w, layer0, budget_s: float, cache_bytes: float = 4e9) -> dict:
     """The oracle (as it stands) on a bounded sample of layer 0's step.
 
@@ -240,8 +268,10 @@ def cpu_baseline(w, layer0, budget_s: float, cache_bytes: float = 4e9) -> dict:
     except Exception:
         cores = 1
     steps = done / n_pairs
-    return {"value": w.batch * steps / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} single-head decode problems (scores, top-k, attention) of layer 0, cycling over "
+    unit = "query tokens/s" if w.n_q > 1 else "tokens/s"
+    what = f"single-head {w.n_q}-query chunk" if w.n_q > 1 else "single-head decode"
+    return {"value": w.batch * w.n_q * steps / elapsed, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{done} {what} problems (scores, top-k, attention) of layer 0, cycling over "
                       f"its {n_pairs} (batch, query head) pairs = {steps:.2f} whole steps in {elapsed:.1f} s of "
                       f"oracle time; float64 conversion and representative builds untimed"}
 
@@ -255,9 +285,7 @@ def run(args):
     w = WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    if w.n_q > 1:
-        raise SystemExit("bench.py times decode workloads; the chunked-prefill workload is timed by "
-                         "--workload with n_q == 1 only in this version")
+    prefill = w.n_q > 1
     es = 4 if w.dtype == "f32" else 2
     est = (w.batch * w.n_kv_heads * (w.sinks + w.window + w.k * w.group * w.block) * w.head_dim * es * 2)
     n_layers = args.layers or max(1, min(8, math.ceil(1.5e9 / max(est, 1))))
@@ -320,7 +348,10 @@ def run(args):
         stage["attend"] += ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) / n_c
 
     split_bytes = avg["kv"] + avg["q"]
-    achieved = split_bytes / (kern_avg * 1e-3) / 1e9
+    cfg = {"workload": w.name, "batch": w.batch, "context_tokens": w.n_tokens, "q_heads": w.n_q_heads,
+           "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block, "reps_per_block": w.reps_per_block,
+           "rep_mode": w.rep_mode, "top_k": w.k, "window": w.window, "sinks": w.sinks, "queries": w.n_q,
+           "layers_rotated": n_layers, "parallelism": "none"}
     res = {
         "metric": "retrieval-attn decode tokens/s @128K ctx; achieved HBM GB/s vs peak",
         "value": w.batch / (ms_step * 1e-3),
@@ -334,19 +365,34 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) K/V/q with planted blocks; no dataset or weights)",
-        "config": {"workload": w.name, "batch": w.batch, "context_tokens": w.n_tokens, "q_heads": w.n_q_heads,
-                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block,
-                   "reps_per_block": w.reps_per_block, "rep_mode": w.rep_mode, "top_k": w.k,
-                   "window": w.window, "sinks": w.sinks, "layers_rotated": n_layers, "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "attn_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
-                     "bytes_per_launch": split_bytes, "avg_launch_us": kern_avg * 1e3},
+        "config": cfg,
+    }
+    if prefill:
+        flops = sum(step_flops(w, st) for (_, st, _) in layers) / n_layers
+        achieved = flops / (kern_avg * 1e-3) / 1e12
+        res.update({
+            "metric": "chunked-prefill query tokens/s; MFMA utilisation vs bf16 dense peak",
+            "value": w.batch * w.n_q / (ms_step * 1e-3),
+            "unit": "query tokens/s",
+            "roofline": {"bound": "mfma", "kernel": "attn_prefill", "achieved": achieved,
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                         "traffic": measured_traffic(w.name, "attn_prefill"), "flops_per_launch": flops,
+                         "avg_launch_us": kern_avg * 1e3},
+            "step_mfma": {"flops": flops, "TFLOP/s": flops / (ms_step * 1e-3) / 1e12,
+                          "frac": flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        })
+    else:
+        achieved = split_bytes / (kern_avg * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "attn_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
+                           "bytes_per_launch": split_bytes, "avg_launch_us": kern_avg * 1e3}
+    res.update({
         "step_hbm": {"algorithmic_bytes": avg["total"], "GB/s": avg["total"] / (ms_step * 1e-3) / 1e9,
                      "frac": avg["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, "parts": avg},
         "stage_us": {k: v * 1e3 for k, v in stage.items()},
         "append_build": {"bytes": built_bytes, "s": t_build, "GB/s": built_bytes / max(t_build, 1e-9) / 1e9},
         "lib_version": _lib.lib.brs_version(),
-    }
+    })
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(w, layers[0][2], args.cpu_seconds)

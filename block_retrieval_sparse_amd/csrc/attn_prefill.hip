@@ -38,9 +38,18 @@ constexpr int kStage = 64;       // tokens per stage (two 32-token halves)
 constexpr float kLazyP = 8.0f;
 constexpr float kFarNegP = -1e30f;
 constexpr int kXcds = 8;
+constexpr int kAhead = 4;         // stages of K/V loads in flight per thread (register ring)
+constexpr int kBufs = 3;          // stage buffers in LDS
+constexpr int kTabTokens = 4096;  // token table ring (64 stages)
+constexpr int kRefill = 32;       // stages refilled at a time (half the ring)
+constexpr int kNoPos = 0x7fffffff;
+constexpr int kOutOfRange = 0x7ffff000;  // buffer offset past any slice: loads return zeros
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data, no swizzle)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_p;
 typedef __attribute__((ext_vector_type(4))) float f32x4_p;
+typedef __attribute__((ext_vector_type(2))) float f32x2_p;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_p;
 typedef __attribute__((ext_vector_type(4))) short i16x4_p;
 typedef __attribute__((address_space(3))) i16x4_p lds_i16x4_p;
 
@@ -54,19 +63,13 @@ struct PrefillArgs {
   int64_t max_items;
   int64_t head_stride;
   int row_stride, hq, hkv, G, n_q, N, d, nvec, nj;
+  int slice_bytes;  // bytes of one (batch, kv head) slice of k / v (buffer range)
+  int win_start;
   float qscale;
   int n_tiles, n_units, per_xcd;
 };
 
 __device__ __forceinline__ bf16x8_p as_bf16x8_p(const uint4& u) { return __builtin_bit_cast(bf16x8_p, u); }
-
-__device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
-  auto rne = [](float f) -> uint32_t {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  };
-  return rne(lo) | (rne(hi) << 16);
-}
 
 int env_flag(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -75,22 +78,52 @@ int env_flag(const char* name, int dflt) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (same column of the
+// accumulator) with the gfx950 lane-swap moves (no LDS round trip).
+__device__ __forceinline__ float xmax16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xmin16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // DP: head dim rounded up to a multiple of 32 (the k chunk of the S^T MFMA).
-template <int DP>
+// ONES: V carries a column of ones in a spare padded column (head dims with
+// d mod 16 in 1..8), so the P V products also yield the softmax row sums.
+template <int DP, bool ONES>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   constexpr int KC = DP / 32;
   constexpr int NJ = DP / 16;
   constexpr int KP = DP + 16;  // LDS row pitch in halves (keeps transposed reads conflict-free)
-  constexpr int VPT = (2 * kStage * (DP / 8) + 511) / 512;  // 16-byte vectors staged per thread
-  __shared__ __align__(16) uint16_t s_k[2][kStage][KP];
-  __shared__ __align__(16) uint16_t s_v[2][kStage][KP];
-  __shared__ int2 s_meta[3][kStage];
+  constexpr int VPT = (kStage * (DP / 8) + 255) / 256;  // 16-byte vectors per thread and stage
+  constexpr int BUF = kStage * KP;                      // halves per stage buffer
+  // stage buffers: K in [0, 3 BUF), V in [3 BUF, 6 BUF)
+  __shared__ __align__(16) uint16_t s_kv[2 * kBufs * BUF];
+  __shared__ int2 s_tab[kTabTokens];  // (position, K/V row byte offset) of stream tokens, a ring
   __shared__ int4 s_items[kPrefItems];
   __shared__ int wave_tot[16];
-  __shared__ int sh_tot[2];
+  __shared__ int sh_tot[4];
   __shared__ float s_ml[4][16][2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, n = lane & 15;
   const int qg = wave & 3, kh = wave >> 2;
 
@@ -107,86 +140,112 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   const int qlast = min(q0 + kPrefQ, a.n_q) - 1;
   const int pmax = a.N - a.n_q + qlast;
 
-  // segments of this head, clipped to positions <= pmax, flattened
+  // The segments of this head clipped to positions <= pmax, in position
+  // order: the plan lists sinks, window, then blocks in block order, and
+  // the blocks lie between sinks and window, so the window goes last.
   const int4 hd = a.hdr[bg];
   const int n_in = hd.x;
   int4 it = make_int4(0, 0, 0, 0);
   int keep = 0, len = 0;
+  bool is_win = false;
   if (tid < n_in) {
     it = a.items[(int64_t)bg * a.max_items + tid];
+    is_win = tid <= 1 && it.x == a.win_start && it.x + it.y == a.N;
     if ((uint32_t)it.z & headbit) {
       len = min(it.x + it.y, pmax + 1) - it.x;
       len = len < 0 ? 0 : len;
       keep = len > 0;
     }
   }
-  const int inc_k = block_inclusive_scan(keep, wave_tot);
-  const int inc_t = block_inclusive_scan(len, wave_tot);
-  if (keep) s_items[inc_k - 1] = make_int4(it.x, len, 0, inc_t - len);
+  if (tid == 0) sh_tot[2] = 0;
+  const int inc_k = block_inclusive_scan(keep && !is_win ? 1 : 0, wave_tot);
+  const int inc_t = block_inclusive_scan(keep && !is_win ? len : 0, wave_tot);
   if (tid == 511) {
     sh_tot[0] = inc_k;
     sh_tot[1] = inc_t;
   }
-  // zero the pad columns of K and V once (never written by the staging)
-  for (int i = tid; i < 2 * 2 * kStage; i += 512) {
-    uint16_t* row = (i < 2 * kStage) ? &s_k[i >> 6][i & 63][0] : &s_v[(i >> 6) - 2][i & 63][0];
-    for (int c = 8 * a.nvec; c < KP; ++c) row[c] = 0;
+  __syncthreads();
+  if (keep && !is_win) s_items[inc_k - 1] = make_int4(it.x, len, 0, inc_t - len);
+  if (keep && is_win) {
+    s_items[sh_tot[0]] = make_int4(it.x, len, 0, sh_tot[1]);
+    sh_tot[2] = 1;
+  }
+  // pad columns of K and V: zero, except V's column of ones
+  for (int i = tid; i < 2 * kBufs * kStage; i += 512) {
+    uint16_t* row = s_kv + i * KP;
+    const bool isv = i >= kBufs * kStage;
+    for (int c = 8 * a.nvec; c < KP; ++c) row[c] = (ONES && isv && c == 8 * a.nvec) ? 0x3f80 : 0;
   }
   __syncthreads();
-  const int ns = sh_tot[0], n_tok = sh_tot[1];
+  const int ns = sh_tot[0] + sh_tot[2];
+  const int n_tok = ns > 0 ? s_items[ns - 1].w + s_items[ns - 1].y : 0;
   const int n_stages = (n_tok + kStage - 1) / kStage;
 
-  // stage metadata (position of each of the 64 rows, -1 = none), computed by wave 0 with a cursor
-  int cur = 0;
-  int4 ci = ns > 0 ? s_items[0] : make_int4(0, 0, 0, 0);
-  auto meta = [&](int stage) {
-    const int tau = stage * kStage + lane;
-    int pos = -1;
-    if (tau < n_tok) {
-      while (tau >= ci.w + ci.y && cur + 1 < ns) ci = s_items[++cur];
-      pos = ci.x + (tau - ci.w);
+  // token table: stream offset tau -> (position, byte offset), kNoPos past the end
+  const int row_bytes = a.row_stride * 2;
+  auto fill = [&](int tau0, int count) {
+    for (int i = tid; i < count; i += 512) {
+      const int tau = tau0 + i;
+      int2 e = make_int2(kNoPos, kOutOfRange);
+      if (tau < n_tok) {
+        int lo = 0, hi = ns - 1;  // last item with w <= tau
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_items[mid].w <= tau) lo = mid; else hi = mid - 1;
+        }
+        const int4 c = s_items[lo];
+        const int pos = c.x + (tau - c.w);
+        e = make_int2(pos, pos * row_bytes);
+      }
+      s_tab[tau & (kTabTokens - 1)] = e;
     }
-    s_meta[stage % 3][lane] = make_int2(pos, 0);
   };
+  fill(0, kTabTokens);
 
-  // staging: thread t moves vectors e = t + 512 j of the stage (K rows first, then V)
+  // staging: waves 0-3 move K, waves 4-7 move V; thread t of the 256 moves
+  // vectors e = t + 256 j of the stage.  Buffer loads with one 32-bit offset
+  // per vector (rows past the end read zeros); kAhead stages of loads are in
+  // flight in a ring of registers.
   const int kvec = kStage * a.nvec;
-  const uint16_t* kb = a.k + (int64_t)bg * a.head_stride;
-  const uint16_t* vb = a.v + (int64_t)bg * a.head_stride;
-  uint4 stg[VPT];
-  auto stage_load = [&](int stage) {
+  const bool stage_v = wave >= 4;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((stage_v ? a.v : a.k) + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kBufferFlags);
+  const int t256 = tid & 255;
+  int srow[VPT], scol[VPT], soff[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int e = t256 + 256 * j;
+    const int r = e / a.nvec, c = e - r * a.nvec;
+    srow[j] = r < kStage ? r : 0;
+    scol[j] = e < kvec ? 16 * c : kOutOfRange;  // lanes without a vector read zeros
+    soff[j] = e < kvec ? (stage_v ? kBufs * BUF : 0) + r * KP + 8 * c : -1;
+  }
+  uint4 stg[kAhead][VPT];
+  auto stage_offsets = [&](int(&at)[VPT], int stage) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int e = tid + 512 * j;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (e < 2 * kvec) {
-        const bool isv = e >= kvec;
-        const int ee = isv ? e - kvec : e;
-        const int r = ee / a.nvec, c = ee - r * a.nvec;
-        const int pos = s_meta[stage % 3][r].x;
-        if (pos >= 0) x = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (int64_t)pos * a.row_stride + 8 * c);
-      }
-      stg[j] = x;
+      const int off = s_tab[(stage * kStage + srow[j]) & (kTabTokens - 1)].y;
+      at[j] = scol[j] == kOutOfRange ? kOutOfRange : off + scol[j];
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_load = [&](uint4(&dst)[VPT], const int(&at)[VPT]) {
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int e = tid + 512 * j;
-      if (e < 2 * kvec) {
-        const bool isv = e >= kvec;
-        const int ee = isv ? e - kvec : e;
-        const int r = ee / a.nvec, c = ee - r * a.nvec;
-        uint16_t* dst = isv ? &s_v[buf][r][8 * c] : &s_k[buf][r][8 * c];
-        *reinterpret_cast<uint4*>(dst) = stg[j];
-      }
-    }
+    for (int j = 0; j < VPT; ++j)
+      dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at[j], 0, 0));
+  };
+  auto stage_store = [&](const uint4(&src)[VPT], int stage) {
+    const int base = (stage % kBufs) * BUF;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      if (soff[j] >= 0) *reinterpret_cast<uint4*>(s_kv + base + soff[j]) = src[j];
   };
 
-  // query rows of this wave as the B operand of S^T = K Q^T
+  // query rows of this wave as the B operand of S^T = K Q^T.  Rows past the
+  // last query compute unused values (rows never mix in either product).
   const int qi = q0 + 16 * qg + n;
   const bool act = qi < a.n_q;
-  const int plim = a.N - a.n_q + qi;
+  const int plim = a.N - a.n_q + qi;                // last visible position of this lane's row
+  const int plim_min = a.N - a.n_q + q0 + 16 * qg;  // the wave's smallest one
   uint4 qb[KC];
   {
     const uint16_t* qrow = a.q + ((int64_t)bh * a.n_q + (act ? qi : 0)) * a.d;
@@ -204,59 +263,84 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     }
   }
   const float qs = a.qscale;
+  const bool qs_pos = qs >= 0.f;
 
   f32x4_p o[NJ];
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) o[jj] = f32x4_p{0.f, 0.f, 0.f, 0.f};
   float mref = kFarNegP, lpart = 0.f;
+  const int r0 = 32 * kh;  // this wave's 32 rows of every stage
 
-  if (n_stages > 0) {
-    if (wave == 0) {
-      meta(0);
-      if (n_stages > 1) meta(1);
-    }
-    __syncthreads();
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
-  }
-
-  for (int s = 0; s < n_stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < n_stages) stage_load(s + 1);
-    if (wave == 0 && s + 2 < n_stages) meta(s + 2);
-
-    // this wave's 32 tokens: stage rows 32 kh .. 32 kh + 31
-    const int r0 = 32 * kh;
-    f32x4_p st[2];
+  // S^T for this wave's rows of stage s
+  auto qk = [&](f32x4_p(&st)[2], int s) {
+    const uint16_t* kbuf = s_kv + (s % kBufs) * BUF;
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx) {
       st[sidx] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&s_k[buf][r0 + 16 * sidx + n][32 * kk + 8 * g4]);
+        const uint4 ka = *reinterpret_cast<const uint4*>(kbuf + (r0 + 16 * sidx + n) * KP + 32 * kk + 8 * g4);
         st[sidx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_p(ka), as_bf16x8_p(qb[kk]), st[sidx], 0, 0, 0);
       }
     }
+  };
+
+  // softmax of stage s from its S^T, then O += P V
+  auto softmax_pv = [&](const f32x4_p(&st)[2], int s) {
+    const uint16_t* vbuf = s_kv + kBufs * BUF + (s % kBufs) * BUF;
+    bf16x8_p vb[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      if (jj < a.nj) {
+        const int col = 16 * jj + 4 * (n & 3);
+        const i16x4_p v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)(vbuf + (r0 + 4 * g4 + (n >> 2)) * KP + col));
+        const i16x4_p v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_p*)(vbuf + (r0 + 16 + 4 * g4 + (n >> 2)) * KP + col));
+        vb[jj] = __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+    const int tbase = s * kStage + r0;
+    // whole: the stream is in position order, so its last token bounds the half
+    const bool whole = s_tab[(tbase + 31) & (kTabTokens - 1)].x <= plim_min;
     float sv[8];
+    bool vis[8];
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int pos = s_meta[s % 3][r0 + 16 * sidx + 4 * g4 + i].x;
-        const bool pass = act && pos >= 0 && pos <= plim;
-        sv[4 * sidx + i] = pass ? st[sidx][i] * qs : -INFINITY;
+        sv[4 * sidx + i] = st[sidx][i];
+        vis[4 * sidx + i] = true;
       }
-    float tm = sv[0];
+    if (!whole) {
 #pragma unroll
-    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, sv[i]);
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+      for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = s_tab[(tbase + 16 * sidx + 4 * g4 + i) & (kTabTokens - 1)].x;
+          vis[4 * sidx + i] = pos <= plim;
+        }
+    }
+    // row extreme of the raw scores over visible tokens (the maximum of
+    // scale * s is scale * max s for scale >= 0, scale * min s otherwise)
+    float e;
+    if (qs_pos) {
+      e = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e = fmaxf(e, vis[i] ? sv[i] : -INFINITY);
+      e = xmax16_32(e);
+    } else {
+      e = INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e = fminf(e, vis[i] ? sv[i] : INFINITY);
+      e = xmin16_32(e);
+    }
+    const float tm = __builtin_isinf(e) ? -INFINITY : e * qs;
     if (__ballot(tm > mref + kLazyP)) {
       const float nm = fmaxf(mref, tm);
       const float al = exp2_fast(mref - nm);
       mref = nm;
-      lpart *= al;
+      if (!ONES) lpart *= al;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = __shfl(al, 4 * g4 + i);
@@ -264,42 +348,94 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
         for (int jj = 0; jj < NJ; ++jj) o[jj][i] *= ai;
       }
     }
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = exp2_fast(sv[i] - mref);
+    // weights 2^(scale s - ref) as bf16 high parts plus bf16 low parts
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ph[i] = pack2_rne(pv[2 * i], pv[2 * i + 1]);
-      const float h0 = __uint_as_float(ph[i] << 16), h1 = __uint_as_float(ph[i] & 0xffff0000u);
-      pl[i] = pack2_rne(pv[2 * i] - h0, pv[2 * i + 1] - h1);
-      lpart += pv[2 * i] + pv[2 * i + 1];
+      f32x2_p p2;
+      p2.x = exp2_fast(__builtin_fmaf(sv[2 * i], qs, -mref));
+      p2.y = exp2_fast(__builtin_fmaf(sv[2 * i + 1], qs, -mref));
+      p2.x = vis[2 * i] ? p2.x : 0.f;
+      p2.y = vis[2 * i + 1] ? p2.y : 0.f;
+      const bf16x2_p hi = __builtin_convertvector(p2, bf16x2_p);
+      const f32x2_p back = __builtin_convertvector(hi, f32x2_p);
+      ph[i] = __builtin_bit_cast(uint32_t, hi);
+      pl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2 - back, bf16x2_p));
+      if (!ONES) lpart += p2.x + p2.y;
     }
     const bf16x8_p pa_hi = __builtin_bit_cast(bf16x8_p, make_uint4(ph[0], ph[1], ph[2], ph[3]));
     const bf16x8_p pa_lo = __builtin_bit_cast(bf16x8_p, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      if (jj < a.nj) {
-        const int col = 16 * jj + 4 * (n & 3);
-        const i16x4_p v0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)&s_v[buf][r0 + 4 * g4 + (n >> 2)][col]);
-        const i16x4_p v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)&s_v[buf][r0 + 16 + 4 * g4 + (n >> 2)][col]);
-        const bf16x8_p vbv = __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vbv, o[jj], 0, 0, 0);
-        o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vbv, o[jj], 0, 0, 0);
+    for (int jj = 0; jj < NJ; ++jj)
+      if (jj < a.nj) o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[jj], o[jj], 0, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      if (jj < a.nj) o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[jj], o[jj], 0, 0, 0);
+  };
+
+  // Pipeline over stages, three LDS buffers: in iteration s the wave
+  // multiplies S^T of stage s+1 while it finishes the softmax and P V of
+  // stage s; stage s+2 moves from registers to LDS and stage s+2+kAhead is
+  // requested into the registers it frees (stages s+3 .. s+1+kAhead are in
+  // flight).  Loads, stores and barriers run unconditionally (past the end
+  // the loads read zeros) so the memory waits stay one ring slot deep.
+  if (n_stages > 0) {
+    __syncthreads();  // token table
+    int at[VPT];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      stage_offsets(at, j);
+      stage_load(stg[j], at);
+    }
+    stage_store(stg[0], 0);
+    stage_offsets(at, kAhead);
+    stage_load(stg[0], at);
+    stage_store(stg[1], 1);
+    stage_offsets(at, kAhead + 1);
+    stage_load(stg[1], at);
+    __syncthreads();
+    f32x4_p st_cur[2], st_nxt[2];
+    qk(st_cur, 0);
+    for (int s0 = 0; s0 < n_stages; s0 += kAhead) {
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) {
+        const int s = s0 + j;
+        // refill the token table half a ring ahead (entries of finished stages)
+        if (s % kRefill == 0 && s >= kRefill) fill((s + kRefill) * kStage, kRefill * kStage);
+        stage_offsets(at, s + 2 + kAhead);
+        if (s + 1 < n_stages) qk(st_nxt, s + 1);
+        if (s < n_stages) softmax_pv(st_cur, s);
+        stage_store(stg[(j + 2) % kAhead], s + 2);
+        stage_load(stg[(j + 2) % kAhead], at);
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) st_cur[q] = st_nxt[q];
       }
     }
-    if (s + 1 < n_stages) stage_store(buf ^ 1);
-    __syncthreads();
   }
 
-  // row sums over the four lanes that share a query row
-  lpart += __shfl_xor(lpart, 16);
-  lpart += __shfl_xor(lpart, 32);
+  // row sums: from the ones column, or over the four lanes that share a row
+  if (ONES) {
+    // o[jj1][i] at lane (g4, n1) holds the sum of row 4 g4 + i; bring row n's to lane n
+    const int c1 = 8 * a.nvec, jj1 = c1 >> 4, n1 = c1 & 15;
+    float li = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      if (jj == jj1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = __shfl(o[jj][i], 16 * (n >> 2) + n1);
+          li = (i == (n & 3)) ? v : li;
+        }
+      }
+    lpart = li;
+  } else {
+    lpart = xsum16_32(lpart);
+  }
 
   // merge the two token halves: waves 4-7 hand (max, sum, O) to waves 0-3 through LDS
-  float* s_o = reinterpret_cast<float*>(&s_k[0][0][0]);  // [4][16][DP] floats
+  __syncthreads();
+  float* s_o = reinterpret_cast<float*>(s_kv);  // [4][16][DP] floats
   if (kh == 1) {
     if (lane < 16) {
       s_ml[qg][lane][0] = mref;
@@ -339,7 +475,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 bool prefill_supported(const AttnGeom& g) {
   if (env_flag("BRS_PREFILL", 1) == 0) return false;
   return g.dtype == BRS_BF16 && g.n_q >= kPrefQ && g.d <= 128 && g.row_stride % 8 == 0 &&
-         ((g.d + 7) / 8) * 8 <= g.row_stride && g.max_items <= kPrefItems && g.N <= INT32_MAX / 2;
+         ((g.d + 7) / 8) * 8 <= g.row_stride && g.max_items <= kPrefItems &&
+         g.head_stride * 2 < (int64_t)kOutOfRange - 4096;
 }
 
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws, float* out,
@@ -366,18 +503,29 @@ hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, 
   a.n_tiles = (g.n_q + kPrefQ - 1) / kPrefQ;
   a.n_units = a.n_tiles * g.batch * g.hq;
   a.per_xcd = (a.n_units + kXcds - 1) / kXcds;
+  a.slice_bytes = (int)(g.head_stride * 2);
+  a.win_start = g.win_start;
   const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(512);
+  const bool ones = 8 * a.nvec < 16 * a.nj;  // a spare padded column exists
+#define BRS_PREFILL_LAUNCH(DP, ONES)                                                   \
+  if (ev0)                                                                             \
+    hipExtLaunchKernelGGL((attn_prefill_kernel<DP, ONES>), grid, block, 0, s, ev0, ev1, 0, a); \
+  else                                                                                 \
+    hipLaunchKernelGGL((attn_prefill_kernel<DP, ONES>), grid, block, 0, s, a);
   if (g.d <= 64) {
-    if (ev0)
-      hipExtLaunchKernelGGL(attn_prefill_kernel<64>, grid, block, 0, s, ev0, ev1, 0, a);
-    else
-      hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, block, 0, s, a);
+    if (ones) {
+      BRS_PREFILL_LAUNCH(64, true)
+    } else {
+      BRS_PREFILL_LAUNCH(64, false)
+    }
   } else {
-    if (ev0)
-      hipExtLaunchKernelGGL(attn_prefill_kernel<128>, grid, block, 0, s, ev0, ev1, 0, a);
-    else
-      hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, block, 0, s, a);
+    if (ones) {
+      BRS_PREFILL_LAUNCH(128, true)
+    } else {
+      BRS_PREFILL_LAUNCH(128, false)
+    }
   }
+#undef BRS_PREFILL_LAUNCH
   return hipGetLastError();
 }
 
