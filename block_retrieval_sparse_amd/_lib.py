@@ -21,7 +21,7 @@ ERRORS = {0: "BRS_OK", -1: "BRS_E_INVAL", -2: "BRS_E_CAPACITY", -3: "BRS_E_UNSUP
 # every symbol include/brs.h declares
 EXPORTS = ["brs_version", "brs_last_error", "brs_memory_check", "brs_mem_append", "brs_eligible_range",
            "brs_score_blocks", "brs_select_topk", "brs_attention_workspace_bytes",
-           "brs_retrieval_attention", "brs_profile_next_attention"]
+           "brs_retrieval_attention", "brs_retrieval_step", "brs_profile_next_attention"]
 
 
 class brs_memory(ctypes.Structure):
@@ -59,6 +59,8 @@ def _load():
         "brs_retrieval_attention": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
                                             c_int64, c_int64, c_float, c_void_p, c_void_p, c_size_t,
                                             c_void_p]),
+        "brs_retrieval_step": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int64, c_int64, c_float,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "brs_profile_next_attention": (c_int, [c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():

@@ -226,25 +226,16 @@ int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_
   return ok();
 }
 
-int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
-                            const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
-                            int64_t window, float scale, float* out, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  brs::AttnGeom g;
-  int rc = attn_setup(m, n_q_heads, n_q, idx_heads, k, n_sink, window, scale, g);
-  if (rc) return rc;
-  if (!q || !out) return fail(BRS_E_INVAL, "q/out must be non-NULL");
-  if (k > 0 && !idx) return fail(BRS_E_INVAL, "idx must be non-NULL when k > 0");
-  if (!aligned(q, 16) || !aligned(out, 16)) return fail(BRS_E_INVAL, "q/out must be 16-byte aligned");
-  if (idx && !aligned(idx, 4)) return fail(BRS_E_INVAL, "idx misaligned");
-  if (!workspace || workspace_bytes < g.total)
-    return fail(BRS_E_WORKSPACE, "workspace of %zu bytes needed", g.total);
-  if (!aligned(workspace, 256)) return fail(BRS_E_WORKSPACE, "workspace must be 256-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
+// plan (unless already enqueued), then the attention kernels
+static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void* q, const int32_t* idx,
+                         bool planned, float* out, void* workspace, hipStream_t s) {
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
-  hipError_t e = brs::launch_attn_plan(g, idx, workspace, out, s);
-  if (e != hipSuccess) return hip_fail(e, "attn_plan");
+  hipError_t e;
+  if (!planned) {
+    e = brs::launch_attn_plan(g, idx, workspace, out, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_plan");
+  }
   if (g.prefill) {
     e = brs::launch_attn_prefill(g, m->k, m->v, q, workspace, out, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "attn_prefill");
@@ -255,6 +246,73 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
   e = brs::launch_attn_merge(g, workspace, out, s);
   if (e != hipSuccess) return hip_fail(e, "attn_merge");
   return ok();
+}
+
+static int check_attention_buffers(const brs::AttnGeom& g, const void* q, const int32_t* idx, int32_t k, float* out,
+                                   void* workspace, size_t workspace_bytes) {
+  if (!q || !out) return fail(BRS_E_INVAL, "q/out must be non-NULL");
+  if (k > 0 && !idx) return fail(BRS_E_INVAL, "idx must be non-NULL when k > 0");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(BRS_E_INVAL, "q/out must be 16-byte aligned");
+  if (idx && !aligned(idx, 4)) return fail(BRS_E_INVAL, "idx misaligned");
+  if (!workspace || workspace_bytes < g.total)
+    return fail(BRS_E_WORKSPACE, "workspace of %zu bytes needed", g.total);
+  if (!aligned(workspace, 256)) return fail(BRS_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return BRS_OK;
+}
+
+int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
+                            const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
+                            int64_t window, float scale, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  brs::AttnGeom g;
+  int rc = attn_setup(m, n_q_heads, n_q, idx_heads, k, n_sink, window, scale, g);
+  if (rc) return rc;
+  rc = check_attention_buffers(g, q, idx, k, out, workspace, workspace_bytes);
+  if (rc) return rc;
+  return run_attention(g, m, q, idx, false, out, workspace, (hipStream_t)stream);
+}
+
+int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const void* qrep,
+                       int32_t k, int64_t n_sink, int64_t window, float scale, float* scores, int32_t* idx,
+                       float* vals, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  const bool cosine = m->rep_mode == BRS_REP_EMBED;
+  const int32_t hs = cosine ? 1 : n_q_heads;
+  int64_t lo = 0, hi = 0;
+  rc = brs_eligible_range(m, n_sink, window, &lo, &hi);
+  if (rc) return rc;
+  brs::AttnGeom g;
+  rc = attn_setup(m, n_q_heads, n_q, hs, k, n_sink, window, scale, g);
+  if (rc) return rc;
+  rc = check_attention_buffers(g, q, idx, k, out, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (k > 2048) return fail(BRS_E_UNSUPPORTED, "k must be at most 2048");
+  if (k > 0) {
+    if (!qrep || !scores) return fail(BRS_E_INVAL, "qrep/scores must be non-NULL when k > 0");
+    if (!aligned(scores, 4) || (vals && !aligned(vals, 4))) return fail(BRS_E_INVAL, "scores/vals misaligned");
+    if (!aligned(qrep, brs::elem_bytes(cosine ? m->rep_dtype : m->dtype))) return fail(BRS_E_INVAL, "qrep misaligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  bool planned = false;
+  if (k > 0) {
+    if (hi > lo) {
+      e = cosine ? brs::launch_score_cosine(*m, qrep, lo, hi, scores, s)
+                 : brs::launch_score_dot(*m, qrep, hs, lo, hi, scores, s);
+      if (e != hipSuccess) return hip_fail(e, "score_blocks");
+    }
+    const int64_t stride = m->capacity / m->block_size;
+    if (brs::select_plan_supported(g, hi - lo)) {
+      e = brs::launch_select_plan(g, scores, stride, lo, hi, idx, vals, workspace, out, s);
+      if (e != hipSuccess) return hip_fail(e, "select_plan");
+      planned = true;
+    } else {
+      e = brs::launch_select_topk(scores, m->batch, hs, stride, lo, hi, k, idx, vals, s);
+      if (e != hipSuccess) return hip_fail(e, "select_topk");
+    }
+  }
+  return run_attention(g, m, q, k > 0 ? idx : nullptr, planned, out, workspace, s);
 }
 
 int brs_profile_next_attention(void* start_event, void* stop_event) {

@@ -24,7 +24,7 @@
 #include <math.h>
 #include <stdlib.h>
 
-#include "brs_internal.h"
+#include "brs_wave_topk.h"
 
 namespace brs {
 namespace {
@@ -182,6 +182,130 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
   }
   if (n_tokens == 0) {
     // nothing to attend for this (batch, kv head): its rows are zeros
+    const int rows = a.G * a.n_q;
+    float* o = a.out + (((int64_t)b * a.hq + g * a.G) * a.n_q) * a.d;
+    for (int i = tid; i < rows * a.d; i += nt) o[i] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// select + plan in one kernel (per-head selections, up to 16 heads per kv
+// head): one workgroup per (batch, kv head); wave j selects the top-k blocks
+// of query head g G + j (writing idx / vals) into LDS, then the workgroup
+// builds the plan from those selections exactly as attn_plan_kernel does
+// from idx, with the chunk-first table kept in LDS.
+
+constexpr int kFusedHeads = 16;   // query heads per kv head
+constexpr int kFusedK = 256;      // largest k
+constexpr int kFirstLds = 1024;   // largest chunk count per (batch, kv head)
+
+struct SelectPlanArgs {
+  PlanArgs p;
+  const float* scores;  // [batch][hq][stride]
+  float* vals;          // [batch][hq][k] or null
+  int64_t stride;
+  int lo, hi;
+};
+
+template <int KPL>
+__global__ __launch_bounds__(1024) void select_plan_kernel(SelectPlanArgs sa) {
+  const PlanArgs& a = sa.p;
+  // selection scratch (hist + sel) and block marks share one buffer
+  constexpr int kSelBytes = kFusedHeads * (256 * 4 + (kFusedK + 64) * 8);
+  constexpr int kScratch = kSelBytes > kMarkBlocks * 4 ? kSelBytes : kMarkBlocks * 4;
+  __shared__ __align__(16) unsigned char scratch[kScratch];
+  __shared__ int32_t lsel[kFusedHeads][kFusedK];
+  __shared__ int first[kFirstLds];
+  __shared__ int wave_tot[16];
+  __shared__ int sh_items, sh_tokens;
+  const int bg = blockIdx.x;
+  const int b = bg / a.hkv, g = bg - b * a.hkv;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int wave = tid >> 6;
+
+  if (wave < a.G) {
+    uint32_t* hist = reinterpret_cast<uint32_t*>(scratch) + wave * 256;
+    uint64_t* sel = reinterpret_cast<uint64_t*>(scratch + kFusedHeads * 256 * 4) + wave * (kFusedK + 64);
+    const int64_t row = (int64_t)b * a.hq + g * a.G + wave;
+    wave_topk<KPL>(sa.scores + row * sa.stride, sa.lo, sa.hi, a.k, hist, sel, const_cast<int32_t*>(a.idx) + row * a.k,
+                   sa.vals ? sa.vals + row * a.k : nullptr, lsel[wave]);
+  }
+  __syncthreads();
+
+  uint32_t* marks = reinterpret_cast<uint32_t*>(scratch);
+  int4* items = a.items + (int64_t)bg * a.max_items;
+  const int CH = a.chunk_tokens;
+  const uint32_t full = a.G >= 32 ? 0xffffffffu : ((1u << a.G) - 1u);
+  const int S = a.sink_end, Wn = a.N - a.win_start;
+  if (tid == 0) {
+    int i = 0;
+    if (S > 0) {
+      items[i] = make_int4(0, S, (int)full, 0);
+      mark_chunks(first, i, 0, S, CH);
+      ++i;
+    }
+    if (Wn > 0) {
+      items[i] = make_int4(a.win_start, Wn, (int)full, S);
+      mark_chunks(first, i, S, Wn, CH);
+    }
+  }
+  int n_items = (S > 0) + (Wn > 0), n_tokens = S + Wn;
+  const int E = a.G * a.k;
+  for (int base = 0; base < a.nb; base += kMarkBlocks) {
+    const int top = min(a.nb, base + kMarkBlocks);
+    for (int i = tid; i < top - base; i += nt) marks[i] = 0u;
+    __syncthreads();
+    for (int e = tid; e < E; e += nt) {
+      const int j = e / a.k;
+      const int blk = lsel[j][e - j * a.k];
+      if (blk >= base && blk < top) {
+        const int lo_t = max(blk * a.B, S);
+        const int hi_t = min((blk + 1) * a.B, a.win_start);
+        if (lo_t < hi_t) atomicOr(&marks[blk - base], 1u << j);
+      }
+    }
+    __syncthreads();
+    const int per = (top - base + nt - 1) / nt;
+    const int r0 = base + tid * per, r1 = min(top, r0 + per);
+    int ci = 0, ct = 0;
+    for (int blk = r0; blk < r1; ++blk) {
+      if (marks[blk - base]) {
+        ++ci;
+        ct += min((blk + 1) * a.B, a.win_start) - max(blk * a.B, S);
+      }
+    }
+    const int inc_i = block_inclusive_scan(ci, wave_tot);
+    const int inc_t = block_inclusive_scan(ct, wave_tot);
+    int oi = n_items + inc_i - ci, ot = n_tokens + inc_t - ct;
+    for (int blk = r0; blk < r1; ++blk) {
+      const uint32_t mk = marks[blk - base];
+      if (!mk) continue;
+      const int lo_t = max(blk * a.B, S);
+      const int len = min((blk + 1) * a.B, a.win_start) - lo_t;
+      items[oi] = make_int4(lo_t, len, (int)mk, ot);
+      mark_chunks(first, oi, ot, len, CH);
+      ++oi;
+      ot += len;
+    }
+    if (tid == nt - 1) {
+      sh_items = inc_i;
+      sh_tokens = inc_t;
+    }
+    __syncthreads();
+    n_items += sh_items;
+    n_tokens += sh_tokens;
+    __syncthreads();
+  }
+  if (tid == 0) a.hdr[bg] = make_int4(n_items, n_tokens, 0, 0);
+  const int n_chunks = (n_tokens + CH - 1) / CH;
+  int4* chunks = a.chunks + (int64_t)bg * a.max_chunks;
+  for (int c = tid; c < a.max_chunks; c += nt) {
+    if (c < n_chunks)
+      chunks[c] = make_int4(first[c], c + 1 < n_chunks ? first[c + 1] + 1 : n_items, min((c + 1) * CH, n_tokens), 0);
+    else
+      chunks[c] = make_int4(0, 0, 0, 0);
+  }
+  if (n_tokens == 0) {
     const int rows = a.G * a.n_q;
     float* o = a.out + (((int64_t)b * a.hq + g * a.G) * a.n_q) * a.d;
     for (int i = tid; i < rows * a.d; i += nt) o[i] = 0.f;
@@ -1047,6 +1171,55 @@ hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, flo
   a.win_start = g.win_start;
   a.chunk_tokens = g.chunk_tokens;
   hipLaunchKernelGGL(attn_plan_kernel, dim3((unsigned)(g.batch * g.hkv)), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+bool select_plan_supported(const AttnGeom& g, int64_t n) {
+  return g.idx_heads == g.hq && g.group <= kFusedHeads && g.k >= 1 && g.k <= kFusedK && n >= 1 && n <= 64 * 32 &&
+         g.max_chunks <= kFirstLds && env_int("BRS_FUSED_SELECT", 1) != 0;
+}
+
+hipError_t launch_select_plan(const AttnGeom& g, const float* scores, int64_t stride, int64_t lo, int64_t hi,
+                              int32_t* idx, float* vals, void* ws, float* out, hipStream_t s) {
+  SelectPlanArgs sa;
+  PlanArgs& a = sa.p;
+  a.idx = idx;
+  a.hdr = (int4*)((char*)ws + g.hdr_off);
+  a.items = (int4*)((char*)ws + g.items_off);
+  a.chunk_first = (int*)((char*)ws + g.first_off);
+  a.chunks = (int4*)((char*)ws + g.chunks_off);
+  a.out = out;
+  a.max_items = g.max_items;
+  a.max_chunks = g.max_chunks;
+  a.hq = g.hq;
+  a.hkv = g.hkv;
+  a.G = g.group;
+  a.k = g.k;
+  a.idx_heads = g.idx_heads;
+  a.n_q = g.n_q;
+  a.d = g.d;
+  a.row_groups = g.row_groups;
+  a.N = g.N;
+  a.B = g.B;
+  a.nb = g.nb;
+  a.sink_end = g.sink_end;
+  a.win_start = g.win_start;
+  a.chunk_tokens = g.chunk_tokens;
+  sa.scores = scores;
+  sa.vals = vals;
+  sa.stride = stride;
+  sa.lo = (int)lo;
+  sa.hi = (int)hi;
+  const int64_t n = hi - lo;
+  const dim3 grid((unsigned)(g.batch * g.hkv)), block((unsigned)(64 * (g.group > 4 ? g.group : 4)));
+  if (n <= 64 * 4)
+    hipLaunchKernelGGL(select_plan_kernel<4>, grid, block, 0, s, sa);
+  else if (n <= 64 * 8)
+    hipLaunchKernelGGL(select_plan_kernel<8>, grid, block, 0, s, sa);
+  else if (n <= 64 * 16)
+    hipLaunchKernelGGL(select_plan_kernel<16>, grid, block, 0, s, sa);
+  else
+    hipLaunchKernelGGL(select_plan_kernel<32>, grid, block, 0, s, sa);
   return hipGetLastError();
 }
 

@@ -96,6 +96,11 @@ struct AttnGeom {
 bool attn_geometry(AttnGeom& g);
 
 hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, float* out, hipStream_t s);
+// Top-k of scores columns [lo, hi) for every query head plus the plan, in one
+// kernel (per-head selections only; n = hi - lo candidates).
+bool select_plan_supported(const AttnGeom& g, int64_t n);
+hipError_t launch_select_plan(const AttnGeom& g, const float* scores, int64_t stride, int64_t lo, int64_t hi,
+                              int32_t* idx, float* vals, void* ws, float* out, hipStream_t s);
 hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
                              float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);

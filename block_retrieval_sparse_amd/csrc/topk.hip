@@ -10,17 +10,10 @@
 //   3. keep every key above it and, among keys equal to it, the lowest block
 //      indices (a prefix count over the workgroup in index order);
 //   4. sort the k winners by counting, on the 64-bit key (score key, ~index).
-#include "brs_internal.h"
+#include "brs_wave_topk.h"
 
 namespace brs {
 namespace {
-
-__device__ __forceinline__ uint32_t order_key(float s) {
-  if (s != s) return 0u;
-  uint32_t u = __float_as_uint(s);
-  if (s == 0.0f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 template <int NT, int KPT>  // KPT = 0: keys re-read from global memory each pass
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
@@ -44,7 +37,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   uint32_t keys[KPT > 0 ? KPT : 1];
   if (KPT > 0) {
 #pragma unroll
-    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) keys[i] = (my0 + i < my1) ? order_key(s[my0 + i]) : 0u;
+    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) keys[i] = (my0 + i < my1) ? topk_key(s[my0 + i]) : 0u;
   }
   auto key_at = [&](int64_t i) -> uint32_t {  // i relative to my0
     if (KPT > 0) {
@@ -54,7 +47,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         if (j == i) r = keys[j];
       return r;
     }
-    return order_key(s[my0 + i]);
+    return topk_key(s[my0 + i]);
   };
   const int64_t mine = my1 > my0 ? my1 - my0 : 0;
 
@@ -147,127 +140,21 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   }
 }
 
-// One wave per row, for up to 64 * KPL candidates and k <= kWaveK: each lane
-// owns a contiguous run of up to KPL keys in registers; the digit search and
-// the compaction use wave shuffles; four rows per workgroup.
+// One wave per row for up to 64 * KPL candidates and k <= kWaveK (the
+// selection of brs_wave_topk.h); four independent rows per workgroup.
 constexpr int kWaveK = 512;
-
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
 
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
                                                         int64_t hi, int k, int rows, int32_t* __restrict__ idx,
                                                         float* __restrict__ vals) {
   __shared__ uint32_t hist[4][256];
-  __shared__ uint64_t sel[4][kWaveK];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ uint64_t sel[4][kWaveK + 64];
+  const int w = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + w;
-  const bool active = row < rows;
-  const float* s = scores + (active ? row : 0) * stride;
-  const int n = (int)(hi - lo);
-  const int c = (n + 63) / 64;
-  const int my0 = (int)lo + lane * c;
-  const int mine = max(0, min(c, (int)hi - my0));
-  uint32_t keys[KPL];
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) keys[i] = (active && i < mine) ? order_key(s[my0 + i]) : 0u;
-
-  const bool all = n <= k;
-  uint32_t thresh = 0;
-  int take_eq = 0;
-  if (!all) {
-    uint32_t prefix = 0, mask = 0;
-    int kk = k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hist[w][4 * lane + i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < KPL; ++i)
-        if (i < mine && (keys[i] & mask) == prefix) atomicAdd(&hist[w][(keys[i] >> shift) & 255u], 1u);
-      __syncthreads();
-      int h[4], run = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[i] = (int)hist[w][255 - (4 * lane + i)];
-        run += h[i];
-      }
-      int before = wave_incl_scan(run) - run;
-      int found = -1, above = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (before < kk && before + h[i] >= kk) {
-          found = 255 - (4 * lane + i);
-          above = before;
-        }
-        before += h[i];
-      }
-      const unsigned long long who = __ballot(found >= 0);
-      const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
-      found = __shfl(found, src);
-      above = __shfl(above, src);
-      kk -= above;
-      prefix |= (uint32_t)(found < 0 ? 0 : found) << shift;
-      mask |= 0xffu << shift;
-    }
-    thresh = prefix;
-    take_eq = kk;
-  }
-  int eq = 0;
-  if (!all) {
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) eq += (i < mine && keys[i] == thresh);
-  }
-  int rank_eq = wave_incl_scan(eq) - eq;
-  bool take[KPL];
-  int ntake = 0;
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    bool t = i < mine && (all || keys[i] > thresh);
-    if (!all && i < mine && keys[i] == thresh) {
-      t = rank_eq < take_eq;
-      ++rank_eq;
-    }
-    take[i] = t;
-    ntake += t;
-  }
-  const int incl = wave_incl_scan(ntake);
-  int p = incl - ntake;
-  const int cnt = min(__shfl(incl, 63), k);
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    if (take[i]) {
-      if (p < k) sel[w][p] = ((uint64_t)keys[i] << 32) | (uint64_t)(0xffffffffu - (uint32_t)(my0 + i));
-      ++p;
-    }
-  }
-  __syncthreads();
-  if (!active) return;
-  int32_t* orow = idx + row * k;
-  float* vrow = vals ? vals + row * k : nullptr;
-  for (int i = lane; i < cnt; i += 64) {
-    const uint64_t me = sel[w][i];
-    int rank = 0;
-    for (int j = 0; j < cnt; ++j) rank += sel[w][j] > me;
-    const int64_t b = (int64_t)(0xffffffffu - (uint32_t)(me & 0xffffffffu));
-    if (rank < k) {
-      orow[rank] = (int32_t)b;
-      if (vrow) vrow[rank] = s[b];
-    }
-  }
-  for (int i = cnt + lane; i < k; i += 64) {
-    orow[i] = -1;
-    if (vrow) vrow[i] = -INFINITY;
-  }
+  if (row >= rows) return;  // whole wave; no workgroup barrier below
+  wave_topk<KPL>(scores + row * stride, (int)lo, (int)hi, k, hist[w], sel[w], idx + row * k,
+                 vals ? vals + row * k : nullptr, nullptr);
 }
 
 }  // namespace
@@ -278,7 +165,10 @@ hipError_t launch_select_topk(const float* scores, int batch, int heads, int64_t
   const int64_t n = hi - lo;
   if (k <= kWaveK && n <= 64 * 32) {
     const unsigned grid = (unsigned)((rows + 3) / 4);
-    if (n <= 64 * 8)
+    if (n <= 64 * 4)
+      hipLaunchKernelGGL((topk_wave_kernel<4>), dim3(grid), dim3(256), 0, s, scores, stride, lo, hi, k, (int)rows, idx,
+                         vals);
+    else if (n <= 64 * 8)
       hipLaunchKernelGGL((topk_wave_kernel<8>), dim3(grid), dim3(256), 0, s, scores, stride, lo, hi, k, (int)rows, idx,
                          vals);
     else if (n <= 64 * 16)

@@ -54,9 +54,24 @@ class RetrievalStep:
         return self.out
 
     def run(self, q: torch.Tensor, qrep: torch.Tensor | None = None, stream=None, profile_events=None):
-        """q ``[batch][Hq][n_q][d]`` (contiguous); qrep is q's last query
+        """One whole step in one library call (brs_retrieval_step).  q
+        ``[batch][Hq][n_q][d]`` (contiguous); qrep is q's last query
         ``[batch][Hq][d]`` for dot scoring or the chunk embedding
         ``[batch][rep_dim]`` for cosine scoring."""
+        if qrep is None:
+            qrep = q[:, :, -1, :]
+            if not qrep.is_contiguous():
+                raise ValueError("pass a contiguous qrep")
+        if profile_events is not None:
+            check(lib.brs_profile_next_attention(profile_events[0], profile_events[1]))
+        check(lib.brs_retrieval_step(self.mem.desc, q.data_ptr(), self.n_q_heads, self.n_q, qrep.data_ptr(), self.k,
+                                     self.n_sink, self.window, self.scale, self.scores.data_ptr(),
+                                     self.idx.data_ptr(), self.vals.data_ptr(), self.out.data_ptr(),
+                                     self.workspace.data_ptr(), self.workspace.numel(), _stream(stream)))
+        return self.out
+
+    def run_separate(self, q: torch.Tensor, qrep: torch.Tensor | None = None, stream=None, profile_events=None):
+        """The same step as three calls: score_blocks, select_topk, retrieval_attention."""
         if qrep is None:
             qrep = q[:, :, -1, :]
             if not qrep.is_contiguous():

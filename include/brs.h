@@ -10,7 +10,8 @@
  *   2. brs_score_blocks    -- relevance of every candidate block to the query;
  *   3. brs_select_topk     -- the k best blocks per score head;
  *   4. brs_retrieval_attention -- exact softmax attention over the sinks,
- *                             the local window and the selected blocks.
+ *                             the local window and the selected blocks;
+ *   brs_retrieval_step        -- 2 to 4 in one call.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -211,6 +212,25 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
                             const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
                             int64_t window, float scale, float* out, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* One whole step (score_blocks, select_topk, retrieval_attention) in one
+ * call, with the candidate range of brs_eligible_range(n_sink, window):
+ * identical results to the three calls made in turn, and the same
+ * selection semantics (per query head for dot scores, per sequence for
+ * cosine).  Selection and attention planning may run as one kernel.
+ *   q, out    : as brs_retrieval_attention (idx_heads = n_q_heads for dot
+ *               scores, 1 for cosine);
+ *   qrep      : as brs_score_blocks (unused when k = 0);
+ *   scores    : [batch][n_score_heads][capacity / block_size] float32;
+ *   idx, vals : [batch][n_score_heads][k] as brs_select_topk (vals may be
+ *               NULL; scores and idx may be NULL when k = 0);
+ *   workspace : brs_attention_workspace_bytes(m, n_q_heads, n_q,
+ *               n_score_heads, k, n_sink, window) bytes.
+ * Errors as the separate calls; nothing is enqueued on error. */
+int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
+                       const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
+                       float* scores, int32_t* idx, float* vals, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Measurement hook: the next brs_retrieval_attention call on this thread
  * records `start_event` and `stop_event` (hipEvent_t, passed as void*) at the

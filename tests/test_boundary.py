@@ -126,3 +126,35 @@ def test_score_select_attention_reject(L):
     assert call(sc=float("inf")) == -1
     assert call(idx=None) == -1
     assert call(q=0x1004) == -1
+
+
+def test_retrieval_step_rejects_before_device_work(L):
+    m = desc(L)
+    n = ctypes.c_size_t()
+    assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 32, 128, 1024, ctypes.byref(n)) == 0
+    ws = n.value
+    args = dict(q=0x1000, hq=8, nq=1, qrep=0x4000, k=32, S=128, Wn=1024, sc=0.1, scores=0x40000, idx=0x2000,
+                vals=0x6000, out=0x3000)
+
+    def call(ws_ptr=0x100000, ws_bytes=ws, mem=m, **kw):
+        a = dict(args)
+        a.update(kw)
+        return L.lib.brs_retrieval_step(mem, a["q"], a["hq"], a["nq"], a["qrep"], a["k"], a["S"], a["Wn"],
+                                        a["sc"], a["scores"], a["idx"], a["vals"], a["out"], ws_ptr, ws_bytes, None)
+
+    assert call(hq=7) == -1                       # not a multiple of the kv heads
+    assert call(nq=5000) == -1
+    assert call(k=0, S=0, Wn=0) == -5             # nothing to attend
+    assert call(k=4096) == -3                     # beyond the selection limit
+    assert call(ws_bytes=ws - 1) == -6
+    assert call(ws_ptr=0x100010) == -6
+    assert call(qrep=None) == -1
+    assert call(scores=None) == -1
+    assert call(idx=None) == -1
+    assert call(scores=0x40002) == -1             # misaligned
+    assert call(sc=float("nan")) == -1
+    assert call(mem=desc(L, reserved=1)) == -1
+    assert call(S=-1) == -1
+    e = desc(L, rep_mode=L.REP_EMBED, rep_heads=1, rep_dim=768)
+    assert L.lib.brs_attention_workspace_bytes(e, 8, 1, 1, 32, 128, 1024, ctypes.byref(n)) == 0
+    assert call(mem=e, ws_bytes=n.value, qrep=0x4001) == -1   # cosine query misaligned

@@ -219,3 +219,24 @@ def test_full_size_memlong_prefill_sampled():
     res = C.check_step(w, mem, x, step, pairs=[(0, 0), (0, 17), (0, 31)],
                        query_rows=[0, 1, 63, 64, 255, 448, 510, 511])
     print(f"memlong: max |err| {res['max_abs_err']:.3g}")
+
+
+@pytest.mark.parametrize("name", ["infllm", "gqa8", "landmark", "retrieval", "memlong", "multi_q", "prefill_gqa"])
+def test_step_call_matches_separate_calls(name):
+    """brs_retrieval_step (selection and plan fused where supported) gives the
+    same scores, selection and attention bits as the three separate calls."""
+    from block_retrieval_sparse_amd.pipeline import RetrievalStep
+
+    w = SMALL[name]
+    mem, x = C.load(w)
+    qrep = x["rq"] if w.rep_mode == "embed" else x["q"][:, :, -1, :].contiguous()
+    one = RetrievalStep(mem, w.n_q_heads, w.n_q, w.k, w.sinks, w.window)
+    three = RetrievalStep(mem, w.n_q_heads, w.n_q, w.k, w.sinks, w.window)
+    one.run(x["q"], qrep)
+    three.run_separate(x["q"], qrep)
+    torch.cuda.synchronize()
+    lo, hi = one.lo, one.hi
+    assert torch.equal(one.scores[:, :, lo:hi], three.scores[:, :, lo:hi])
+    assert torch.equal(one.idx, three.idx)
+    assert torch.equal(one.vals, three.vals)
+    assert torch.equal(one.out, three.out)
