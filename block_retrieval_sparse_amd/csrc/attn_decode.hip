@@ -30,7 +30,6 @@ namespace brs {
 namespace {
 
 constexpr float kNegInf = -INFINITY;
-constexpr int kMergeC = 256;   // chunk weights cached in LDS by the merging workgroup
 constexpr int kItemsLds = 256;  // segments of one chunk staged in LDS
 constexpr int kTargetWaves = 2048;
 
@@ -379,29 +378,15 @@ __device__ __forceinline__ int stage_items(const SplitArgs& a, int bg, const int
 // ---------------------------------------------------------------------------
 // merge: one workgroup per query row.
 //   out = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  M = max_c m_c.
-// Chunks are split into `slices` interleaved runs whose loads are all in
-// flight; runs are summed in increasing slice order (deterministic).
-
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  __syncthreads();
-  if (lane == 0) tmp[wave] = v;
-  __syncthreads();
-  v = tmp[0];
-  for (int w = 1; w < nwaves; ++w) v = is_max ? fmaxf(v, tmp[w]) : v + tmp[w];
-  return v;
-}
+// Chunks are split into `slices` interleaved runs; each thread issues the
+// loads of eight chunks at once and keeps a running log-sum-exp; the runs
+// are combined in increasing slice order (deterministic).
 
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict__ hdr, const float2* __restrict__ ml,
                                                         const float* __restrict__ o, float* __restrict__ out, int hq,
                                                         int hkv, int n_q, int d, int chunk_tokens, int max_chunks) {
-  __shared__ float tmp[16];
-  __shared__ float sh_w[kMergeC];
-  __shared__ float4 red[256];
+  __shared__ float4 s_acc[256];
+  __shared__ float2 s_ml[256];
   const int64_t row = blockIdx.x;  // ((b * hq + h) * n_q + i)
   const int64_t bh = row / n_q;
   const int b = (int)(bh / hq), h = (int)(bh - (int64_t)b * hq);
@@ -410,62 +395,91 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict_
   if (n_tokens == 0) return;  // the plan kernel wrote zeros
   const int n_chunks = min((n_tokens + chunk_tokens - 1) / chunk_tokens, max_chunks);
   const float2* mlr = ml + row * max_chunks;
-  float M = kNegInf;
-  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) M = fmaxf(M, mlr[c].x);
-  M = block_reduce(M, true, tmp);
-  float L = 0.f;
-  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
-    const float2 v = mlr[c];
-    if (v.x != kNegInf) L += v.y * exp2f(v.x - M);
-  }
-  L = block_reduce(L, false, tmp);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int c = threadIdx.x; c < min(n_chunks, kMergeC); c += blockDim.x) {
-    const float mc = mlr[c].x;
-    sh_w[c] = (mc == kNegInf) ? 0.f : exp2f(mc - M) * inv;
-  }
-  __syncthreads();
-  auto weight = [&](int c) -> float {
-    if (c < kMergeC) return sh_w[c];
-    const float mc = mlr[c].x;
-    return (mc == kNegInf) ? 0.f : exp2f(mc - M) * inv;
-  };
   const float* ob = o + row * max_chunks * (int64_t)d;
   if ((d & 3) == 0 && d / 4 <= (int)blockDim.x) {
+    // thread (slice sl, float4 column e4) takes chunks sl, sl + slices, ...:
+    // all its loads are issued together, then a local log-sum-exp, then the
+    // slices combine in slice order
     const int D4 = d >> 2;
     const int slices = blockDim.x / D4;
     const int e4 = threadIdx.x % D4, sl = threadIdx.x / D4;
+    float m = -INFINITY, l = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (sl < slices) {
       const float4* p = reinterpret_cast<const float4*>(ob) + e4;
-#pragma unroll 8
-      for (int c = sl; c < n_chunks; c += slices) {
-        const float w = weight(c);
-        const float4 v = p[(int64_t)c * D4];
-        acc.x = fmaf(v.x, w, acc.x);
-        acc.y = fmaf(v.y, w, acc.y);
-        acc.z = fmaf(v.z, w, acc.z);
-        acc.w = fmaf(v.w, w, acc.w);
+      for (int c0 = sl; c0 < n_chunks; c0 += 8 * slices) {
+        float2 v[8];
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * slices;
+          const bool ok = c < n_chunks;
+          v[u] = ok ? mlr[c] : make_float2(-INFINITY, 0.f);
+          x[u] = ok ? p[(int64_t)c * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mn = fmaxf(mn, v[u].x);
+        if (mn != -INFINITY) {
+          const float al = exp2f(m - mn);  // m = -inf gives 0
+          l *= al;
+          acc.x *= al;
+          acc.y *= al;
+          acc.z *= al;
+          acc.w *= al;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float w = v[u].x == -INFINITY ? 0.f : exp2f(v[u].x - mn);
+            l = fmaf(v[u].y, w, l);
+            acc.x = fmaf(x[u].x, w, acc.x);
+            acc.y = fmaf(x[u].y, w, acc.y);
+            acc.z = fmaf(x[u].z, w, acc.z);
+            acc.w = fmaf(x[u].w, w, acc.w);
+          }
+          m = mn;
+        }
       }
     }
-    red[threadIdx.x] = acc;
+    s_acc[threadIdx.x] = acc;
+    s_ml[threadIdx.x] = make_float2(m, l);
     __syncthreads();
     if (threadIdx.x < D4) {
-      float4 t = red[threadIdx.x];
-      for (int s2 = 1; s2 < slices; ++s2) {
-        const float4 v = red[s2 * D4 + threadIdx.x];
-        t.x += v.x;
-        t.y += v.y;
-        t.z += v.z;
-        t.w += v.w;
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < slices; ++s2) M = fmaxf(M, s_ml[s2 * D4 + threadIdx.x].x);
+      float L = 0.f;
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (M != -INFINITY) {
+        for (int s2 = 0; s2 < slices; ++s2) {
+          const float2 q = s_ml[s2 * D4 + threadIdx.x];
+          const float w = q.x == -INFINITY ? 0.f : exp2f(q.x - M);
+          const float4 v = s_acc[s2 * D4 + threadIdx.x];
+          L = fmaf(q.y, w, L);
+          t.x = fmaf(v.x, w, t.x);
+          t.y = fmaf(v.y, w, t.y);
+          t.z = fmaf(v.z, w, t.z);
+          t.w = fmaf(v.w, w, t.w);
+        }
       }
-      reinterpret_cast<float4*>(out + row * d)[threadIdx.x] = t;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      reinterpret_cast<float4*>(out + row * d)[threadIdx.x] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
     }
     return;
   }
+  // any head dim: one pass for the maximum, one for the sum and the output
+  float M = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, mlr[c].x);
+  float L = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    const float2 v = mlr[c];
+    L += v.x == -INFINITY ? 0.f : v.y * exp2f(v.x - M);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   for (int e = threadIdx.x; e < d; e += blockDim.x) {
     float acc = 0.f;
-    for (int c = 0; c < n_chunks; ++c) acc = fmaf(ob[(int64_t)c * d + e], weight(c), acc);
+    for (int c = 0; c < n_chunks; ++c) {
+      const float mc = mlr[c].x;
+      acc = fmaf(ob[(int64_t)c * d + e], mc == -INFINITY ? 0.f : exp2f(mc - M) * inv, acc);
+    }
     out[row * d + e] = acc;
   }
 }
