@@ -189,10 +189,11 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
 
 // ---------------------------------------------------------------------------
 // select + plan in one kernel (per-head selections, up to 16 heads per kv
-// head): one workgroup per (batch, kv head); wave j selects the top-k blocks
-// of query head g G + j (writing idx / vals) into LDS, then the workgroup
-// builds the plan from those selections exactly as attn_plan_kernel does
-// from idx, with the chunk-first table kept in LDS.
+// head): one workgroup per (batch, kv head); thread group j (64 to 256
+// threads) selects the top-k blocks of query head g G + j (writing idx /
+// vals) into LDS, then the workgroup builds the plan from those selections
+// exactly as attn_plan_kernel does from idx, with the chunk-first table kept
+// in LDS.
 
 constexpr int kFusedHeads = 16;   // query heads per kv head
 constexpr int kFusedK = 256;      // largest k
@@ -206,28 +207,34 @@ struct SelectPlanArgs {
   int lo, hi;
 };
 
-template <int KPL>
+template <int KPT>
 __global__ __launch_bounds__(1024) void select_plan_kernel(SelectPlanArgs sa) {
   const PlanArgs& a = sa.p;
-  // selection scratch (hist + sel) and block marks share one buffer
-  constexpr int kSelBytes = kFusedHeads * (256 * 4 + (kFusedK + 64) * 8);
+  // selection state (per row) and block marks share one buffer
+  constexpr int kSelBytes = kFusedHeads * (int)(sizeof(TopkRowShared) + kFusedK * 8);
   constexpr int kScratch = kSelBytes > kMarkBlocks * 4 ? kSelBytes : kMarkBlocks * 4;
   __shared__ __align__(16) unsigned char scratch[kScratch];
   __shared__ int32_t lsel[kFusedHeads][kFusedK];
   __shared__ int first[kFirstLds];
   __shared__ int wave_tot[16];
-  __shared__ int sh_items, sh_tokens;
+  __shared__ int sh_items, sh_tokens, sh_flag;
   const int bg = blockIdx.x;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int wave = tid >> 6;
 
-  if (wave < a.G) {
-    uint32_t* hist = reinterpret_cast<uint32_t*>(scratch) + wave * 256;
-    uint64_t* sel = reinterpret_cast<uint64_t*>(scratch + kFusedHeads * 256 * 4) + wave * (kFusedK + 64);
-    const int64_t row = (int64_t)b * a.hq + g * a.G + wave;
-    wave_topk<KPL>(sa.scores + row * sa.stride, sa.lo, sa.hi, a.k, hist, sel, const_cast<int32_t*>(a.idx) + row * a.k,
-                   sa.vals ? sa.vals + row * a.k : nullptr, lsel[wave]);
+  // row group j = tid / tpr selects the top-k of query head g G + j
+  const int tpr = nt / a.G;
+  TopkRowShared* shs = reinterpret_cast<TopkRowShared*>(scratch);
+  uint64_t* sels = reinterpret_cast<uint64_t*>(scratch + kFusedHeads * sizeof(TopkRowShared));
+  for (int i = tid; i < a.G * 256; i += nt) shs[i / 256].hist[i % 256] = 0u;
+  if (tid < a.G) shs[tid].cnt = 0;
+  if (tid == 0) sh_flag = 0;
+  __syncthreads();
+  {
+    const int j = tid / tpr;
+    const int64_t row = (int64_t)b * a.hq + g * a.G + j;
+    group_topk<KPT>(sa.scores + row * sa.stride, sa.lo, sa.hi, a.k, tpr, shs[j], &sh_flag, sels + j * kFusedK,
+                    const_cast<int32_t*>(a.idx) + row * a.k, sa.vals ? sa.vals + row * a.k : nullptr, lsel[j]);
   }
   __syncthreads();
 
@@ -1225,12 +1232,19 @@ hipError_t launch_select_plan(const AttnGeom& g, const float* scores, int64_t st
   sa.lo = (int)lo;
   sa.hi = (int)hi;
   const int64_t n = hi - lo;
-  const dim3 grid((unsigned)(g.batch * g.hkv)), block((unsigned)(64 * (g.group > 4 ? g.group : 4)));
-  if (n <= 64 * 4)
+  int tpr = 256;
+  while (tpr * g.group > 1024) tpr >>= 1;  // 64 threads per row at 16 heads
+  const dim3 grid((unsigned)(g.batch * g.hkv)), block((unsigned)(tpr * g.group));
+  const int64_t kpt = (n + tpr - 1) / tpr;
+  if (kpt <= 1)
+    hipLaunchKernelGGL(select_plan_kernel<1>, grid, block, 0, s, sa);
+  else if (kpt <= 2)
+    hipLaunchKernelGGL(select_plan_kernel<2>, grid, block, 0, s, sa);
+  else if (kpt <= 4)
     hipLaunchKernelGGL(select_plan_kernel<4>, grid, block, 0, s, sa);
-  else if (n <= 64 * 8)
+  else if (kpt <= 8)
     hipLaunchKernelGGL(select_plan_kernel<8>, grid, block, 0, s, sa);
-  else if (n <= 64 * 16)
+  else if (kpt <= 16)
     hipLaunchKernelGGL(select_plan_kernel<16>, grid, block, 0, s, sa);
   else
     hipLaunchKernelGGL(select_plan_kernel<32>, grid, block, 0, s, sa);

@@ -1,19 +1,18 @@
-// Exact top-k of one row of block scores by a single wave (MemLong 2.3.2:
-// the top-k of the similarity scores, found by an exact search, 2.4.2).
+// Exact top-k of one row of block scores by a group of 64 to 256 threads
+// (MemLong 2.3.2: the top-k of the similarity scores, found by an exact
+// search, 2.4.2).
 //
 // Order: score descending, then block index ascending; NaN below every
-// number; -0 equal to +0.  The wave holds up to 64 * KPL scores in
-// registers, loaded coalesced (element i of lane l is column lo + 64 i + l,
-// so index order is i-major, lane-minor).  Steps:
+// number; -0 equal to +0.  Each thread holds up to KPT scores in registers,
+// loaded coalesced (element i of thread t is column lo + tpr i + t).  Steps:
 //   1. map each score to a 32-bit key whose unsigned order is the score
 //      order (NaN -> 0, +-0 -> 0x80000000);
 //   2. radix-select the k-th largest key, 8 bits per pass, with a 256-bin
-//      histogram in the wave's own LDS (no workgroup barrier); a pass whose
-//      remaining candidates all share one digit needs no histogram;
-//   3. keep every key above it and, of the keys equal to it, those with the
-//      lowest indices (ballot prefix counts in index order), compacted by
-//      ballot into LDS;
-//   4. rank the kept entries by counting on the 64-bit key (score key, ~index).
+//      histogram per row in LDS;
+//   3. if more keys equal that threshold than there are places left, pick
+//      the lowest indices among them by a second radix select on ~index;
+//   4. gather the k kept entries (any order) and rank them by counting on the
+//      64-bit key (score key, ~index), which is the output order.
 // Returned scores are the row's own values (re-read for the zero and NaN
 // keys, whose sign or payload the key does not keep).
 #ifndef BRS_WAVE_TOPK_H_
@@ -35,28 +34,6 @@ __device__ __forceinline__ float topk_key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// wave-wide min / max of unsigned values (DPP within rows, then lane swaps)
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));
-  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  v = min(a[0], a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return min(b[0], b[1]);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));
-  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  v = max(a[0], a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return max(b[0], b[1]);
-}
-
 // makes this wave's LDS writes visible to its own later LDS reads
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -76,114 +53,151 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
   return v;
 }
 
-// Top-k of srow[lo, hi) (hi - lo <= 64 * KPL, 1 <= k).  hist: 256 words
-// of LDS, sel: k + 64 64-bit words of LDS (the last 64 absorb the writes of
-// lanes that keep nothing), both private to the wave.  Results in rank
-// order go to gidx / gvals (global; gvals may be null) and lidx (LDS; may be
-// null); slots past min(k, hi - lo) get -1 and -inf.
-template <int KPL>
-__device__ void wave_topk(const float* __restrict__ srow, int lo, int hi, int k, uint32_t* hist, uint64_t* sel,
-                          int32_t* gidx, float* gvals, int32_t* lidx) {
-  const int lane = threadIdx.x & 63;
-  const int n = hi - lo;
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  uint32_t keys[KPL];
-  uint32_t vmask = 0u;
-  if (n > 0) {
-    // unconditional loads (lanes past the end re-read column lo) keep them all in flight
+// LDS state of one row's selection.
+struct TopkRowShared {
+  uint32_t hist[256];
+  int wtot[4];
+  int digit, above, neq, cnt;
+};
+
+// One radix pass over the keys still matching `prefix` under `mask`:
+// finds the digit (bits shift..shift+7) that holds the kk-th largest key.
+// Every thread of the workgroup must call it (three barriers).  hist is
+// zero on entry and on exit.  A wave whose matching keys in one slot share
+// a digit adds them with one atomic instead of one per lane.
+template <int KPT>
+__device__ __forceinline__ void topk_radix_pass(const uint32_t (&keys)[KPT], uint32_t vmask, uint32_t prefix,
+                                                uint32_t mask, int shift, int& kk, int tpr, TopkRowShared& sh,
+                                                uint32_t& digit_out) {
+  const int t = threadIdx.x % tpr, lane = threadIdx.x & 63, wv = t >> 6;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int e = lo + 64 * i + lane;
-      const bool v = e < hi;
-      keys[i] = topk_key(srow[v ? e : lo]);
-      vmask |= v ? (1u << i) : 0u;
+  for (int i = 0; i < KPT; ++i) {
+    const bool match = ((vmask >> i) & 1u) && (keys[i] & mask) == prefix;
+    const uint32_t dg = (keys[i] >> shift) & 255u;
+    const uint64_t m = __ballot(match);
+    if (m) {
+      const int src = (int)__ffsll((long long)m) - 1;
+      const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+      const bool same = __ballot(match && dg == d0) == m;
+      if (same) {
+        if (lane == src) atomicAdd(&sh.hist[d0], (uint32_t)__popcll(m));
+      } else if (match) {
+        atomicAdd(&sh.hist[dg], 1u);
+      }
     }
   }
-  const bool all = n <= k;
-  uint32_t thresh = 0u;
-  int take_eq = 0;
-  if (!all) {
-    uint32_t prefix = 0u, mask = 0u;
-    int kk = k;
+  __syncthreads();
+  // bins in descending digit order, 256 / tpr per thread (tpr <= 256)
+  const int bpt = 256 / tpr;
+  int h[4] = {0, 0, 0, 0}, run = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < bpt) {
+      const int bin = 255 - (bpt * t + j);
+      h[j] = (int)sh.hist[bin];
+      sh.hist[bin] = 0u;
+      run += h[j];
+    }
+  const int incl = wave_scan_incl(run);
+  if (lane == 63) sh.wtot[wv] = incl;
+  __syncthreads();
+  int before = incl - run;
+  for (int w = 0; w < wv; ++w) before += sh.wtot[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < bpt) {
+      if (before < kk && before + h[j] >= kk) {
+        sh.digit = 255 - (bpt * t + j);
+        sh.above = before;
+        sh.neq = h[j];
+      }
+      before += h[j];
+    }
+  __syncthreads();
+  digit_out = (uint32_t)sh.digit;
+  kk -= sh.above;
+}
+
+// Radix select of the kk-th largest key among the valid ones (4 passes).
+// Returns the threshold key; kk becomes the number of keys equal to it to
+// take, and sh.neq holds how many there are.
+template <int KPT>
+__device__ __forceinline__ uint32_t topk_radix_select(const uint32_t (&keys)[KPT], uint32_t vmask, int& kk, int tpr,
+                                                      TopkRowShared& sh) {
+  uint32_t prefix = 0u, mask = 0u;
 #pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      // common case: every candidate still in play has the same digit
-      {
-        uint32_t dmin = 0xffffffffu, dmax = 0u;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t dg;
+    topk_radix_pass<KPT>(keys, vmask, prefix, mask, shift, kk, tpr, sh, dg);
+    prefix |= dg << shift;
+    mask |= 0xffu << shift;
+  }
+  return prefix;
+}
+
+// Top-k of srow[lo, hi) by the tpr threads of one row group (tpr a power of
+// two in 64..256, hi - lo <= tpr * KPT, 1 <= k).  Every thread of the
+// workgroup must call it, with the same lo, hi and k (barriers).  sh:
+// zeroed hist and cnt; sel: k 64-bit words of LDS.  Results in rank order
+// go to gidx / gvals (global; gvals may be null) and lidx (LDS; may be
+// null); slots past min(k, hi - lo) get -1 and -inf.
+template <int KPT>
+__device__ void group_topk(const float* __restrict__ srow, int lo, int hi, int k, int tpr, TopkRowShared& sh,
+                           int* wg_flag, uint64_t* sel, int32_t* gidx, float* gvals, int32_t* lidx) {
+  const int t = threadIdx.x % tpr;
+  const int n = hi - lo;
+  uint32_t keys[KPT];
+  uint32_t vmask = 0u;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i)
-          if (((vmask >> i) & 1u) && (keys[i] & mask) == prefix) {
-            const uint32_t dg = (keys[i] >> shift) & 255u;
-            dmin = dg < dmin ? dg : dmin;
-            dmax = dg > dmax ? dg : dmax;
-          }
-        dmin = (uint32_t)wave_min_u32(dmin);
-        dmax = (uint32_t)wave_max_u32(dmax);
-        if (dmin == dmax) {
-          prefix |= dmin << shift;
-          mask |= 0xffu << shift;
-          continue;
-        }
+  for (int i = 0; i < KPT; ++i) {
+    const int e = lo + tpr * i + t;
+    const bool v = e < hi;
+    // unconditional loads (lanes past the end re-read column lo) keep them all in flight
+    keys[i] = n > 0 ? topk_key(srow[v ? e : lo]) : 0u;
+    vmask |= v ? (1u << i) : 0u;
+  }
+  const bool all = n <= k;  // the same for every row of the workgroup
+  uint32_t thresh = 0u, thresh2 = 0u;
+  bool ties = false;
+  if (!all) {
+    int kk = k;
+    thresh = topk_radix_select<KPT>(keys, vmask, kk, tpr, sh);
+    // more keys equal to the threshold than places: the lowest indices win,
+    // i.e. the largest ~index, found by a second select among those keys
+    ties = sh.neq > kk;
+    if (t == 0 && ties) *wg_flag = 1;
+    __syncthreads();
+    if (*wg_flag) {
+      uint32_t keys2[KPT];
+      uint32_t vmask2 = 0u;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        keys2[i] = 0xffffffffu - (uint32_t)(lo + tpr * i + t);
+        vmask2 |= (((vmask >> i) & 1u) && keys[i] == thresh) ? (1u << i) : 0u;
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) hist[4 * lane + t] = 0u;
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < KPL; ++i)
-        if (((vmask >> i) & 1u) && (keys[i] & mask) == prefix) atomicAdd(&hist[(keys[i] >> shift) & 255u], 1u);
-      wave_lds_sync();
-      // lane l holds the bins of digits 255 - 4l .. 252 - 4l (descending)
-      int h[4], run = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        h[t] = (int)hist[255 - (4 * lane + t)];
-        run += h[t];
-      }
-      int before = wave_scan_incl(run) - run;
-      int found = -1, above = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (before < kk && before + h[t] >= kk) {
-          found = 255 - (4 * lane + t);
-          above = before;
-        }
-        before += h[t];
-      }
-      const uint64_t who = __ballot(found >= 0);
-      const int src = who ? (int)__ffsll((long long)who) - 1 : 0;
-      found = __shfl(found, src);
-      above = __shfl(above, src);
-      kk -= above;
-      prefix |= (uint32_t)(found < 0 ? 0 : found) << shift;
-      mask |= 0xffu << shift;
-      wave_lds_sync();
+      int kk2 = kk > 0 ? kk : 1;
+      thresh2 = topk_radix_select<KPT>(keys2, vmask2, kk2, tpr, sh);
+      if (kk <= 0) thresh2 = 0xffffffffu;  // nothing equal to the threshold is taken
     }
-    thresh = prefix;
-    take_eq = kk;
   }
-  // keep, in index order: keys above the threshold, then the first take_eq equal to it
-  int eq_base = 0, base = 0;
+  // the kept keys, in any order, then ranked by (score key, ~index)
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
+  for (int i = 0; i < KPT; ++i) {
     const bool v = (vmask >> i) & 1u;
-    const bool gt = v && (all || keys[i] > thresh);
-    const bool eq = v && !all && keys[i] == thresh;
-    const uint64_t em = __ballot(eq);
-    const int er = eq_base + __popcll(em & lt);
-    eq_base += __popcll(em);
-    const bool take = gt || (eq && er < take_eq);
-    const uint64_t tm = __ballot(take);
-    const int p = base + __popcll(tm & lt);
-    sel[(take && p < k) ? p : k + lane] =
-        ((uint64_t)keys[i] << 32) | (uint64_t)(0xffffffffu - (uint32_t)(lo + 64 * i + lane));
-    base += __popcll(tm);
+    const uint32_t inv_idx = 0xffffffffu - (uint32_t)(lo + tpr * i + t);
+    const bool take = v && (all || keys[i] > thresh || (keys[i] == thresh && (!ties || inv_idx >= thresh2)));
+    if (take) {
+      const int p = atomicAdd(&sh.cnt, 1);
+      if (p < k) sel[p] = ((uint64_t)keys[i] << 32) | (uint64_t)inv_idx;
+    }
   }
-  const int cnt = base < k ? base : k;
-  wave_lds_sync();
-  for (int r = lane; r < cnt; r += 64) {
+  __syncthreads();
+  const int cnt = sh.cnt < k ? sh.cnt : k;
+  for (int r = t; r < cnt; r += tpr) {
     const uint64_t me = sel[r];
     int rank = 0;
+#pragma unroll 8
     for (int j = 0; j < cnt; ++j) rank += sel[j] > me;
     const int b = (int)(0xffffffffu - (uint32_t)(me & 0xffffffffu));
     const uint32_t key = (uint32_t)(me >> 32);
@@ -192,7 +206,7 @@ __device__ void wave_topk(const float* __restrict__ srow, int lo, int hi, int k,
     if (gvals) gvals[rank] = val;
     if (lidx) lidx[rank] = b;
   }
-  for (int r = cnt + lane; r < k; r += 64) {
+  for (int r = cnt + t; r < k; r += tpr) {
     gidx[r] = -1;
     if (gvals) gvals[r] = -INFINITY;
     if (lidx) lidx[r] = -1;

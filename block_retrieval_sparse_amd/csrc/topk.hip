@@ -140,21 +140,26 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   }
 }
 
-// One wave per row for up to 64 * KPL candidates and k <= kWaveK (the
-// selection of brs_wave_topk.h); four independent rows per workgroup.
-constexpr int kWaveK = 512;
+// One 256-thread workgroup per row for up to 256 * KPT candidates and
+// k <= kGroupK (the selection of brs_wave_topk.h).
+constexpr int kGroupK = 512;
 
-template <int KPL>
-__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
-                                                        int64_t hi, int k, int rows, int32_t* __restrict__ idx,
-                                                        float* __restrict__ vals) {
-  __shared__ uint32_t hist[4][256];
-  __shared__ uint64_t sel[4][kWaveK + 64];
-  const int w = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + w;
-  if (row >= rows) return;  // whole wave; no workgroup barrier below
-  wave_topk<KPL>(scores + row * stride, (int)lo, (int)hi, k, hist[w], sel[w], idx + row * k,
-                 vals ? vals + row * k : nullptr, nullptr);
+template <int KPT>
+__global__ __launch_bounds__(256) void topk_group_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
+                                                         int64_t hi, int k, int32_t* __restrict__ idx,
+                                                         float* __restrict__ vals) {
+  __shared__ TopkRowShared sh;
+  __shared__ uint64_t sel[kGroupK];
+  __shared__ int flag;
+  const int64_t row = blockIdx.x;
+  for (int i = threadIdx.x; i < 256; i += 256) sh.hist[i] = 0u;
+  if (threadIdx.x == 0) {
+    sh.cnt = 0;
+    flag = 0;
+  }
+  __syncthreads();
+  group_topk<KPT>(scores + row * stride, (int)lo, (int)hi, k, 256, sh, &flag, sel, idx + row * k,
+                  vals ? vals + row * k : nullptr, nullptr);
 }
 
 }  // namespace
@@ -163,20 +168,16 @@ hipError_t launch_select_topk(const float* scores, int batch, int heads, int64_t
                               int k, int32_t* idx, float* vals, hipStream_t s) {
   const int64_t rows = (int64_t)batch * heads;
   const int64_t n = hi - lo;
-  if (k <= kWaveK && n <= 64 * 32) {
-    const unsigned grid = (unsigned)((rows + 3) / 4);
-    if (n <= 64 * 4)
-      hipLaunchKernelGGL((topk_wave_kernel<4>), dim3(grid), dim3(256), 0, s, scores, stride, lo, hi, k, (int)rows, idx,
-                         vals);
-    else if (n <= 64 * 8)
-      hipLaunchKernelGGL((topk_wave_kernel<8>), dim3(grid), dim3(256), 0, s, scores, stride, lo, hi, k, (int)rows, idx,
-                         vals);
-    else if (n <= 64 * 16)
-      hipLaunchKernelGGL((topk_wave_kernel<16>), dim3(grid), dim3(256), 0, s, scores, stride, lo, hi, k, (int)rows,
-                         idx, vals);
+  if (k <= kGroupK && n <= 256 * 8) {
+    const dim3 grid((unsigned)rows), block(256);
+    if (n <= 256)
+      hipLaunchKernelGGL((topk_group_kernel<1>), grid, block, 0, s, scores, stride, lo, hi, k, idx, vals);
+    else if (n <= 512)
+      hipLaunchKernelGGL((topk_group_kernel<2>), grid, block, 0, s, scores, stride, lo, hi, k, idx, vals);
+    else if (n <= 1024)
+      hipLaunchKernelGGL((topk_group_kernel<4>), grid, block, 0, s, scores, stride, lo, hi, k, idx, vals);
     else
-      hipLaunchKernelGGL((topk_wave_kernel<32>), dim3(grid), dim3(256), 0, s, scores, stride, lo, hi, k, (int)rows,
-                         idx, vals);
+      hipLaunchKernelGGL((topk_group_kernel<8>), grid, block, 0, s, scores, stride, lo, hi, k, idx, vals);
     return hipGetLastError();
   }
   if (n <= 256 * 4)
