@@ -105,18 +105,21 @@ __device__ __forceinline__ float xsum16_32(float v) {
 }
 
 // DP: head dim rounded up to a multiple of 32 (the k chunk of the S^T MFMA).
+// NJ: 16-column output tiles in use, ceil(d / 16) (compile-time, so the
+// P V loop has no branches).
 // ONES: V carries a column of ones in a spare padded column (head dims with
 // d mod 16 in 1..8), so the P V products also yield the softmax row sums.
-template <int DP, bool ONES>
+template <int DP, int NJ, bool ONES>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   constexpr int KC = DP / 32;
-  constexpr int NJ = DP / 16;
+  static_assert(NJ >= 1 && NJ <= DP / 16, "output tiles");
   constexpr int KP = DP + 16;  // LDS row pitch in halves (keeps transposed reads conflict-free)
   constexpr int VPT = (kStage * (DP / 8) + 255) / 256;  // 16-byte vectors per thread and stage
   constexpr int BUF = kStage * KP;                      // halves per stage buffer
   // stage buffers: K in [0, 3 BUF), V in [3 BUF, 6 BUF)
   __shared__ __align__(16) uint16_t s_kv[2 * kBufs * BUF];
-  __shared__ int2 s_tab[kTabTokens];  // (position, K/V row byte offset) of stream tokens, a ring
+  __shared__ int2 s_tab[kTabTokens];
+  __shared__ uint4 s_junk[256];  // (position, K/V row byte offset) of stream tokens, a ring
   __shared__ int4 s_items[kPrefItems];
   __shared__ int wave_tot[16];
   __shared__ int sh_tot[4];
@@ -233,11 +236,14 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < VPT; ++j)
       dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at[j], 0, 0));
   };
+  // lanes without a vector store into a junk slot: no branch around the stores
   auto stage_store = [&](const uint4(&src)[VPT], int stage) {
     const int base = (stage % kBufs) * BUF;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j)
-      if (soff[j] >= 0) *reinterpret_cast<uint4*>(s_kv + base + soff[j]) = src[j];
+    for (int j = 0; j < VPT; ++j) {
+      uint4* dst = soff[j] >= 0 ? reinterpret_cast<uint4*>(s_kv + base + soff[j]) : &s_junk[t256];
+      *dst = src[j];
+    }
   };
 
   // query rows of this wave as the B operand of S^T = K Q^T.  Rows past the
@@ -263,7 +269,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     }
   }
   const float qs = a.qscale;
-  const bool qs_pos = qs >= 0.f;
 
   f32x4_p o[NJ];
 #pragma unroll
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     bf16x8_p vb[NJ];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
-      if (jj < a.nj) {
+      {
         const int col = 16 * jj + 4 * (n & 3);
         const i16x4_p v0 =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)(vbuf + (r0 + 4 * g4 + (n >> 2)) * KP + col));
@@ -321,21 +326,13 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
           vis[4 * sidx + i] = pos <= plim;
         }
     }
-    // row extreme of the raw scores over visible tokens (the maximum of
-    // scale * s is scale * max s for scale >= 0, scale * min s otherwise)
-    float e;
-    if (qs_pos) {
-      e = -INFINITY;
+    // scaled logits (log2 units) and their row maximum over visible tokens
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e = fmaxf(e, vis[i] ? sv[i] : -INFINITY);
-      e = xmax16_32(e);
-    } else {
-      e = INFINITY;
+    for (int i = 0; i < 8; ++i) sv[i] = sv[i] * qs;
+    float e = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e = fminf(e, vis[i] ? sv[i] : INFINITY);
-      e = xmin16_32(e);
-    }
-    const float tm = __builtin_isinf(e) ? -INFINITY : e * qs;
+    for (int i = 0; i < 8; ++i) e = fmaxf(e, vis[i] ? sv[i] : -INFINITY);
+    const float tm = xmax16_32(e);
     if (__ballot(tm > mref + kLazyP)) {
       const float nm = fmaxf(mref, tm);
       const float al = exp2_fast(mref - nm);
@@ -353,8 +350,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x2_p p2;
-      p2.x = exp2_fast(__builtin_fmaf(sv[2 * i], qs, -mref));
-      p2.y = exp2_fast(__builtin_fmaf(sv[2 * i + 1], qs, -mref));
+      p2.x = exp2_fast(sv[2 * i] - mref);
+      p2.y = exp2_fast(sv[2 * i + 1] - mref);
       p2.x = vis[2 * i] ? p2.x : 0.f;
       p2.y = vis[2 * i + 1] ? p2.y : 0.f;
       const bf16x2_p hi = __builtin_convertvector(p2, bf16x2_p);
@@ -367,10 +364,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     const bf16x8_p pa_lo = __builtin_bit_cast(bf16x8_p, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
-      if (jj < a.nj) o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[jj], o[jj], 0, 0, 0);
+      o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[jj], o[jj], 0, 0, 0);
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
-      if (jj < a.nj) o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[jj], o[jj], 0, 0, 0);
+      o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[jj], o[jj], 0, 0, 0);
   };
 
   // Pipeline over stages, three LDS buffers: in iteration s the wave
@@ -507,26 +504,35 @@ hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, 
   a.win_start = g.win_start;
   const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(512);
   const bool ones = 8 * a.nvec < 16 * a.nj;  // a spare padded column exists
-#define BRS_PREFILL_LAUNCH(DP, ONES)                                                   \
-  if (ev0)                                                                             \
-    hipExtLaunchKernelGGL((attn_prefill_kernel<DP, ONES>), grid, block, 0, s, ev0, ev1, 0, a); \
-  else                                                                                 \
-    hipLaunchKernelGGL((attn_prefill_kernel<DP, ONES>), grid, block, 0, s, a);
+#define BRS_PREFILL_LAUNCH(DP, NJ, ONES)                                                      \
+  if (a.nj == NJ && ones == ONES) {                                                          \
+    if (ev0)                                                                                  \
+      hipExtLaunchKernelGGL((attn_prefill_kernel<DP, NJ, ONES>), grid, block, 0, s, ev0, ev1, 0, a); \
+    else                                                                                      \
+      hipLaunchKernelGGL((attn_prefill_kernel<DP, NJ, ONES>), grid, block, 0, s, a);          \
+    return hipGetLastError();                                                                 \
+  }
   if (g.d <= 64) {
-    if (ones) {
-      BRS_PREFILL_LAUNCH(64, true)
-    } else {
-      BRS_PREFILL_LAUNCH(64, false)
-    }
+    BRS_PREFILL_LAUNCH(64, 1, true)
+    BRS_PREFILL_LAUNCH(64, 1, false)
+    BRS_PREFILL_LAUNCH(64, 2, true)
+    BRS_PREFILL_LAUNCH(64, 2, false)
+    BRS_PREFILL_LAUNCH(64, 3, true)
+    BRS_PREFILL_LAUNCH(64, 3, false)
+    BRS_PREFILL_LAUNCH(64, 4, true)
+    BRS_PREFILL_LAUNCH(64, 4, false)
   } else {
-    if (ones) {
-      BRS_PREFILL_LAUNCH(128, true)
-    } else {
-      BRS_PREFILL_LAUNCH(128, false)
-    }
+    BRS_PREFILL_LAUNCH(128, 5, true)
+    BRS_PREFILL_LAUNCH(128, 5, false)
+    BRS_PREFILL_LAUNCH(128, 6, true)
+    BRS_PREFILL_LAUNCH(128, 6, false)
+    BRS_PREFILL_LAUNCH(128, 7, true)
+    BRS_PREFILL_LAUNCH(128, 7, false)
+    BRS_PREFILL_LAUNCH(128, 8, true)
+    BRS_PREFILL_LAUNCH(128, 8, false)
   }
 #undef BRS_PREFILL_LAUNCH
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace brs
