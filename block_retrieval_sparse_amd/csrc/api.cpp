@@ -226,13 +226,13 @@ int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_
   return ok();
 }
 
-// plan (unless already enqueued), then the attention kernels
+// plan (unless the split kernels build it themselves), then the attention kernels
 static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void* q, const int32_t* idx,
-                         bool planned, float* out, void* workspace, hipStream_t s) {
+                         float* out, void* workspace, hipStream_t s) {
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   hipError_t e;
-  if (!planned) {
+  if (!g.local_plan) {
     e = brs::launch_attn_plan(g, idx, workspace, out, s);
     if (e != hipSuccess) return hip_fail(e, "attn_plan");
   }
@@ -241,7 +241,7 @@ static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void
     if (e != hipSuccess) return hip_fail(e, "attn_prefill");
     return ok();
   }
-  e = brs::launch_attn_split(g, m->k, m->v, q, workspace, out, s, e0, e1);
+  e = brs::launch_attn_split(g, m->k, m->v, q, idx, workspace, out, s, e0, e1);
   if (e != hipSuccess) return hip_fail(e, "attn_split");
   e = brs::launch_attn_merge(g, workspace, out, s);
   if (e != hipSuccess) return hip_fail(e, "attn_merge");
@@ -269,7 +269,7 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
   if (rc) return rc;
   rc = check_attention_buffers(g, q, idx, k, out, workspace, workspace_bytes);
   if (rc) return rc;
-  return run_attention(g, m, q, idx, false, out, workspace, (hipStream_t)stream);
+  return run_attention(g, m, q, idx, out, workspace, (hipStream_t)stream);
 }
 
 int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const void* qrep,
@@ -295,7 +295,6 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  bool planned = false;
   if (k > 0) {
     if (hi > lo) {
       e = cosine ? brs::launch_score_cosine(*m, qrep, lo, hi, scores, s)
@@ -303,16 +302,10 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
       if (e != hipSuccess) return hip_fail(e, "score_blocks");
     }
     const int64_t stride = m->capacity / m->block_size;
-    if (brs::select_plan_supported(g, hi - lo)) {
-      e = brs::launch_select_plan(g, scores, stride, lo, hi, idx, vals, workspace, out, s);
-      if (e != hipSuccess) return hip_fail(e, "select_plan");
-      planned = true;
-    } else {
-      e = brs::launch_select_topk(scores, m->batch, hs, stride, lo, hi, k, idx, vals, s);
-      if (e != hipSuccess) return hip_fail(e, "select_topk");
-    }
+    e = brs::launch_select_topk(scores, m->batch, hs, stride, lo, hi, k, idx, vals, s);
+    if (e != hipSuccess) return hip_fail(e, "select_topk");
   }
-  return run_attention(g, m, q, k > 0 ? idx : nullptr, planned, out, workspace, s);
+  return run_attention(g, m, q, k > 0 ? idx : nullptr, out, workspace, s);
 }
 
 int brs_profile_next_attention(void* start_event, void* stop_event) {

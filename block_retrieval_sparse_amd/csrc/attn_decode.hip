@@ -24,7 +24,7 @@
 #include <math.h>
 #include <stdlib.h>
 
-#include "brs_wave_topk.h"
+#include "brs_internal.h"
 
 namespace brs {
 namespace {
@@ -188,137 +188,6 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// select + plan in one kernel (per-head selections, up to 16 heads per kv
-// head): one workgroup per (batch, kv head); thread group j (64 to 256
-// threads) selects the top-k blocks of query head g G + j (writing idx /
-// vals) into LDS, then the workgroup builds the plan from those selections
-// exactly as attn_plan_kernel does from idx, with the chunk-first table kept
-// in LDS.
-
-constexpr int kFusedHeads = 16;   // query heads per kv head
-constexpr int kFusedK = 256;      // largest k
-constexpr int kFirstLds = 1024;   // largest chunk count per (batch, kv head)
-
-struct SelectPlanArgs {
-  PlanArgs p;
-  const float* scores;  // [batch][hq][stride]
-  float* vals;          // [batch][hq][k] or null
-  int64_t stride;
-  int lo, hi;
-};
-
-template <int KPT>
-__global__ __launch_bounds__(1024) void select_plan_kernel(SelectPlanArgs sa) {
-  const PlanArgs& a = sa.p;
-  // selection state (per row) and block marks share one buffer
-  constexpr int kSelBytes = kFusedHeads * (int)(sizeof(TopkRowShared) + kFusedK * 8);
-  constexpr int kScratch = kSelBytes > kMarkBlocks * 4 ? kSelBytes : kMarkBlocks * 4;
-  __shared__ __align__(16) unsigned char scratch[kScratch];
-  __shared__ int32_t lsel[kFusedHeads][kFusedK];
-  __shared__ int first[kFirstLds];
-  __shared__ int wave_tot[16];
-  __shared__ int sh_items, sh_tokens, sh_flag;
-  const int bg = blockIdx.x;
-  const int b = bg / a.hkv, g = bg - b * a.hkv;
-  const int tid = threadIdx.x, nt = blockDim.x;
-
-  // row group j = tid / tpr selects the top-k of query head g G + j
-  const int tpr = nt / a.G;
-  TopkRowShared* shs = reinterpret_cast<TopkRowShared*>(scratch);
-  uint64_t* sels = reinterpret_cast<uint64_t*>(scratch + kFusedHeads * sizeof(TopkRowShared));
-  for (int i = tid; i < a.G * 256; i += nt) shs[i / 256].hist[i % 256] = 0u;
-  if (tid < a.G) shs[tid].cnt = 0;
-  if (tid == 0) sh_flag = 0;
-  __syncthreads();
-  {
-    const int j = tid / tpr;
-    const int64_t row = (int64_t)b * a.hq + g * a.G + j;
-    group_topk<KPT>(sa.scores + row * sa.stride, sa.lo, sa.hi, a.k, tpr, shs[j], &sh_flag, sels + j * kFusedK,
-                    const_cast<int32_t*>(a.idx) + row * a.k, sa.vals ? sa.vals + row * a.k : nullptr, lsel[j]);
-  }
-  __syncthreads();
-
-  uint32_t* marks = reinterpret_cast<uint32_t*>(scratch);
-  int4* items = a.items + (int64_t)bg * a.max_items;
-  const int CH = a.chunk_tokens;
-  const uint32_t full = a.G >= 32 ? 0xffffffffu : ((1u << a.G) - 1u);
-  const int S = a.sink_end, Wn = a.N - a.win_start;
-  if (tid == 0) {
-    int i = 0;
-    if (S > 0) {
-      items[i] = make_int4(0, S, (int)full, 0);
-      mark_chunks(first, i, 0, S, CH);
-      ++i;
-    }
-    if (Wn > 0) {
-      items[i] = make_int4(a.win_start, Wn, (int)full, S);
-      mark_chunks(first, i, S, Wn, CH);
-    }
-  }
-  int n_items = (S > 0) + (Wn > 0), n_tokens = S + Wn;
-  const int E = a.G * a.k;
-  for (int base = 0; base < a.nb; base += kMarkBlocks) {
-    const int top = min(a.nb, base + kMarkBlocks);
-    for (int i = tid; i < top - base; i += nt) marks[i] = 0u;
-    __syncthreads();
-    for (int e = tid; e < E; e += nt) {
-      const int j = e / a.k;
-      const int blk = lsel[j][e - j * a.k];
-      if (blk >= base && blk < top) {
-        const int lo_t = max(blk * a.B, S);
-        const int hi_t = min((blk + 1) * a.B, a.win_start);
-        if (lo_t < hi_t) atomicOr(&marks[blk - base], 1u << j);
-      }
-    }
-    __syncthreads();
-    const int per = (top - base + nt - 1) / nt;
-    const int r0 = base + tid * per, r1 = min(top, r0 + per);
-    int ci = 0, ct = 0;
-    for (int blk = r0; blk < r1; ++blk) {
-      if (marks[blk - base]) {
-        ++ci;
-        ct += min((blk + 1) * a.B, a.win_start) - max(blk * a.B, S);
-      }
-    }
-    const int inc_i = block_inclusive_scan(ci, wave_tot);
-    const int inc_t = block_inclusive_scan(ct, wave_tot);
-    int oi = n_items + inc_i - ci, ot = n_tokens + inc_t - ct;
-    for (int blk = r0; blk < r1; ++blk) {
-      const uint32_t mk = marks[blk - base];
-      if (!mk) continue;
-      const int lo_t = max(blk * a.B, S);
-      const int len = min((blk + 1) * a.B, a.win_start) - lo_t;
-      items[oi] = make_int4(lo_t, len, (int)mk, ot);
-      mark_chunks(first, oi, ot, len, CH);
-      ++oi;
-      ot += len;
-    }
-    if (tid == nt - 1) {
-      sh_items = inc_i;
-      sh_tokens = inc_t;
-    }
-    __syncthreads();
-    n_items += sh_items;
-    n_tokens += sh_tokens;
-    __syncthreads();
-  }
-  if (tid == 0) a.hdr[bg] = make_int4(n_items, n_tokens, 0, 0);
-  const int n_chunks = (n_tokens + CH - 1) / CH;
-  int4* chunks = a.chunks + (int64_t)bg * a.max_chunks;
-  for (int c = tid; c < a.max_chunks; c += nt) {
-    if (c < n_chunks)
-      chunks[c] = make_int4(first[c], c + 1 < n_chunks ? first[c + 1] + 1 : n_items, min((c + 1) * CH, n_tokens), 0);
-    else
-      chunks[c] = make_int4(0, 0, 0, 0);
-  }
-  if (n_tokens == 0) {
-    const int rows = a.G * a.n_q;
-    float* o = a.out + (((int64_t)b * a.hq + g * a.G) * a.n_q) * a.d;
-    for (int i = tid; i < rows * a.d; i += nt) o[i] = 0.f;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // split
 
 struct SplitArgs {
@@ -338,6 +207,12 @@ struct SplitArgs {
   float qscale;
   int chunk_tokens, wave_tokens, nw;
   int rows, rows_per_group, row_groups;
+  // in-kernel plan (when `local`): the selections and the set's geometry
+  int local;
+  const int32_t* idx;
+  int kk, idx_heads, B, nb, sink_end, win_start;  // kk: selections per row
+  int4* hdr_out;  // (segments, tokens) per (batch, kv head), for the merge
+  float* out;     // zero rows when nothing is attended
 };
 
 template <typename T>
@@ -380,6 +255,136 @@ __device__ __forceinline__ int stage_items(const SplitArgs& a, int bg, const int
   for (int j = threadIdx.x; j < ns; j += blockDim.x) lds[j] = g[desc.x + j];
   __syncthreads();
   return ns;
+}
+
+// The segments of chunk c computed in the workgroup itself from the
+// selections (no plan kernel): per-head bitmaps of the selected blocks that
+// hold a token outside sinks and window, a prefix count of the union over
+// 32-block words, and the flattened offsets in closed form -- every
+// selected block has B tokens in the set except the first eligible block
+// (cut by the sinks) and the last (cut by the window), which are the first
+// and last of the union when selected.  Same segments, in the same order,
+// as the plan kernel: sinks, window, then blocks in block order.
+// Returns the number of segments staged in `lds`, or -1 when the chunk lies
+// past the end; *t_end is the chunk's last flattened token + 1.
+constexpr int kPlanWords = 1024;  // bitmap words in LDS: heads x ceil(nb / 32)
+
+struct ChunkPlanLds {
+  uint32_t bits[kPlanWords];
+  int misc[4];  // segments, chunk end token, (unused), (unused)
+};
+
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+__device__ int chunk_plan(const SplitArgs& a, int b, int g, int c, int rg, int4* lds, ChunkPlanLds& pl,
+                          int* t_end) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+  const int W = (a.nb + 31) >> 5;
+  const int hb = a.idx_heads == 1 ? 1 : a.G;  // bitmaps: one per head, or one shared
+  const int S = a.sink_end, ws = a.win_start, B = a.B;
+  for (int i = tid; i < hb * W; i += nt) pl.bits[i] = 0u;
+  __syncthreads();
+  const int E = hb * a.kk;
+  for (int e = tid; e < E; e += nt) {
+    const int j = e / a.kk;
+    const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + j;
+    const int blk = a.idx[row * a.kk + (e - j * a.kk)];
+    if (blk >= 0 && blk < a.nb && max(blk * B, S) < min((blk + 1) * B, ws))
+      atomicOr(&pl.bits[j * W + (blk >> 5)], 1u << (blk & 31));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // wave 0: the union's popcounts by word, their prefix (DPP scan, 64 words
+    // at a time), the set's size, then each lane expands its word's blocks
+    // that fall in this chunk into segments
+    auto word = [&](int w) -> uint32_t {
+      uint32_t u = 0u;
+      if (w < W)
+        for (int j = 0; j < hb; ++j) u |= pl.bits[j * W + w];
+      return u;
+    };
+    int n_sel = 0;
+    for (int w0 = 0; w0 < W; w0 += 64) n_sel += __builtin_amdgcn_readlane(wave_incl_scan_dpp(__popc(word(w0 + lane))), 63);
+    auto in_union = [&](int blk) -> bool {
+      if (blk < 0 || blk >= a.nb) return false;
+      return (word(blk >> 5) >> (blk & 31)) & 1u;
+    };
+    const int bs = S / B, bw = ws / B;
+    const int cut_s = (S % B != 0 && in_union(bs)) ? S - bs * B : 0;
+    const int cut_w = (ws % B != 0 && in_union(bw)) ? (bw + 1) * B - ws : 0;
+    const int Wn = a.N - ws;
+    const int n_tokens = S + Wn + n_sel * B - cut_s - cut_w;
+    const int t0 = c * a.chunk_tokens;
+    if (c == 0 && rg == 0 && lane == 0)
+      a.hdr_out[(int64_t)b * a.hkv + g] = make_int4((S > 0) + (Wn > 0) + n_sel, n_tokens, 0, 0);
+    int ns = -1, t1 = 0;
+    if (n_tokens > 0 && t0 < n_tokens) {
+      t1 = min(t0 + a.chunk_tokens, n_tokens);
+      const uint32_t full = a.G >= 32 ? 0xffffffffu : ((1u << a.G) - 1u);
+      int nhead = 0;
+      if (S > 0 && t0 < S) nhead++;
+      if (Wn > 0 && t0 < S + Wn && t1 > S) nhead++;
+      if (lane == 0) {
+        int i = 0;
+        if (S > 0 && t0 < S) lds[i++] = make_int4(0, S, (int)full, 0);
+        if (Wn > 0 && t0 < S + Wn && t1 > S) lds[i++] = make_int4(ws, Wn, (int)full, S);
+      }
+      // ranks [r0, r1) overlap the chunk: offset of rank r = base + r B - (r > 0 ? cut_s : 0)
+      const int base = S + Wn;
+      int r0 = 0;
+      if (t0 > base) r0 = (t0 - base + cut_s) / B;
+      int r1 = n_sel;
+      if (t1 - base < n_sel * B) {
+        const int num = t1 - base + cut_s + B - 1;
+        r1 = num > 0 ? num / B : 0;
+        r1 = min(r1, n_sel);
+      }
+      int before = 0;  // selected blocks in earlier word groups
+      for (int w0 = 0; w0 < W; w0 += 64) {
+        const int w = w0 + lane;
+        uint32_t u = word(w);
+        const int cnt = __popc(u);
+        const int incl = wave_incl_scan_dpp(cnt);
+        int r = before + incl - cnt;
+        while (u) {
+          const int bit = __builtin_ctz(u);
+          u &= u - 1u;
+          if (r >= r0 && r < r1) {
+            const int blk = w * 32 + bit;
+            uint32_t mk = full;
+            if (hb > 1) {
+              mk = 0u;
+              for (int j = 0; j < hb; ++j) mk |= ((pl.bits[j * W + w] >> bit) & 1u) << j;
+            }
+            const int pos = max(blk * B, S);
+            lds[nhead + (r - r0)] = make_int4(pos, min((blk + 1) * B, ws) - pos, (int)mk, base + r * B - (r > 0 ? cut_s : 0));
+          }
+          ++r;
+        }
+        before += __builtin_amdgcn_readlane(incl, 63);
+      }
+      ns = nhead + (r1 > r0 ? r1 - r0 : 0);
+    } else if (n_tokens == 0 && c == 0 && rg == 0) {
+      // nothing attended: this (batch, kv head)'s rows are zeros (written once)
+      float* o = a.out + (((int64_t)b * a.hq + g * a.G) * a.n_q) * a.d;
+      for (int i = lane; i < a.G * a.n_q * a.d; i += 64) o[i] = 0.f;
+    }
+    if (lane == 0) {
+      pl.misc[0] = ns;
+      pl.misc[1] = t1;
+    }
+  }
+  __syncthreads();
+  *t_end = pl.misc[1];
+  return pl.misc[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -516,6 +521,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_kernel(SplitArgs a) {
   static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "lanes per token");
   static_assert(NU >= 1 && NU * E16 == DPL, "16-byte units");
   __shared__ int4 s_items[kItemsLds];
+  __shared__ ChunkPlanLds s_plan;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / L, sub = lane % L;
@@ -545,9 +551,16 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_kernel(SplitArgs a) {
     }
   }
 
-  const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
-  if (desc.x >= desc.y) return;  // past the end of this (batch, kv head)'s tokens
-  const int ns = stage_items(a, bg, desc, s_items);
+  int ns, t_end;
+  if (a.local) {
+    ns = chunk_plan(a, b, g, c, rg, s_items, s_plan, &t_end);
+    if (ns < 0) return;  // past the end of this (batch, kv head)'s tokens
+  } else {
+    const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
+    if (desc.x >= desc.y) return;
+    ns = stage_items(a, bg, desc, s_items);
+    t_end = desc.z;
+  }
   const int t0 = c * a.chunk_tokens;
 
   float m[ROWS], l[ROWS], o[ROWS][DPL];
@@ -565,7 +578,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_kernel(SplitArgs a) {
 
   // this wave's run of the flattened token list
   const int w0 = t0 + wave * a.wave_tokens;
-  const int w1 = min(w0 + a.wave_tokens, desc.z);
+  const int w1 = min(w0 + a.wave_tokens, t_end);
   int cur = 0;
   int4 it = s_items[0];
 
@@ -759,6 +772,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a
   constexpr int KC = D / 32;  // 32-wide k chunks of the head dim
   constexpr int NJ = D / 16;  // 16-wide output column tiles
   __shared__ int4 s_items[kItemsLds];
+  __shared__ ChunkPlanLds s_plan;
   // V tiles, rows padded by 32 bytes: the four rows one transposed read
   // gathers then fall on disjoint banks.  Reused to combine the waves.
   constexpr int VS = D + 16;
@@ -786,12 +800,19 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a
       qb[kk] = act ? *reinterpret_cast<const uint4*>(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
   }
 
-  const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
-  if (desc.x >= desc.y) return;
-  const int ns = stage_items(a, bg, desc, s_items);
+  int ns, t_end;
+  if (a.local) {
+    ns = chunk_plan(a, b, g, c, rg, s_items, s_plan, &t_end);
+    if (ns < 0) return;
+  } else {
+    const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
+    if (desc.x >= desc.y) return;
+    ns = stage_items(a, bg, desc, s_items);
+    t_end = desc.z;
+  }
   const int t0 = c * a.chunk_tokens;
   const int w0 = t0 + wave * a.wave_tokens;
-  const int w1 = min(w0 + a.wave_tokens, desc.z);
+  const int w1 = min(w0 + a.wave_tokens, t_end);
 
   const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bg * a.head_stride + 8 * g4;
   const uint16_t* vb = (const uint16_t*)a.v + (int64_t)bg * a.head_stride + 8 * g4;
@@ -956,16 +977,23 @@ template <typename T>
 __global__ __launch_bounds__(64) void attn_split_generic_kernel(SplitArgs a) {
   constexpr int NE = 8;  // dims per lane, head_dim <= 512
   __shared__ int4 s_items[kItemsLds];
+  __shared__ ChunkPlanLds s_plan;
   const int lane = threadIdx.x;
   const int c = blockIdx.x, bg = blockIdx.y, rg = blockIdx.z;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
-  const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
-  if (desc.x >= desc.y) return;  // past the end of this (batch, kv head)'s tokens
+  int ns, t1;
+  if (a.local) {
+    ns = chunk_plan(a, b, g, c, rg, s_items, s_plan, &t1);
+    if (ns < 0) return;  // past the end of this (batch, kv head)'s tokens
+  } else {
+    const int4 desc = a.chunks[(int64_t)bg * a.max_chunks + c];
+    if (desc.x >= desc.y) return;
+    ns = stage_items(a, bg, desc, s_items);
+    t1 = desc.z;
+  }
   const int t0 = c * a.chunk_tokens;
-  const int t1 = desc.z;
   const int rows_here = min(a.rows_per_group, a.rows - rg * a.rows_per_group);
   const int D = a.d;
-  const int ns = stage_items(a, bg, desc, s_items);
 
   float qf[kRowsMax][NE], m[kRowsMax], l[kRowsMax], o[kRowsMax][NE];
   uint32_t rowbit[kRowsMax];
@@ -1161,6 +1189,11 @@ bool attn_geometry(AttnGeom& g) {
   g.ml_off = g.chunks_off + up((size_t)bg * g.max_chunks * sizeof(int4));
   // the prefill kernel needs only the plan; the split path also keeps partials
   g.prefill = prefill_supported(g);
+  {
+    const int64_t W = ((int64_t)g.nb + 31) / 32;
+    const int64_t hb = g.idx_heads == 1 ? 1 : g.group;
+    g.local_plan = !g.prefill && hb * W <= kPlanWords && env_int("BRS_LOCAL_PLAN", 1) != 0;
+  }
   const size_t parts = g.prefill ? 0 : rows_total * g.max_chunks;
   g.o_off = g.ml_off + up(parts * sizeof(float2));
   g.total = g.o_off + up(parts * (size_t)g.d * sizeof(float));
@@ -1195,64 +1228,8 @@ hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, flo
   return hipGetLastError();
 }
 
-bool select_plan_supported(const AttnGeom& g, int64_t n) {
-  return g.idx_heads == g.hq && g.group <= kFusedHeads && g.k >= 1 && g.k <= kFusedK && n >= 1 && n <= 64 * 32 &&
-         g.max_chunks <= kFirstLds && env_int("BRS_FUSED_SELECT", 1) != 0;
-}
-
-hipError_t launch_select_plan(const AttnGeom& g, const float* scores, int64_t stride, int64_t lo, int64_t hi,
-                              int32_t* idx, float* vals, void* ws, float* out, hipStream_t s) {
-  SelectPlanArgs sa;
-  PlanArgs& a = sa.p;
-  a.idx = idx;
-  a.hdr = (int4*)((char*)ws + g.hdr_off);
-  a.items = (int4*)((char*)ws + g.items_off);
-  a.chunk_first = (int*)((char*)ws + g.first_off);
-  a.chunks = (int4*)((char*)ws + g.chunks_off);
-  a.out = out;
-  a.max_items = g.max_items;
-  a.max_chunks = g.max_chunks;
-  a.hq = g.hq;
-  a.hkv = g.hkv;
-  a.G = g.group;
-  a.k = g.k;
-  a.idx_heads = g.idx_heads;
-  a.n_q = g.n_q;
-  a.d = g.d;
-  a.row_groups = g.row_groups;
-  a.N = g.N;
-  a.B = g.B;
-  a.nb = g.nb;
-  a.sink_end = g.sink_end;
-  a.win_start = g.win_start;
-  a.chunk_tokens = g.chunk_tokens;
-  sa.scores = scores;
-  sa.vals = vals;
-  sa.stride = stride;
-  sa.lo = (int)lo;
-  sa.hi = (int)hi;
-  const int64_t n = hi - lo;
-  int tpr = 256;
-  while (tpr * g.group > 1024) tpr >>= 1;  // 64 threads per row at 16 heads
-  const dim3 grid((unsigned)(g.batch * g.hkv)), block((unsigned)(tpr * g.group));
-  const int64_t kpt = (n + tpr - 1) / tpr;
-  if (kpt <= 1)
-    hipLaunchKernelGGL(select_plan_kernel<1>, grid, block, 0, s, sa);
-  else if (kpt <= 2)
-    hipLaunchKernelGGL(select_plan_kernel<2>, grid, block, 0, s, sa);
-  else if (kpt <= 4)
-    hipLaunchKernelGGL(select_plan_kernel<4>, grid, block, 0, s, sa);
-  else if (kpt <= 8)
-    hipLaunchKernelGGL(select_plan_kernel<8>, grid, block, 0, s, sa);
-  else if (kpt <= 16)
-    hipLaunchKernelGGL(select_plan_kernel<16>, grid, block, 0, s, sa);
-  else
-    hipLaunchKernelGGL(select_plan_kernel<32>, grid, block, 0, s, sa);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws, float* out,
-                             hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
+                             void* ws, float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   SplitArgs a;
   a.k = k;
   a.v = v;
@@ -1279,18 +1256,34 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   a.rows = g.group * g.n_q;
   a.rows_per_group = g.rows_per_group;
   a.row_groups = g.row_groups;
+  a.local = g.local_plan ? 1 : 0;
+  a.idx = idx;
+  a.kk = idx ? g.k : 0;
+  a.idx_heads = g.idx_heads;
+  a.B = g.B;
+  a.nb = g.nb;
+  a.sink_end = g.sink_end;
+  a.win_start = g.win_start;
+  a.hdr_out = (int4*)((char*)ws + g.hdr_off);
+  a.out = out;
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
   if (g.mfma) {
     const dim3 block(64 * g.nw);
+  // LDS sized for the waves actually launched: a smaller footprint lets
+  // several workgroups share a CU
 #define BRS_LAUNCH_MFMA(DD, NWM)                                                                            \
-  if (g.d == DD) {                                                                                          \
+  if (g.d == DD && g.nw <= NWM) {                                                                           \
     if (ev0)                                                                                                \
       hipExtLaunchKernelGGL((attn_split_mfma_kernel<DD, NWM>), grid, block, 0, s, ev0, ev1, 0, a);         \
     else                                                                                                    \
       hipLaunchKernelGGL((attn_split_mfma_kernel<DD, NWM>), grid, block, 0, s, a);                         \
     return hipGetLastError();                                                                               \
   }
+    BRS_LAUNCH_MFMA(64, 2)
+    BRS_LAUNCH_MFMA(64, 4)
     BRS_LAUNCH_MFMA(64, 8)
+    BRS_LAUNCH_MFMA(128, 2)
+    BRS_LAUNCH_MFMA(128, 4)
     BRS_LAUNCH_MFMA(128, 8)
 #undef BRS_LAUNCH_MFMA
     return hipErrorInvalidValue;

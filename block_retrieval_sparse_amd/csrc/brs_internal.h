@@ -80,6 +80,7 @@ struct AttnGeom {
   bool fast;              // head_dim and row layout served by the vector kernel
   bool mfma;              // bfloat16 served by the matrix-core kernel
   bool prefill;           // chunk of queries served by the matrix-core prefill kernel
+  bool local_plan;        // split workgroups build their segments from idx (no plan kernel)
   int64_t max_items;      // segments per (batch, kv head)
   int64_t max_tokens;     // bound on attended tokens per (batch, kv head)
   int nw;                 // waves per split workgroup
@@ -96,13 +97,9 @@ struct AttnGeom {
 bool attn_geometry(AttnGeom& g);
 
 hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, float* out, hipStream_t s);
-// Top-k of scores columns [lo, hi) for every query head plus the plan, in one
-// kernel (per-head selections only; n = hi - lo candidates).
-bool select_plan_supported(const AttnGeom& g, int64_t n);
-hipError_t launch_select_plan(const AttnGeom& g, const float* scores, int64_t stride, int64_t lo, int64_t hi,
-                              int32_t* idx, float* vals, void* ws, float* out, hipStream_t s);
-hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
-                             float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
+                             void* ws, float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);
 // Chunked prefill on the matrix cores (reads the plan's segments from ws).
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,

@@ -217,7 +217,7 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
  * call, with the candidate range of brs_eligible_range(n_sink, window):
  * identical results to the three calls made in turn, and the same
  * selection semantics (per query head for dot scores, per sequence for
- * cosine).  Selection and attention planning may run as one kernel.
+ * cosine).
  *   q, out    : as brs_retrieval_attention (idx_heads = n_q_heads for dot
  *               scores, 1 for cosine);
  *   qrep      : as brs_score_blocks (unused when k = 0);

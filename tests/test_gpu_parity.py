@@ -223,7 +223,7 @@ def test_full_size_memlong_prefill_sampled():
 
 @pytest.mark.parametrize("name", ["infllm", "gqa8", "landmark", "retrieval", "memlong", "multi_q", "prefill_gqa"])
 def test_step_call_matches_separate_calls(name):
-    """brs_retrieval_step (selection and plan fused where supported) gives the
+    """brs_retrieval_step (one call; the split kernels plan in-kernel) gives the
     same scores, selection and attention bits as the three separate calls."""
     from block_retrieval_sparse_amd.pipeline import RetrievalStep
 
