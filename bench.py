@@ -62,13 +62,14 @@ class HipEvents:
 
 
 KERNEL_SOURCES = {
-    "attn_split": ("block_retrieval_sparse_amd/csrc/attn_decode.hip", "block_retrieval_sparse_amd/csrc/brs_internal.h"),
+    "attn_step": ("block_retrieval_sparse_amd/csrc/attn_decode.hip", "block_retrieval_sparse_amd/csrc/brs_internal.h",
+                  "block_retrieval_sparse_amd/csrc/brs_wave_topk.h"),
     "attn_prefill": ("block_retrieval_sparse_amd/csrc/attn_prefill.hip",
                      "block_retrieval_sparse_amd/csrc/brs_internal.h"),
 }
 
 
-def sources_sha256(paths=KERNEL_SOURCES["attn_split"]) -> str:
+def sources_sha256(paths=KERNEL_SOURCES["attn_step"]) -> str:
     import hashlib
 
     h = hashlib.sha256()
@@ -78,7 +79,7 @@ def sources_sha256(paths=KERNEL_SOURCES["attn_split"]) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str = "attn_split"):
+def measured_traffic(workload: str, kernel: str = "attn_step"):
     """HBM bytes per launch of the main attention kernel from the committed
     counter summary for this workload, or None when there is none or the
     kernel's sources have changed since the counters were taken."""
@@ -383,7 +384,7 @@ def run(args):
         })
     else:
         achieved = split_bytes / (kern_avg * 1e-3) / 1e9
-        res["roofline"] = {"bound": "hbm", "kernel": "attn_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        res["roofline"] = {"bound": "hbm", "kernel": "attn_step", "achieved": achieved, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                            "bytes_per_launch": split_bytes, "avg_launch_us": kern_avg * 1e3}
     res.update({

@@ -232,7 +232,7 @@ static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   hipError_t e;
-  if (!g.local_plan) {
+  if (!g.local_plan && !g.slot) {
     e = brs::launch_attn_plan(g, idx, workspace, out, s);
     if (e != hipSuccess) return hip_fail(e, "attn_plan");
   }
@@ -302,6 +302,16 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
       if (e != hipSuccess) return hip_fail(e, "score_blocks");
     }
     const int64_t stride = m->capacity / m->block_size;
+    if (brs::step_supported(g, lo, hi, k)) {
+      // selection and attention in one launch, then the merge
+      hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
+      g_prof_start = g_prof_stop = nullptr;
+      e = brs::launch_attn_step(g, m->k, m->v, q, scores, stride, lo, hi, idx, vals, workspace, out, s, e0, e1);
+      if (e != hipSuccess) return hip_fail(e, "select_topk + attention");
+      e = brs::launch_attn_merge(g, workspace, out, s);
+      if (e != hipSuccess) return hip_fail(e, "attn_merge");
+      return ok();
+    }
     e = brs::launch_select_topk(scores, m->batch, hs, stride, lo, hi, k, idx, vals, s);
     if (e != hipSuccess) return hip_fail(e, "select_topk");
   }

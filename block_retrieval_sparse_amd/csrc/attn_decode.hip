@@ -25,6 +25,7 @@
 #include <stdlib.h>
 
 #include "brs_internal.h"
+#include "brs_wave_topk.h"
 
 namespace brs {
 namespace {
@@ -213,6 +214,17 @@ struct SplitArgs {
   int kk, idx_heads, B, nb, sink_end, win_start;  // kk: selections per row
   int4* hdr_out;  // (segments, tokens) per (batch, kv head), for the merge
   float* out;     // zero rows when nothing is attended
+  // slot layout: padded sinks (tokens), slot stride, sink/window and slot
+  // tokens, selection entries per kv slice
+  int slot_ps, slot_bs, len_a, len_b, n_ent;
+  int slice_bytes;  // bytes of one (batch, kv head) slice of k / v
+  // in-kernel selection: the score rows and where the selection goes
+  const float* scores;
+  int64_t score_stride;
+  int sel_lo, sel_hi;
+  int32_t* idx_out;
+  float* vals_out;
+  int n_units, per_xcd, xcd_map;  // one-dimensional grid of units
 };
 
 template <typename T>
@@ -396,16 +408,22 @@ __device__ int chunk_plan(const SplitArgs& a, int b, int g, int c, int rg, int4*
 
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict__ hdr, const float2* __restrict__ ml,
                                                         const float* __restrict__ o, float* __restrict__ out, int hq,
-                                                        int hkv, int n_q, int d, int chunk_tokens, int max_chunks) {
+                                                        int hkv, int n_q, int d, int chunk_tokens, int max_chunks,
+                                                        int used_chunks) {
   __shared__ float4 s_acc[256];
   __shared__ float2 s_ml[256];
   const int64_t row = blockIdx.x;  // ((b * hq + h) * n_q + i)
   const int64_t bh = row / n_q;
   const int b = (int)(bh / hq), h = (int)(bh - (int64_t)b * hq);
   const int bg = b * hkv + h / (hq / hkv);
-  const int n_tokens = hdr[bg].y;
-  if (n_tokens == 0) return;  // the plan kernel wrote zeros
-  const int n_chunks = min((n_tokens + chunk_tokens - 1) / chunk_tokens, max_chunks);
+  // chunk_tokens = 0: the first used_chunks chunks hold partials (slot
+  // layout); else the plan's token count says how many do
+  int n_chunks = used_chunks;
+  if (chunk_tokens > 0) {
+    const int n_tokens = hdr[bg].y;
+    if (n_tokens == 0) return;  // the plan kernel wrote zeros
+    n_chunks = min((n_tokens + chunk_tokens - 1) / chunk_tokens, max_chunks);
+  }
   const float2* mlr = ml + row * max_chunks;
   const float* ob = o + row * max_chunks * (int64_t)d;
   if ((d & 3) == 0 && d / 4 <= (int)blockDim.x) {
@@ -888,14 +906,13 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int2 md = s_meta[wave][16 * sidx + 4 * g4 + i];
-        const bool pass = ((uint32_t)md.y & rowbit) && md.x <= plim;
+        const bool pass = (((uint32_t)md.y & rowbit) != 0u) & (md.x <= plim);  // no branch around the read
         sv[4 * sidx + i] = pass ? st[sidx][i] * qs : kNegInf;
       }
     float tm = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tm = fmaxf(tm, sv[i]);
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = xmax16_32(tm);
     if (__ballot(tm > mref + kLazy)) {
       const float nm = fmaxf(mref, tm);
       const float al = fast_exp2(mref - nm);
@@ -969,6 +986,415 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a
     a.o[pidx * D + e] = Os;
     if (e == 0) a.ml[pidx] = make_float2(M, Ls);
   }
+}
+
+// Slot layout (matrix cores, bfloat16): the token list of a kv slice is
+// fixed before any selection is read -- the sinks, the window (each padded to
+// whole 32-token tiles), then one slot of roundup(B, 32) tokens per
+// selection entry (head-major, rank order).  A slot tile is resolved from
+// the entries alone: the block it names is clipped against sinks and
+// window, dropped when an earlier entry names the same block (the union:
+// each token once per kv slice), and masked to every query head whose
+// selection holds it.  No plan kernel and no LDS bitmap.
+//
+// A unit (kv slice, row group, chunk) is one workgroup of eight waves, about
+// one per CU.  Waves 0-3 first obtain the selections -- read from idx, or
+// selected in the kernel itself (attn_step_kernel: wave w takes the top-k of
+// its kv slice's score row w) -- while waves 4-7 run the sink/window tiles,
+// which need none (the slice's waves 4-7 take them in turn: tiles gw, gw + W,
+// ...).  After one barrier every wave runs its equal share of slot tiles.
+// K and V come through buffer loads with one 32-bit offset per token;
+// invalid tokens get an offset past the slice and read zeros without
+// touching memory.
+constexpr int kXcdCount = 8;           // XCDs; consecutive workgroups go to consecutive XCDs
+constexpr int kSlotRegs = 8;           // selection entries per lane: at most 512 per kv slice
+constexpr int kSlotOOR = 0x7ffff000;   // buffer offset past any slice
+constexpr int kSlotFlags = 0x00020000; // raw buffer resource word 3 (32-bit data, no swizzle)
+constexpr int kSlotWaves = 8;          // waves per slot workgroup
+constexpr int kSelWaves = 4;           // waves 0-3 select (at most four score rows); 4-7 take the sink/window tiles
+constexpr int kStepK = 128;            // largest k selected inside the attention kernel
+constexpr int kStepCand = 256;         // candidates the fast selection ranks (else the radix select)
+constexpr int kWaitVm0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unconstrained
+
+// A pointer the compiler keeps in scalar registers (a buffer resource built
+// from a vector register would need a loop over its distinct values).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
+template <int D>
+struct SlotLds {
+  __align__(16) uint16_t v[kSlotWaves][32][D + 16];  // V rows padded by 32 bytes (conflict-free transposed reads)
+  float m[kSlotWaves][16], l[kSlotWaves][16];
+  int ents[64 * kSlotRegs];  // the kv slice's selection entries, head-major
+};
+
+// In-kernel selection: one score row per selection wave.
+struct StepLds {
+  TopkRowShared tk[kSelWaves];
+  uint64_t sel[kSelWaves][kStepCand];  // kStepCand >= kStepK: also the radix select's kept keys
+  uint32_t selv[kSelWaves][kStepCand];
+  int flag[kSelWaves];
+};
+
+template <int D, int KPTW, int DEPTH>  // KPTW > 0: select in the kernel, KPTW scores per lane;
+                                        // DEPTH tiles of loads in flight per wave
+__device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<D>& sm, StepLds* st) {
+  constexpr bool STEP = KPTW > 0;
+  constexpr int KC = D / 32;  // 32-wide k chunks of the head dim
+  constexpr int NJ = D / 16;  // 16-wide output column tiles
+  auto& s_v = sm.v;
+  auto& s_m = sm.m;
+  auto& s_l = sm.l;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = lane >> 4, n = lane & 15;
+  const int c = unit % a.max_chunks, rest = unit / a.max_chunks;
+  const int rg = rest % a.row_groups, bg = rest / a.row_groups;
+  const int b = bg / a.hkv, g = bg - b * a.hkv;
+  const int rows_here = min(a.rows_per_group, a.rows - rg * a.rows_per_group);
+
+  // query row n of this group as the B operand; lanes past the group's rows
+  // load row 0 again: their logits are masked (rowbit 0) and their output
+  // rows never written, so no zeroing (which would wait for the loads)
+  const bool act = n < rows_here;
+  const int gr = rg * a.rows_per_group + n;
+  const int jh = act ? gr / a.n_q : 0, qi = act ? gr - jh * a.n_q : 0;
+  const uint32_t rowbit = act ? (1u << jh) : 0u;
+  const int plim = a.N - a.n_q + qi;
+  uint4 qb[KC];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.hq + g * a.G + jh) * a.n_q + qi) * D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) qb[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+  }
+
+  // the wave's tiles: fa sink/window tiles (waves 4-7, strided over the
+  // slice's such waves), then its run of slot tiles
+  constexpr int kFixWaves = kSlotWaves - kSelWaves;
+  const bool fixw = wave >= kSelWaves;
+  const int tA = a.len_a >> 5, tB = a.len_b >> 5;
+  const int wf_all = a.max_chunks * kFixWaves, gwf = c * kFixWaves + (wave - kSelWaves);
+  const int fa = fixw && tA > gwf ? (tA - 1 - gwf) / wf_all + 1 : 0;
+  const int wt_all = a.max_chunks * kSlotWaves, gw = c * kSlotWaves + wave;
+  const int qB = (tB + wt_all - 1) / wt_all, b0 = gw * qB;
+  const int n_tiles = fa + max(0, min(b0 + qB, tB) - b0);
+
+  // selection entries of this (batch, kv head): entry e = lane + 64 r, head e / K
+  const int E = a.n_ent, K = a.kk;
+  const int nreg = (E + 63) >> 6;
+  const uint32_t full = a.G >= 32 ? 0xffffffffu : ((1u << a.G) - 1u);
+  int ent[kSlotRegs];
+  if constexpr (!STEP) {
+#pragma unroll
+    for (int r = 0; r < kSlotRegs; ++r) {
+      const int e = lane + 64 * r, ec = min(e, E - 1);
+      const int j = ec / K;
+      const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + j;
+      const int v = a.idx[row * K + (ec - j * K)];
+      ent[r] = e < E ? v : -2;
+    }
+  }
+
+  // the slot last resolved (wave-uniform): its block and head mask (0: skipped)
+  int c_slot = -1, c_blk = 0;
+  uint32_t c_mk = 0u;
+  auto resolve = [&](int s) {
+    c_slot = s;
+    c_mk = 0u;
+    c_blk = __builtin_amdgcn_readfirstlane(sm.ents[s]);
+    const int X = c_blk;
+    if (X < 0 || X >= a.nb || max(X * a.B, a.sink_end) >= min(X * a.B + a.B, a.win_start)) return;
+    // entries naming the same block: the first one attends it for all their heads
+    int first = 1 << 30, tot = 0;
+#pragma unroll
+    for (int rr = 0; rr < kSlotRegs; ++rr) {
+      if (rr < nreg) {
+        const uint64_t m = __ballot(ent[rr] == X);
+        tot += __popcll(m);
+        if (m && first == 1 << 30) first = 64 * rr + __builtin_ctzll(m);
+      }
+    }
+    if (first < s) return;
+    if (a.idx_heads == 1) {
+      c_mk = full;
+    } else if (tot == 1) {
+      c_mk = 1u << (s / K);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < kSlotRegs; ++rr) {
+        if (rr < nreg) {
+          uint64_t m = __ballot(ent[rr] == X);
+          while (m) {
+            c_mk |= 1u << ((64 * rr + __builtin_ctzll(m)) / K);
+            m &= m - 1ull;
+          }
+        }
+      }
+    }
+  };
+  // the wave's tile i (wave-uniform): first row, valid row range, head mask;
+  // slots = false leaves slot tiles empty (before the selections are known)
+  auto tile_info = [&](int i, int& pos0, int& vlo, int& vhi, uint32_t& mk, bool slots) {
+    pos0 = 0;
+    vlo = 0;
+    vhi = 0;
+    mk = 0u;
+    if (i >= n_tiles) return;
+    if (i < fa) {
+      const int tb = (gwf + i * wf_all) << 5;
+      if (tb < a.slot_ps) {
+        pos0 = tb;
+        vhi = a.sink_end;
+      } else {
+        pos0 = a.win_start + (tb - a.slot_ps);
+        vlo = a.win_start;
+        vhi = a.N;
+      }
+      mk = full;
+    } else {
+      if (!slots) return;
+      const int tb = (b0 + i - fa) << 5;
+      const int s = tb / a.slot_bs, off = tb - s * a.slot_bs;
+      if (s != c_slot) resolve(s);
+      if (c_mk == 0u) return;
+      const int X = c_blk;
+      vlo = max(X * a.B, a.sink_end);
+      vhi = min(X * a.B + a.B, a.win_start);
+      pos0 = X * a.B + off;
+      mk = c_mk;
+    }
+  };
+
+  const int rs2 = a.row_stride * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr((const uint16_t*)a.k + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kSlotFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr((const uint16_t*)a.v + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kSlotFlags);
+  const float qs = a.qscale;
+
+  f32x4_t o[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) o[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mref = kFarNeg, lpart = 0.f;
+
+  struct Tile {
+    uint4 k[2][KC], v[2][KC];
+    int pos0, vlo, vhi;  // first row, valid rows [vlo, vhi)
+    uint32_t mk;         // query heads that attend the tile
+  };
+  // loads are issued whatever the tile: invalid tokens read zeros
+  auto load = [&](Tile& tl, int i, bool slots) {
+    tile_info(i, tl.pos0, tl.vlo, tl.vhi, tl.mk, slots);
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      const int pos = tl.pos0 + 16 * sidx + n;
+      const bool val = (tl.mk != 0u) & (pos >= tl.vlo) & (pos < tl.vhi);
+      const int off = val ? pos * rs2 + 16 * g4 : kSlotOOR;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        tl.k[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        tl.v[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 64 * kk, 0, 0));
+    }
+  };
+
+  // one tile: V to LDS, S^T on the matrix cores, the loads of tile tn into
+  // the same registers, then softmax and O += P V
+  auto step = [&](Tile& tl, int tn, bool slots) {
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        *reinterpret_cast<uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]) = tl.v[sidx][kk];
+    f32x4_t st2[2];
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      st2[sidx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        st2[sidx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[sidx][kk]), as_bf16x8(qb[kk]), st2[sidx], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int p0 = tl.pos0, vlo = tl.vlo, vhi = tl.vhi;
+    const bool rowok = (tl.mk & rowbit) != 0u;
+    load(tl, tn, slots);
+    // logits of this lane: tokens 4*g4 + i (first half) and 16 + 4*g4 + i, query row n
+    float sv[8];
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = p0 + 16 * sidx + 4 * g4 + i;
+        const bool pass = rowok & (pos >= vlo) & (pos < vhi) & (pos <= plim);
+        sv[4 * sidx + i] = pass ? st2[sidx][i] * qs : kNegInf;
+      }
+    float tm = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, sv[i]);
+    tm = xmax16_32(tm);
+    if (__ballot(tm > mref + kLazy)) {
+      const float nm = fmaxf(mref, tm);
+      const float al = fast_exp2(mref - nm);
+      mref = nm;
+      lpart *= al;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(al, 4 * g4 + i);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) o[jj][i] *= ai;
+      }
+    }
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(sv[i] - mref);
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
+      const float h0 = __uint_as_float(ph[i] << 16), h1 = __uint_as_float(ph[i] & 0xffff0000u);
+      pl[i] = pack_bf16x2(pv[2 * i] - h0, pv[2 * i + 1] - h1);
+      lpart += pv[2 * i] + pv[2 * i + 1];
+    }
+    const bf16x8_t pa_hi = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8_t pa_lo = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int col = 16 * jj + 4 * (n & 3);
+      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&s_v[wave][4 * g4 + (n >> 2)][col]);
+      const i16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&s_v[wave][16 + 4 * g4 + (n >> 2)][col]);
+      const bf16x8_t vbv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vbv, o[jj], 0, 0, 0);
+      o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vbv, o[jj], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Phase 1: waves 4-7 run their sink/window tiles (the prefetch past the
+  // last one stays empty); waves 0-3 obtain the selections.  Phase 2, after
+  // the barrier: every wave runs its slot tiles.  (DEPTH: tiles of loads in
+  // flight per wave in phase 2.)
+  Tile ta, tb;
+  if (fixw && fa > 0) {
+    load(ta, 0, false);
+    for (int it = 0; it < fa; ++it) step(ta, it + 1, false);
+  }
+  if constexpr (STEP) {
+    // wave w selects score row w of the kv slice; its only loads are the
+    // scores, so waiting for them waits for nothing else
+    const int R = a.idx_heads == 1 ? 1 : a.G;
+    if (wave < R) {
+      const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + wave;
+      uint32_t raw[KPTW];
+      topk_load_raw<KPTW>(a.scores + row * a.score_stride, a.sel_lo, a.sel_hi, 64, raw);
+      const bool out = c == 0 && rg == 0;  // one workgroup per kv slice writes the selection
+      int32_t* gi = out ? a.idx_out + row * K : nullptr;
+      float* gv = out && a.vals_out ? a.vals_out + row * K : nullptr;
+      if (!wave_topk_filter<KPTW>(raw, a.sel_lo, a.sel_hi, K, kStepCand, st->sel[wave], st->selv[wave], gi, gv,
+                                  sm.ents + wave * K)) {
+        TopkRowShared& tk = st->tk[wave];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tk.hist[lane + 64 * j] = 0u;
+        if (lane == 0) {
+          tk.cnt = 0;
+          st->flag[wave] = 0;
+        }
+        wave_lds_sync();
+        group_topk_raw<KPTW, true>(raw, a.sel_lo, a.sel_hi, K, 64, tk, &st->flag[wave], st->sel[wave],
+                                   st->selv[wave], gi, gv, sm.ents + wave * K, nullptr);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSlotRegs; ++r) {
+      const int e = lane + 64 * r;
+      ent[r] = e < E ? sm.ents[min(e, E - 1)] : -2;
+    }
+  } else {
+    if (wave == 0) {
+#pragma unroll
+      for (int r = 0; r < kSlotRegs; ++r)
+        if (r < nreg) sm.ents[lane + 64 * r] = ent[r];
+    }
+    __syncthreads();
+  }
+  const int ns = n_tiles - fa;  // slot tiles of this wave
+  load(ta, fa, true);
+  if (DEPTH == 1) {
+    for (int it = 0; it < ns; ++it) step(ta, fa + it + 1, true);
+  } else {
+    load(tb, fa + 1, true);
+    for (int it = 0; it < (ns + 1) / 2; ++it) {
+      step(ta, fa + 2 * it + 2, true);
+      step(tb, fa + 2 * it + 3, true);
+    }
+  }
+
+  // row sums over the four lanes that share a query row
+  lpart += __shfl_xor(lpart, 16);
+  lpart += __shfl_xor(lpart, 32);
+
+  // combine the waves: O rows 4*g4 + i, columns 16*jj + n; V tiles' LDS reused
+  __syncthreads();
+  float* s_o = reinterpret_cast<float*>(&sm.v[0][0][0]);  // [8][16][D] floats fit in [8][32][D + 16] halves
+  if (lane < 16) {
+    s_m[wave][lane] = mref;
+    s_l[wave][lane] = lpart;
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[((int64_t)wave * 16 + 4 * g4 + i) * D + 16 * jj + n] = o[jj][i];
+  __syncthreads();
+  for (int t = threadIdx.x; t < rows_here * D; t += blockDim.x) {
+    const int r = t / D, e = t - r * D;
+    float M = kFarNeg;
+    for (int w = 0; w < kSlotWaves; ++w) M = fmaxf(M, s_m[w][r]);
+    float Ls = 0.f, Os = 0.f;
+    for (int w = 0; w < kSlotWaves; ++w) {
+      const float f = fast_exp2(s_m[w][r] - M);
+      Ls += s_l[w][r] * f;
+      Os += s_o[((int64_t)w * 16 + r) * D + e] * f;
+    }
+    const int64_t pidx = row_index(a, b, g, rg * a.rows_per_group + r) * a.max_chunks + c;
+    a.o[pidx * D + e] = Os;
+    if (e == 0) a.ml[pidx] = make_float2(M, Ls);
+  }
+}
+
+// units dealt to the XCDs in contiguous runs (workgroup w runs on XCD w % 8)
+__device__ __forceinline__ int slot_unit_index(const SplitArgs& a) {
+  const int xcd = blockIdx.x % kXcdCount, wslot = blockIdx.x / kXcdCount;
+  return a.xcd_map ? xcd * a.per_xcd + wslot : blockIdx.x;
+}
+
+// Attention over the slot layout with the selections read from idx.
+template <int D, int DEPTH>
+__global__ __launch_bounds__(64 * kSlotWaves) void attn_split_slot_kernel(SplitArgs a) {
+  __shared__ SlotLds<D> sm;
+  const int unit = slot_unit_index(a);
+  if (unit >= a.n_units) return;
+  slot_unit<D, 0, DEPTH>(a, unit, sm, nullptr);
+}
+
+// The whole decode step after scoring: the selection of every score row of
+// the kv slice (written out by the slice's first workgroup), then the same
+// attention as attn_split_slot_kernel -- identical partials.
+template <int D, int KPTW, int DEPTH>
+__global__ __launch_bounds__(64 * kSlotWaves) void attn_step_kernel(SplitArgs a) {
+  __shared__ SlotLds<D> sm;
+  __shared__ StepLds st;
+  const int unit = slot_unit_index(a);
+  if (unit >= a.n_units) return;
+  slot_unit<D, KPTW, DEPTH>(a, unit, sm, &st);
 }
 
 // Any head_dim <= 512 and any row stride: one token at a time per wave,
@@ -1154,6 +1580,19 @@ bool attn_geometry(AttnGeom& g) {
   const int64_t bg = (int64_t)g.batch * g.hkv;
   g.max_items = 2 + uniq;
   g.max_tokens = (int64_t)g.sink_end + (g.N - g.win_start) + uniq * g.B;
+  // the prefill kernel needs only the plan; the split path also keeps partials
+  g.prefill = prefill_supported(g);
+  // slot layout: every selection entry gets its own padded slot
+  g.slot = g.mfma && !g.prefill && E >= 1 && E <= 64 * kSlotRegs && E <= g.nb &&
+           g.head_stride * 2 < (int64_t)kSlotOOR - 4096 && env_int("BRS_SLOT", 1) != 0;
+  if (g.slot) {
+    auto pad32 = [](int64_t x) { return (x + 31) / 32 * 32; };
+    g.slot_ps = (int)pad32(g.sink_end);
+    g.slot_bs = (int)pad32(g.B);
+    g.len_a = g.slot_ps + (int)pad32(g.N - g.win_start);
+    g.len_b = (int)(E * g.slot_bs);
+    g.max_tokens = (int64_t)g.len_a + g.len_b;
+  }
   if (g.max_tokens > INT32_MAX) return false;
   // tokens per wave: about kTargetWaves waves over the whole problem, in whole steps
   const int64_t total = g.max_tokens * bg * g.row_groups;
@@ -1173,13 +1612,25 @@ bool attn_geometry(AttnGeom& g) {
   }
   // a chunk meets at most chunk_tokens / B + 6 segments (sinks, window, the two
   // blocks cut by them, whole blocks, one more at each end): keep them in LDS
-  const int64_t cap = (int64_t)(kItemsLds - 8) * g.B;
-  while ((int64_t)g.nw * g.wave_tokens > cap && g.wave_tokens > st) g.wave_tokens -= st;
-  while ((int64_t)g.nw * g.wave_tokens > cap && g.nw > 1) g.nw >>= 1;
-  if ((int64_t)g.nw * g.wave_tokens > cap) return false;
+  if (!g.slot) {
+    const int64_t cap = (int64_t)(kItemsLds - 8) * g.B;
+    while ((int64_t)g.nw * g.wave_tokens > cap && g.wave_tokens > st) g.wave_tokens -= st;
+    while ((int64_t)g.nw * g.wave_tokens > cap && g.nw > 1) g.nw >>= 1;
+    if ((int64_t)g.nw * g.wave_tokens > cap) return false;
+  }
   g.chunk_tokens = g.nw * g.wave_tokens;
   int64_t mc = (g.max_tokens + g.chunk_tokens - 1) / g.chunk_tokens;
   g.max_chunks = (int)(mc < 1 ? 1 : mc);
+  if (g.slot) {
+    // about one four-wave workgroup per CU, each wave with at least one tile
+    const int units = g.batch * g.hkv * g.row_groups;
+    const int tiles = (int)(g.max_tokens / 32);
+    int nc = env_int("BRS_SLOT_WGS", 256) / units;
+    nc = nc > tiles / kSlotWaves ? tiles / kSlotWaves : nc;
+    g.nw = kSlotWaves;
+    g.max_chunks = nc < 1 ? 1 : nc;
+    g.depth = env_int("BRS_DEPTH", 1) == 2 ? 2 : 1;
+  }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows_total = (size_t)g.batch * g.hq * g.n_q;
   g.hdr_off = 0;
@@ -1187,12 +1638,10 @@ bool attn_geometry(AttnGeom& g) {
   g.first_off = g.items_off + up((size_t)bg * g.max_items * sizeof(int4));
   g.chunks_off = g.first_off + up((size_t)bg * g.max_chunks * sizeof(int));
   g.ml_off = g.chunks_off + up((size_t)bg * g.max_chunks * sizeof(int4));
-  // the prefill kernel needs only the plan; the split path also keeps partials
-  g.prefill = prefill_supported(g);
   {
     const int64_t W = ((int64_t)g.nb + 31) / 32;
     const int64_t hb = g.idx_heads == 1 ? 1 : g.group;
-    g.local_plan = !g.prefill && hb * W <= kPlanWords && env_int("BRS_LOCAL_PLAN", 1) != 0;
+    g.local_plan = !g.prefill && !g.slot && hb * W <= kPlanWords && env_int("BRS_LOCAL_PLAN", 1) != 0;
   }
   const size_t parts = g.prefill ? 0 : rows_total * g.max_chunks;
   g.o_off = g.ml_off + up(parts * sizeof(float2));
@@ -1228,8 +1677,18 @@ hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, flo
   return hipGetLastError();
 }
 
-hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
-                             void* ws, float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+namespace {
+void slot_args(const AttnGeom& g, SplitArgs& a) {
+  a.slot_ps = g.slot_ps;
+  a.slot_bs = g.slot_bs;
+  a.len_a = g.len_a;
+  a.len_b = g.len_b;
+  a.n_ent = g.idx_heads == 1 ? g.k : g.group * g.k;
+  a.slice_bytes = (int)(g.head_stride * 2);
+}
+
+SplitArgs split_args(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx, void* ws,
+                     float* out) {
   SplitArgs a;
   a.k = k;
   a.v = v;
@@ -1266,7 +1725,81 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   a.win_start = g.win_start;
   a.hdr_out = (int4*)((char*)ws + g.hdr_off);
   a.out = out;
+  slot_args(g, a);
+  a.n_units = g.max_chunks * g.batch * g.hkv * g.row_groups;
+  a.per_xcd = (a.n_units + kXcdCount - 1) / kXcdCount;
+  a.xcd_map = env_int("BRS_XCD", 1) != 0;
+  return a;
+}
+unsigned slot_grid(const SplitArgs& a) { return (unsigned)(a.xcd_map ? a.per_xcd * kXcdCount : a.n_units); }
+}  // namespace
+
+bool step_supported(const AttnGeom& g, int64_t lo, int64_t hi, int k) {
+  const int R = g.idx_heads == 1 ? 1 : g.group;
+  return g.slot && R <= kSelWaves && k >= 1 && k <= kStepK && hi - lo <= 64 * 32 && (g.d == 64 || g.d == 128) &&
+         env_int("BRS_STEP", 1) != 0;
+}
+
+hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, const void* q, const float* scores,
+                            int64_t stride, int64_t lo, int64_t hi, int32_t* idx, float* vals, void* ws, float* out,
+                            hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  SplitArgs a = split_args(g, k, v, q, idx, ws, out);
+  a.scores = scores;
+  a.score_stride = stride;
+  a.sel_lo = (int)lo;
+  a.sel_hi = (int)hi;
+  a.idx_out = idx;
+  a.vals_out = vals;
+  const dim3 grid(slot_grid(a)), block(64 * kSlotWaves);
+  const int64_t n = hi - lo;
+#define BRS_LAUNCH_STEP1(DD, KP, DEP)                                                               \
+  if (g.d == DD && g.depth == DEP) {                                                                \
+    if (ev0)                                                                                        \
+      hipExtLaunchKernelGGL((attn_step_kernel<DD, KP, DEP>), grid, block, 0, s, ev0, ev1, 0, a);    \
+    else                                                                                            \
+      hipLaunchKernelGGL((attn_step_kernel<DD, KP, DEP>), grid, block, 0, s, a);                    \
+    return hipGetLastError();                                                                       \
+  }
+#define BRS_LAUNCH_STEP(DD, KP) BRS_LAUNCH_STEP1(DD, KP, 1) BRS_LAUNCH_STEP1(DD, KP, 2)
+  if (n <= 256) {
+    BRS_LAUNCH_STEP(64, 4)
+    BRS_LAUNCH_STEP(128, 4)
+  } else if (n <= 512) {
+    BRS_LAUNCH_STEP(64, 8)
+    BRS_LAUNCH_STEP(128, 8)
+  } else if (n <= 1024) {
+    BRS_LAUNCH_STEP(64, 16)
+    BRS_LAUNCH_STEP(128, 16)
+  } else {
+    BRS_LAUNCH_STEP(64, 32)
+    BRS_LAUNCH_STEP(128, 32)
+  }
+#undef BRS_LAUNCH_STEP
+#undef BRS_LAUNCH_STEP1
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
+                             void* ws, float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  SplitArgs a = split_args(g, k, v, q, idx, ws, out);
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
+  if (g.slot) {
+    const dim3 grid1(slot_grid(a)), block(64 * kSlotWaves);
+#define BRS_LAUNCH_SLOT(DD, DEP)                                                                     \
+  if (g.d == DD && g.depth == DEP) {                                                                 \
+    if (ev0)                                                                                         \
+      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, DEP>), grid1, block, 0, s, ev0, ev1, 0, a);  \
+    else                                                                                             \
+      hipLaunchKernelGGL((attn_split_slot_kernel<DD, DEP>), grid1, block, 0, s, a);                  \
+    return hipGetLastError();                                                                        \
+  }
+    BRS_LAUNCH_SLOT(64, 1)
+    BRS_LAUNCH_SLOT(128, 1)
+    BRS_LAUNCH_SLOT(64, 2)
+    BRS_LAUNCH_SLOT(128, 2)
+#undef BRS_LAUNCH_SLOT
+    return hipErrorInvalidValue;
+  }
   if (g.mfma) {
     const dim3 block(64 * g.nw);
   // LDS sized for the waves actually launched: a smaller footprint lets
@@ -1319,7 +1852,7 @@ hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_
   const int64_t rows = (int64_t)g.batch * g.hq * g.n_q;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows), dim3(256), 0, s, (const int4*)((char*)ws + g.hdr_off),
                      (const float2*)((char*)ws + g.ml_off), (const float*)((char*)ws + g.o_off), out, g.hq, g.hkv,
-                     g.n_q, g.d, g.chunk_tokens, g.max_chunks);
+                     g.n_q, g.d, g.slot ? 0 : g.chunk_tokens, g.max_chunks, g.max_chunks);
   return hipGetLastError();
 }
 

@@ -53,6 +53,27 @@ __device__ inline int block_inclusive_scan(int v, int* wave_tot /* [16] shared *
   return v + add;
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (same column of the
+// accumulator) with the gfx950 lane-swap moves (no LDS round trip).
+__device__ __forceinline__ float xmax16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xmin16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // attention plan
 //
@@ -81,6 +102,10 @@ struct AttnGeom {
   bool mfma;              // bfloat16 served by the matrix-core kernel
   bool prefill;           // chunk of queries served by the matrix-core prefill kernel
   bool local_plan;        // split workgroups build their segments from idx (no plan kernel)
+  bool slot;              // split workgroups read the selections directly (slot layout, no plan)
+  int slot_ps, slot_bs;   // slot layout: padded sinks, slot stride (tokens)
+  int depth;              // slot layout: tiles of loads in flight per wave
+  int len_a, len_b;       // slot layout: sink/window tokens, slot tokens (padded)
   int64_t max_items;      // segments per (batch, kv head)
   int64_t max_tokens;     // bound on attended tokens per (batch, kv head)
   int nw;                 // waves per split workgroup
@@ -101,6 +126,13 @@ hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, flo
 hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
                              void* ws, float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);
+// Whole decode step after scoring in one attention launch, the selection
+// made inside it (slot layout): same partials as launch_attn_split given
+// that selection.
+bool step_supported(const AttnGeom& g, int64_t lo, int64_t hi, int k);
+hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, const void* q, const float* scores,
+                            int64_t stride, int64_t lo, int64_t hi, int32_t* idx, float* vals, void* ws, float* out,
+                            hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 // Chunked prefill on the matrix cores (reads the plan's segments from ws).
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
                                float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);

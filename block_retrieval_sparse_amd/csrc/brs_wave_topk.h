@@ -13,8 +13,8 @@
 //      the lowest indices among them by a second radix select on ~index;
 //   4. gather the k kept entries (any order) and rank them by counting on the
 //      64-bit key (score key, ~index), which is the output order.
-// Returned scores are the row's own values (re-read for the zero and NaN
-// keys, whose sign or payload the key does not keep).
+// Returned scores are the row's own bits, kept beside the keys (a key does
+// not hold the sign of zero or a NaN payload).
 #ifndef BRS_WAVE_TOPK_H_
 #define BRS_WAVE_TOPK_H_
 
@@ -53,6 +53,16 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
   return v;
 }
 
+// Barrier of the threads that share one row: the workgroup, or (WAVE) the
+// one wave that holds the row.
+template <bool WAVE>
+__device__ __forceinline__ void row_sync() {
+  if constexpr (WAVE)
+    wave_lds_sync();
+  else
+    __syncthreads();
+}
+
 // LDS state of one row's selection.
 struct TopkRowShared {
   uint32_t hist[256];
@@ -62,10 +72,10 @@ struct TopkRowShared {
 
 // One radix pass over the keys still matching `prefix` under `mask`:
 // finds the digit (bits shift..shift+7) that holds the kk-th largest key.
-// Every thread of the workgroup must call it (three barriers).  hist is
+// Every thread of the row group must call it (three barriers).  hist is
 // zero on entry and on exit.  A wave whose matching keys in one slot share
 // a digit adds them with one atomic instead of one per lane.
-template <int KPT>
+template <int KPT, bool WAVE>
 __device__ __forceinline__ void topk_radix_pass(const uint32_t (&keys)[KPT], uint32_t vmask, uint32_t prefix,
                                                 uint32_t mask, int shift, int& kk, int tpr, TopkRowShared& sh,
                                                 uint32_t& digit_out) {
@@ -86,7 +96,7 @@ __device__ __forceinline__ void topk_radix_pass(const uint32_t (&keys)[KPT], uin
       }
     }
   }
-  __syncthreads();
+  row_sync<WAVE>();
   // bins in descending digit order, 256 / tpr per thread (tpr <= 256)
   const int bpt = 256 / tpr;
   int h[4] = {0, 0, 0, 0}, run = 0;
@@ -100,7 +110,7 @@ __device__ __forceinline__ void topk_radix_pass(const uint32_t (&keys)[KPT], uin
     }
   const int incl = wave_scan_incl(run);
   if (lane == 63) sh.wtot[wv] = incl;
-  __syncthreads();
+  row_sync<WAVE>();
   int before = incl - run;
   for (int w = 0; w < wv; ++w) before += sh.wtot[w];
 #pragma unroll
@@ -113,7 +123,7 @@ __device__ __forceinline__ void topk_radix_pass(const uint32_t (&keys)[KPT], uin
       }
       before += h[j];
     }
-  __syncthreads();
+  row_sync<WAVE>();
   digit_out = (uint32_t)sh.digit;
   kk -= sh.above;
 }
@@ -121,7 +131,7 @@ __device__ __forceinline__ void topk_radix_pass(const uint32_t (&keys)[KPT], uin
 // Radix select of the kk-th largest key among the valid ones (4 passes).
 // Returns the threshold key; kk becomes the number of keys equal to it to
 // take, and sh.neq holds how many there are.
-template <int KPT>
+template <int KPT, bool WAVE>
 __device__ __forceinline__ uint32_t topk_radix_select(const uint32_t (&keys)[KPT], uint32_t vmask, int& kk, int tpr,
                                                       TopkRowShared& sh) {
   uint32_t prefix = 0u, mask = 0u;
@@ -129,45 +139,61 @@ __device__ __forceinline__ uint32_t topk_radix_select(const uint32_t (&keys)[KPT
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     uint32_t dg;
-    topk_radix_pass<KPT>(keys, vmask, prefix, mask, shift, kk, tpr, sh, dg);
+    topk_radix_pass<KPT, WAVE>(keys, vmask, prefix, mask, shift, kk, tpr, sh, dg);
     prefix |= dg << shift;
     mask |= 0xffu << shift;
   }
   return prefix;
 }
 
-// Top-k of srow[lo, hi) by the tpr threads of one row group (tpr a power of
-// two in 64..256, hi - lo <= tpr * KPT, 1 <= k).  Every thread of the
-// workgroup must call it, with the same lo, hi and k (barriers).  sh:
-// zeroed hist and cnt; sel: k 64-bit words of LDS.  Results in rank order
-// go to gidx / gvals (global; gvals may be null) and lidx (LDS; may be
-// null); slots past min(k, hi - lo) get -1 and -inf.
+// The scores of one row as raw bits, thread t holding columns lo + tpr i + t
+// (lanes past the end re-read column lo: the loads are unconditional, so
+// they all stay in flight together).
 template <int KPT>
-__device__ void group_topk(const float* __restrict__ srow, int lo, int hi, int k, int tpr, TopkRowShared& sh,
-                           int* wg_flag, uint64_t* sel, int32_t* gidx, float* gvals, int32_t* lidx) {
+__device__ __forceinline__ void topk_load_raw(const float* __restrict__ srow, int lo, int hi, int tpr,
+                                              uint32_t (&raw)[KPT]) {
+  const int t = threadIdx.x % tpr;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int e = lo + tpr * i + t;
+    raw[i] = hi > lo ? __float_as_uint(srow[e < hi ? e : lo]) : 0u;
+  }
+}
+
+// Top-k of srow[lo, hi) by the tpr threads of one row group (tpr a power of
+// two in 64..256, hi - lo <= tpr * KPT, 1 <= k): the whole workgroup, or
+// (WAVE, tpr = 64) a single wave.  raw: the row from topk_load_raw.  Every
+// thread of the group must call it, with the same lo, hi and k (barriers).
+// sh: zeroed hist and cnt; sel, selv: k 64-bit and k 32-bit words of LDS.
+// Results in rank order go to gidx / gvals (global) and lidx / lvals (LDS),
+// each of which may be null; slots past min(k, hi - lo) get -1 and -inf.
+// The returned scores are the row's own bits (kept beside the keys, which
+// do not hold the sign of zero or a NaN payload).
+template <int KPT, bool WAVE = false>
+__device__ void group_topk_raw(const uint32_t (&raw)[KPT], int lo, int hi, int k, int tpr, TopkRowShared& sh,
+                               int* wg_flag, uint64_t* sel, uint32_t* selv, int32_t* gidx, float* gvals,
+                               int32_t* lidx, float* lvals) {
   const int t = threadIdx.x % tpr;
   const int n = hi - lo;
   uint32_t keys[KPT];
   uint32_t vmask = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int e = lo + tpr * i + t;
-    const bool v = e < hi;
-    // unconditional loads (lanes past the end re-read column lo) keep them all in flight
-    keys[i] = n > 0 ? topk_key(srow[v ? e : lo]) : 0u;
+    const bool v = lo + tpr * i + t < hi;
+    keys[i] = n > 0 ? topk_key(__uint_as_float(raw[i])) : 0u;
     vmask |= v ? (1u << i) : 0u;
   }
-  const bool all = n <= k;  // the same for every row of the workgroup
+  const bool all = n <= k;  // the same for every thread of the group
   uint32_t thresh = 0u, thresh2 = 0u;
   bool ties = false;
   if (!all) {
     int kk = k;
-    thresh = topk_radix_select<KPT>(keys, vmask, kk, tpr, sh);
+    thresh = topk_radix_select<KPT, WAVE>(keys, vmask, kk, tpr, sh);
     // more keys equal to the threshold than places: the lowest indices win,
     // i.e. the largest ~index, found by a second select among those keys
     ties = sh.neq > kk;
     if (t == 0 && ties) *wg_flag = 1;
-    __syncthreads();
+    row_sync<WAVE>();
     if (*wg_flag) {
       uint32_t keys2[KPT];
       uint32_t vmask2 = 0u;
@@ -177,7 +203,7 @@ __device__ void group_topk(const float* __restrict__ srow, int lo, int hi, int k
         vmask2 |= (((vmask >> i) & 1u) && keys[i] == thresh) ? (1u << i) : 0u;
       }
       int kk2 = kk > 0 ? kk : 1;
-      thresh2 = topk_radix_select<KPT>(keys2, vmask2, kk2, tpr, sh);
+      thresh2 = topk_radix_select<KPT, WAVE>(keys2, vmask2, kk2, tpr, sh);
       if (kk <= 0) thresh2 = 0xffffffffu;  // nothing equal to the threshold is taken
     }
   }
@@ -189,10 +215,13 @@ __device__ void group_topk(const float* __restrict__ srow, int lo, int hi, int k
     const bool take = v && (all || keys[i] > thresh || (keys[i] == thresh && (!ties || inv_idx >= thresh2)));
     if (take) {
       const int p = atomicAdd(&sh.cnt, 1);
-      if (p < k) sel[p] = ((uint64_t)keys[i] << 32) | (uint64_t)inv_idx;
+      if (p < k) {
+        sel[p] = ((uint64_t)keys[i] << 32) | (uint64_t)inv_idx;
+        selv[p] = raw[i];
+      }
     }
   }
-  __syncthreads();
+  row_sync<WAVE>();
   const int cnt = sh.cnt < k ? sh.cnt : k;
   for (int r = t; r < cnt; r += tpr) {
     const uint64_t me = sel[r];
@@ -200,17 +229,109 @@ __device__ void group_topk(const float* __restrict__ srow, int lo, int hi, int k
 #pragma unroll 8
     for (int j = 0; j < cnt; ++j) rank += sel[j] > me;
     const int b = (int)(0xffffffffu - (uint32_t)(me & 0xffffffffu));
-    const uint32_t key = (uint32_t)(me >> 32);
-    const float val = (key == 0u || key == 0x80000000u) ? srow[b] : topk_key_value(key);
-    gidx[rank] = b;
+    const float val = __uint_as_float(selv[r]);
+    if (gidx) gidx[rank] = b;
     if (gvals) gvals[rank] = val;
     if (lidx) lidx[rank] = b;
+    if (lvals) lvals[rank] = val;
   }
   for (int r = cnt + t; r < k; r += tpr) {
-    gidx[r] = -1;
+    if (gidx) gidx[r] = -1;
+    if (gvals) gvals[r] = -INFINITY;
+    if (lidx) lidx[r] = -1;
+    if (lvals) lvals[r] = -INFINITY;
+  }
+}
+
+// Exact top-k of one row by one wave, fast path (raw, lo, hi, k as in
+// group_topk_raw; k <= 64).  A lower bound on the k-th largest key is the
+// k-th largest of the 64 lane maxima (found bit by bit with ballots); the
+// keys at or above it -- a few more than k on ordinary data -- are gathered
+// in LDS and ranked by counting on (score key, ~index).  Returns false, with
+// nothing written, when more than cap keys pass the bound (many equal
+// scores); the radix select then does the work.  sel / selv: cap words.
+constexpr int kBisect = 10;  // halvings of the lane-maximum range in wave_topk_filter
+
+template <int KPT>
+__device__ bool wave_topk_filter(const uint32_t (&raw)[KPT], int lo, int hi, int k, int cap, uint64_t* sel,
+                                 uint32_t* selv, int32_t* gidx, float* gvals, int32_t* lidx) {
+  const int lane = threadIdx.x & 63;
+  const int n = hi - lo;
+  uint32_t keys[KPT];
+  uint32_t vmask = 0u, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool v = lo + 64 * i + lane < hi;
+    keys[i] = n > 0 ? topk_key(__uint_as_float(raw[i])) : 0u;
+    vmask |= v ? (1u << i) : 0u;
+    mx = v ? max(mx, keys[i]) : mx;
+  }
+  uint32_t tau = 0u;
+  if (n > k) {
+    if (k > 64) return false;
+    // bisection between the smallest and largest lane maximum, keeping
+    // "at least k maxima >= tau" true; stopped after kBisect halvings (a
+    // lower bound is all that is needed: a few more keys pass it)
+    uint32_t lo_t = mx, hi_t = mx;
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo_t = min(lo_t, (uint32_t)__shfl_xor((int)lo_t, off));
+      hi_t = max(hi_t, (uint32_t)__shfl_xor((int)hi_t, off));
+    }
+    lo_t = __builtin_amdgcn_readfirstlane(lo_t);
+    hi_t = __builtin_amdgcn_readfirstlane(hi_t);
+#pragma unroll
+    for (int it = 0; it < kBisect; ++it) {
+      const uint32_t mid = lo_t + ((hi_t - lo_t + 1u) >> 1);
+      if (__popcll(__ballot(mx >= mid)) >= (uint64_t)k)
+        lo_t = mid;
+      else
+        hi_t = mid - 1u;
+    }
+    tau = lo_t;
+  }
+  // the keys at or above tau, gathered in LDS (in order of i, then lane)
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool take = ((vmask >> i) & 1u) && keys[i] >= tau;
+    const uint64_t m = __ballot(take);
+    const int p = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (take && p < cap) {
+      sel[p] = ((uint64_t)keys[i] << 32) | (uint64_t)(0xffffffffu - (uint32_t)(lo + 64 * i + lane));
+      selv[p] = raw[i];
+    }
+    total += (int)__popcll(m);
+  }
+  if (total > cap) return false;
+  wave_lds_sync();
+  for (int r = lane; r < total; r += 64) {
+    const uint64_t me = sel[r];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < total; ++j) rank += sel[j] > me;
+    if (rank < k) {
+      const int b = (int)(0xffffffffu - (uint32_t)(me & 0xffffffffu));
+      if (gidx) gidx[rank] = b;
+      if (gvals) gvals[rank] = __uint_as_float(selv[r]);
+      if (lidx) lidx[rank] = b;
+    }
+  }
+  for (int r = total + lane; r < k; r += 64) {
+    if (gidx) gidx[r] = -1;
     if (gvals) gvals[r] = -INFINITY;
     if (lidx) lidx[r] = -1;
   }
+  return true;
+}
+
+// Load and select in one call (see group_topk_raw).
+template <int KPT, bool WAVE = false>
+__device__ void group_topk(const float* __restrict__ srow, int lo, int hi, int k, int tpr, TopkRowShared& sh,
+                           int* wg_flag, uint64_t* sel, uint32_t* selv, int32_t* gidx, float* gvals,
+                           int32_t* lidx) {
+  uint32_t raw[KPT];
+  topk_load_raw<KPT>(srow, lo, hi, tpr, raw);
+  group_topk_raw<KPT, WAVE>(raw, lo, hi, k, tpr, sh, wg_flag, sel, selv, gidx, gvals, lidx, nullptr);
 }
 
 }  // namespace brs

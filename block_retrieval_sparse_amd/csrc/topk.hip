@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256) void topk_group_kernel(const float* __restrict
                                                          float* __restrict__ vals) {
   __shared__ TopkRowShared sh;
   __shared__ uint64_t sel[kGroupK];
+  __shared__ uint32_t selv[kGroupK];
   __shared__ int flag;
   const int64_t row = blockIdx.x;
   for (int i = threadIdx.x; i < 256; i += 256) sh.hist[i] = 0u;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void topk_group_kernel(const float* __restrict
     flag = 0;
   }
   __syncthreads();
-  group_topk<KPT>(scores + row * stride, (int)lo, (int)hi, k, 256, sh, &flag, sel, idx + row * k,
+  group_topk<KPT>(scores + row * stride, (int)lo, (int)hi, k, 256, sh, &flag, sel, selv, idx + row * k,
                   vals ? vals + row * k : nullptr, nullptr);
 }
 

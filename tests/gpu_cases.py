@@ -29,11 +29,13 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def load(w: Workload, device="cuda", pieces: int = 1, capacity: int | None = None):
-    """Generate workload ``w`` and append it into a fresh KVMemory in ``pieces`` appends."""
+def load(w: Workload, device="cuda", pieces: int = 1, capacity: int | None = None, x: dict | None = None):
+    """Generate workload ``w`` (or take its inputs ``x``) and append it into a
+    fresh KVMemory in ``pieces`` appends."""
     import block_retrieval_sparse_amd as brs
 
-    x = I.make_all(w, device)
+    if x is None:
+        x = I.make_all(w, device)
     rep_dtype = torch.bfloat16 if w.rep_mode == "embed" else I.torch_dtype(w)
     mem = brs.KVMemory(w.batch, w.n_kv_heads, w.head_dim, capacity or w.n_tokens, w.block,
                        dtype=I.torch_dtype(w), rep_mode=w.rep_mode, reps_per_block=w.reps_per_block,

@@ -86,6 +86,41 @@ def test_step(name):
             assert set(blocks) <= set(idx[b, h].tolist()), (b, h)
 
 
+@pytest.mark.parametrize("kind", ["equal", "few", "nan", "quantized"])
+def test_step_selection_ties_and_nan(kind):
+    """The decode step selects inside its attention kernel; scores with many
+    exact ties (every block equal, three distinct representatives, rounded
+    representatives) and NaN scores must give the oracle's selection (ties to
+    the lowest block index, NaN last) and the same bits as the standalone
+    selection followed by the attention call."""
+    from block_retrieval_sparse_amd.pipeline import RetrievalStep
+    from synth import inputs as I
+
+    w = W["landmark_decode_32k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=40000 + 17, k=32)
+    x = I.make_all(w, "cuda")
+    reps = x["given_reps"]
+    g = torch.Generator(device="cpu").manual_seed(7)
+    if kind == "equal":
+        reps[:] = reps[:, :, :1]
+    elif kind == "few":
+        pick = torch.randint(0, 3, (reps.shape[2],), generator=g).to(reps.device)
+        reps[:] = reps[:, :, :3][:, :, pick]
+    elif kind == "nan":
+        bad = torch.randint(0, reps.shape[2], (40,), generator=g).to(reps.device)
+        reps[:, :, bad] = float("nan")
+    else:
+        reps[:] = (reps.float() * 2).round().to(reps.dtype) / 2
+    mem, x = C.load(w, x=x)
+    step = run_step(mem, w, x)
+    C.check_step(w, mem, x, step, check_scores=kind != "nan")  # NaN payloads are not compared
+    three = RetrievalStep(mem, w.n_q_heads, w.n_q, w.k, w.sinks, w.window)
+    three.run_separate(x["q"], x["q"][:, :, -1, :].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(step.idx, three.idx)
+    assert torch.equal(step.vals.nan_to_num(0), three.vals.nan_to_num(0))
+    assert torch.equal(step.out, three.out)
+
+
 def test_determinism():
     w = SMALL["retrieval"]
     mem, x = C.load(w)
@@ -223,8 +258,9 @@ def test_full_size_memlong_prefill_sampled():
 
 @pytest.mark.parametrize("name", ["infllm", "gqa8", "landmark", "retrieval", "memlong", "multi_q", "prefill_gqa"])
 def test_step_call_matches_separate_calls(name):
-    """brs_retrieval_step (one call; the split kernels plan in-kernel) gives the
-    same scores, selection and attention bits as the three separate calls."""
+    """brs_retrieval_step (one call; for decode the attention kernel makes the
+    selection itself) gives the same scores, selection and attention bits as
+    the three separate calls."""
     from block_retrieval_sparse_amd.pipeline import RetrievalStep
 
     w = SMALL[name]
