@@ -2,14 +2,15 @@
 // indices of the similarity scores, found with an exact search, 2.4.2).
 //
 // Order: score descending, then block index ascending; NaN below every
-// number; -0 equal to +0.  One workgroup per (batch, head):
-//   1. map each score to a 32-bit key whose unsigned order is that score
-//      order (NaN -> 0);
-//   2. radix-select the k-th largest key, 8 bits per pass, with a 256-bin
-//      histogram in LDS;
-//   3. keep every key above it and, among keys equal to it, the lowest block
-//      indices (a prefix count over the workgroup in index order);
-//   4. sort the k winners by counting, on the 64-bit key (score key, ~index).
+// number; -0 equal to +0.  Each score maps to a 32-bit key whose unsigned
+// order is that score order (NaN -> 0).
+//   k <= 64, up to 2048 candidates: one wave per row; a lower bound on the
+//     k-th key from the lane maxima, then the keys above it ranked by
+//     counting (a one-wave radix select when too many keys reach the bound);
+//   k <= 512, up to 2048 candidates: one 256-thread workgroup per row, radix
+//     select of the k-th key with a 256-bin histogram in LDS, ties at it to
+//     the lowest indices, rank sort of the winners;
+//   otherwise: the same with 1024 threads, keys in registers or re-read.
 #include "brs_wave_topk.h"
 
 namespace brs {
@@ -163,12 +164,56 @@ __global__ __launch_bounds__(256) void topk_group_kernel(const float* __restrict
                   vals ? vals + row * k : nullptr, nullptr);
 }
 
+// One wave per row (four rows per 256-thread workgroup) for k <= 64 and up
+// to 64 * KPT candidates: the bound-and-rank selection of brs_wave_topk.h,
+// with the one-wave radix select for rows with too many keys at the bound.
+constexpr int kWaveCand = 256;
+
+template <int KPT>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
+                                                        int64_t hi, int k, int64_t rows, int32_t* __restrict__ idx,
+                                                        float* __restrict__ vals) {
+  __shared__ TopkRowShared sh[4];
+  __shared__ uint64_t sel[4][kWaveCand];
+  __shared__ uint32_t selv[4][kWaveCand];
+  __shared__ int flag[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;  // whole waves only: the code below syncs within the wave
+  uint32_t raw[KPT];
+  topk_load_raw<KPT>(scores + row * stride, (int)lo, (int)hi, 64, raw);
+  int32_t* gi = idx + row * k;
+  float* gv = vals ? vals + row * k : nullptr;
+  if (wave_topk_filter<KPT>(raw, (int)lo, (int)hi, k, kWaveCand, sel[wave], selv[wave], gi, gv, nullptr)) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sh[wave].hist[lane + 64 * j] = 0u;
+  if (lane == 0) {
+    sh[wave].cnt = 0;
+    flag[wave] = 0;
+  }
+  wave_lds_sync();
+  group_topk_raw<KPT, true>(raw, (int)lo, (int)hi, k, 64, sh[wave], &flag[wave], sel[wave], selv[wave], gi, gv,
+                            nullptr, nullptr);
+}
+
 }  // namespace
 
 hipError_t launch_select_topk(const float* scores, int batch, int heads, int64_t stride, int64_t lo, int64_t hi,
                               int k, int32_t* idx, float* vals, hipStream_t s) {
   const int64_t rows = (int64_t)batch * heads;
   const int64_t n = hi - lo;
+  if (k <= 64 && n <= 64 * 32) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (n <= 64 * 4)
+      hipLaunchKernelGGL((topk_wave_kernel<4>), grid, block, 0, s, scores, stride, lo, hi, k, rows, idx, vals);
+    else if (n <= 64 * 8)
+      hipLaunchKernelGGL((topk_wave_kernel<8>), grid, block, 0, s, scores, stride, lo, hi, k, rows, idx, vals);
+    else if (n <= 64 * 16)
+      hipLaunchKernelGGL((topk_wave_kernel<16>), grid, block, 0, s, scores, stride, lo, hi, k, rows, idx, vals);
+    else
+      hipLaunchKernelGGL((topk_wave_kernel<32>), grid, block, 0, s, scores, stride, lo, hi, k, rows, idx, vals);
+    return hipGetLastError();
+  }
   if (k <= kGroupK && n <= 256 * 8) {
     const dim3 grid((unsigned)rows), block(256);
     if (n <= 256)
