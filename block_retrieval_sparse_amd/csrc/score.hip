@@ -47,6 +47,74 @@ __device__ __forceinline__ double nan_max(double a, double b) {
   return (b > a || b != b) ? b : a;
 }
 
+// p0, p1 = this lane's value and its partner's, in either order: the partner
+// is lane ^ OFF for OFF = 1, 2, 16, 32, and for OFF = 4, 8 the half-row /
+// row mirror (lane 2*OFF-1-i of its group of 2*OFF: the same value as
+// lane ^ OFF once each group of OFF lanes holds one value).  DPP moves and
+// gfx950 row swaps on the two 32-bit halves: VALU work, no LDS permutes.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(double v, double& p0, double& p1) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  auto join = [](uint32_t l, uint32_t h) { return __builtin_bit_cast(double, ((uint64_t)h << 32) | l); };
+  if constexpr (OFF <= 8) {
+    constexpr int ctrl = OFF == 1 ? 0xb1 : OFF == 2 ? 0x4e : OFF == 4 ? 0x141 : 0x140;
+    p0 = v;
+    p1 = join((uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, ctrl, 0xf, 0xf, false),
+              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, ctrl, 0xf, 0xf, false));
+  } else if constexpr (OFF == 16) {
+    // a swap returns {own, partner} or {partner, own} by row; both halves
+    // are swapped alike, so element e of the two halves is one value
+    const auto x = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto y = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    p0 = join(x[0], y[0]);
+    p1 = join(x[1], y[1]);
+  } else {
+    static_assert(OFF == 32, "offset");
+    const auto x = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto y = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    p0 = join(x[0], y[0]);
+    p1 = join(x[1], y[1]);
+  }
+}
+template <int OFF>
+__device__ __forceinline__ double pair_sum(double v) {
+  double p0, p1;
+  lane_pair<OFF>(v, p0, p1);
+  return p0 + p1;
+}
+template <int OFF>
+__device__ __forceinline__ double pair_max(double v) {
+  double p0, p1;
+  lane_pair<OFF>(v, p0, p1);
+  return nan_max(p0, p1);
+}
+
+// Sum over aligned groups of L lanes (every lane gets its group's total).
+template <int L>
+__device__ __forceinline__ double group_sum_f64(double v) {
+  if constexpr (L >= 2) v = pair_sum<1>(v);
+  if constexpr (L >= 4) v = pair_sum<2>(v);
+  if constexpr (L >= 8) v = pair_sum<4>(v);
+  if constexpr (L >= 16) v = pair_sum<8>(v);
+  if constexpr (L >= 32) v = pair_sum<16>(v);
+  if constexpr (L >= 64) v = pair_sum<32>(v);
+  return v;
+}
+
+// NaN-keeping max over aligned groups of n = L * R lanes whose groups of L
+// lanes each hold one value (n a power of two up to 64).
+template <int L>
+__device__ __forceinline__ double group_max_f64(double v, int n) {
+  if constexpr (L <= 1) if (n > 1) v = pair_max<1>(v);
+  if constexpr (L <= 2) if (n > 2) v = pair_max<2>(v);
+  if constexpr (L <= 4) if (n > 4) v = pair_max<4>(v);
+  if constexpr (L <= 8) if (n > 8) v = pair_max<8>(v);
+  if constexpr (L <= 16) if (n > 16) v = pair_max<16>(v);
+  if constexpr (L <= 32) if (n > 32) v = pair_max<32>(v);
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ double elem_f64(const T* p, int64_t i);
 template <>
@@ -182,14 +250,7 @@ __global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict
       acc[j] = a;
     }
 #pragma unroll
-    for (int off = 1; off < L; off <<= 1) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] += __shfl_xor(acc[j], off);
-    }
-    for (int off = L; off < L * R; off <<= 1) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] = nan_max(acc[j], __shfl_xor(acc[j], off));
-    }
+    for (int j = 0; j < G; ++j) acc[j] = group_max_f64<L>(group_sum_f64<L>(acc[j]), L * R);
     if (row < row_hi && (row % R) == 0) {
       const int64_t blk = row / R;
 #pragma unroll
