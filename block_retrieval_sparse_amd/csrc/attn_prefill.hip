@@ -194,21 +194,24 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((stage_v ? a.v : a.k) + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kBufferFlags);
   const int t256 = tid & 255;
-  int srow[VPT], scol[VPT], soff[VPT];
+  int srow[VPT], scol[VPT], soff[VPT], smask[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int e = t256 + 256 * j;
     const int r = e / a.nvec, c = e - r * a.nvec;
     srow[j] = r < kStage ? r : 0;
     scol[j] = e < kvec ? 16 * c : kOutOfRange;  // lanes without a vector read zeros
+    smask[j] = e < kvec ? -1 : 0;
     soff[j] = e < kvec ? (stage_v ? kBufs * BUF : 0) + r * KP + 8 * c : -1;
   }
   uint4 stg[kAhead][VPT];
   auto stage_offsets = [&](int(&at)[VPT], int stage) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
+      // the table read is unconditional (a select would make it a branch
+      // with a wait of its own); lanes without a vector mask it away
       const int off = s_tab[(stage * kStage + srow[j]) & (kTabTokens - 1)].y;
-      at[j] = scol[j] == kOutOfRange ? kOutOfRange : off + scol[j];
+      at[j] = (off & smask[j]) + scol[j];
     }
   };
   auto stage_load = [&](uint4(&dst)[VPT], const int(&at)[VPT]) {
@@ -248,7 +251,18 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
       qb[kk] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
-  const float qs = a.qscale;
+  // a negative scale is taken as |scale| with the query negated (exact in
+  // bf16), so the logits below are always scaled by a positive factor
+  const float qs = fabsf(a.qscale);
+  if (a.qscale < 0.f) {
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      qb[kk].x ^= 0x80008000u;
+      qb[kk].y ^= 0x80008000u;
+      qb[kk].z ^= 0x80008000u;
+      qb[kk].w ^= 0x80008000u;
+    }
+  }
 
   f32x4_p o[NJ];
 #pragma unroll
@@ -288,31 +302,28 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     const int tbase = s * kStage + r0;
     // whole: the stream is in position order, so its last token bounds the half
     const bool whole = s_tab[(tbase + 31) & (kTabTokens - 1)].x <= plim_min;
-    float sv[8];
-    bool vis[8];
+    // logits of tokens past a row's causal limit become -inf, so their
+    // weights come out as zero
+    float x[8];
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[4 * sidx + i] = st[sidx][i];
-        vis[4 * sidx + i] = true;
-      }
+      for (int i = 0; i < 4; ++i) x[4 * sidx + i] = st[sidx][i];
     if (!whole) {
 #pragma unroll
       for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = s_tab[(tbase + 16 * sidx + 4 * g4 + i) & (kTabTokens - 1)].x;
-          vis[4 * sidx + i] = pos <= plim;
+          x[4 * sidx + i] = pos <= plim ? x[4 * sidx + i] : -INFINITY;
         }
     }
-    // scaled logits (log2 units) and their row maximum over visible tokens
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = sv[i] * qs;
+    // row maximum of the scaled logits (log2 units): the raw maximum times
+    // the scale, so the scale itself goes into the exponent's fma
     float e = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e = fmaxf(e, vis[i] ? sv[i] : -INFINITY);
-    const float tm = xmax16_32(e);
+    for (int i = 0; i < 8; ++i) e = fmaxf(e, x[i]);
+    const float tm = xmax16_32(e) * qs;
     if (__ballot(tm > mref + kLazyP)) {
       const float nm = fmaxf(mref, tm);
       const float al = exp2_fast(mref - nm);
@@ -330,10 +341,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x2_p p2;
-      p2.x = exp2_fast(sv[2 * i] - mref);
-      p2.y = exp2_fast(sv[2 * i + 1] - mref);
-      p2.x = vis[2 * i] ? p2.x : 0.f;
-      p2.y = vis[2 * i + 1] ? p2.y : 0.f;
+      p2.x = exp2_fast(fmaf(x[2 * i], qs, -mref));
+      p2.y = exp2_fast(fmaf(x[2 * i + 1], qs, -mref));
       const bf16x2_p hi = __builtin_convertvector(p2, bf16x2_p);
       const f32x2_p back = __builtin_convertvector(hi, f32x2_p);
       ph[i] = __builtin_bit_cast(uint32_t, hi);

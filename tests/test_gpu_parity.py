@@ -50,11 +50,11 @@ SMALL = {
 }
 
 
-def run_step(mem, w, x, k=None, sinks=None, window=None):
+def run_step(mem, w, x, k=None, sinks=None, window=None, scale=None):
     from block_retrieval_sparse_amd.pipeline import RetrievalStep
 
     step = RetrievalStep(mem, w.n_q_heads, w.n_q, w.k if k is None else k, w.sinks if sinks is None else sinks,
-                         w.window if window is None else window)
+                         w.window if window is None else window, scale=scale)
     qrep = x["rq"] if w.rep_mode == "embed" else x["q"][:, :, -1, :].contiguous()
     step.run(x["q"], qrep)
     return step
@@ -84,6 +84,18 @@ def test_step(name):
         idx = step.idx.cpu().numpy()
         for (b, h), blocks in x["planted"].items():
             assert set(blocks) <= set(idx[b, h].tolist()), (b, h)
+
+
+@pytest.mark.parametrize("name", ["prefill_gqa", "memlong", "infllm", "bf16_d64"])
+@pytest.mark.parametrize("scale", [-0.3, 1.5])
+def test_step_softmax_scale(name, scale):
+    """A negative softmax scale, and a large one (attention close to one-hot,
+    where the precision of the weights matters most)."""
+    w = SMALL[name]
+    mem, x = C.load(w)
+    step = run_step(mem, w, x, scale=scale)
+    res = C.check_step(w, mem, x, step)
+    print(f"{name} scale {scale}: max |err| {res['max_abs_err']:.3g}")
 
 
 @pytest.mark.parametrize("kind", ["equal", "few", "nan", "quantized"])
