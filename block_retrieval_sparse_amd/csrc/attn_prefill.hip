@@ -194,24 +194,28 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((stage_v ? a.v : a.k) + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kBufferFlags);
   const int t256 = tid & 255;
-  int srow[VPT], scol[VPT], soff[VPT], smask[VPT];
+  // Per vector: its row's table entry within a stage (byte offset), its
+  // column in bytes, and its LDS slot.  A lane without a vector gets column
+  // kOutOfRange: row offset + kOutOfRange stays below 2^32 (a slice is under
+  // kOutOfRange - 4096 bytes) and past the buffer's end, so it reads zeros.
+  uint32_t stab[VPT], scol[VPT];
+  int soff[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int e = t256 + 256 * j;
     const int r = e / a.nvec, c = e - r * a.nvec;
-    srow[j] = r < kStage ? r : 0;
-    scol[j] = e < kvec ? 16 * c : kOutOfRange;  // lanes without a vector read zeros
-    smask[j] = e < kvec ? -1 : 0;
+    stab[j] = (uint32_t)(r < kStage ? r : 0) * (uint32_t)sizeof(int2);
+    scol[j] = e < kvec ? 16u * c : (uint32_t)kOutOfRange;
     soff[j] = e < kvec ? (stage_v ? kBufs * BUF : 0) + r * KP + 8 * c : -1;
   }
   uint4 stg[kAhead][VPT];
   auto stage_offsets = [&](int(&at)[VPT], int stage) {
+    // a stage's 64 table entries never wrap around the ring
+    const char* tab = reinterpret_cast<const char*>(s_tab) + ((stage * kStage) & (kTabTokens - 1)) * sizeof(int2);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      // the table read is unconditional (a select would make it a branch
-      // with a wait of its own); lanes without a vector mask it away
-      const int off = s_tab[(stage * kStage + srow[j]) & (kTabTokens - 1)].y;
-      at[j] = (off & smask[j]) + scol[j];
+      const uint32_t off = (uint32_t)reinterpret_cast<const int2*>(tab + stab[j])->y;
+      at[j] = (int)(off + scol[j]);
     }
   };
   auto stage_load = [&](uint4(&dst)[VPT], const int(&at)[VPT]) {
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   };
 
   // softmax of stage s from its S^T, then O += P V
-  auto softmax_pv = [&](const f32x4_p(&st)[2], int s) {
+  auto softmax_pv = [&](f32x4_p(&st)[2], int s) {  // st: masked in place
     const uint16_t* vbuf = s_kv + kBufs * BUF + (s % kBufs) * BUF;
     bf16x8_p vb[NJ];
 #pragma unroll
@@ -304,20 +308,21 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     const bool whole = s_tab[(tbase + 31) & (kTabTokens - 1)].x <= plim_min;
     // logits of tokens past a row's causal limit become -inf, so their
     // weights come out as zero
-    float x[8];
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * sidx + i] = st[sidx][i];
+    // (in place, so both branches leave the logits in the same registers)
     if (!whole) {
 #pragma unroll
       for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = s_tab[(tbase + 16 * sidx + 4 * g4 + i) & (kTabTokens - 1)].x;
-          x[4 * sidx + i] = pos <= plim ? x[4 * sidx + i] : -INFINITY;
+          st[sidx][i] = pos <= plim ? st[sidx][i] : -INFINITY;
         }
     }
+    float x[8];
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * sidx + i] = st[sidx][i];
     // row maximum of the scaled logits (log2 units): the raw maximum times
     // the scale, so the scale itself goes into the exponent's fma
     float e = -INFINITY;
@@ -380,12 +385,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     stage_offsets(at, kAhead + 1);
     stage_load(stg[1], at);
     __syncthreads();
-    f32x4_p st_cur[2], st_nxt[2];
-    qk(st_cur, 0);
+    // S^T tiles of even stages in st_a, odd ones in st_b (kAhead is even)
+    static_assert(kAhead % 2 == 0, "stage parity");
+    f32x4_p st_a[2], st_b[2];
+    qk(st_a, 0);
     for (int s0 = 0; s0 < n_stages; s0 += kAhead) {
 #pragma unroll
       for (int j = 0; j < kAhead; ++j) {
         const int s = s0 + j;
+        f32x4_p(&st_cur)[2] = (j % 2 == 0) ? st_a : st_b;
+        f32x4_p(&st_nxt)[2] = (j % 2 == 0) ? st_b : st_a;
         // refill the token table half a ring ahead (entries of finished stages)
         if (s % kRefill == 0 && s >= kRefill) fill((s + kRefill) * kStage, kRefill * kStage);
         stage_offsets(at, s + 2 + kAhead);
@@ -394,8 +403,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
         stage_store(stg[(j + 2) % kAhead], s + 2);
         stage_load(stg[(j + 2) % kAhead], at);
         __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) st_cur[q] = st_nxt[q];
       }
     }
   }
