@@ -34,6 +34,10 @@ softmax attention over the local context plus the selected blocks.
 * O6 attention (``attention``): MemLong Figure 3 (local context is causal;
   retrieved chunks are visible in full), RetrievalAttention "proposed
   method" (exact attention over the tokens that matter).
+* O7 attention-score representatives (``attention_weights``,
+  ``attention_lse``, ``window_mass``, ``reps_attnscore``): InfLLM "method"
+  (a memory unit's representative tokens are those that received the most
+  attention in earlier attention computations).
 
 Readings where the pages are silent (the same list is kept with the design
 notes): attention sinks are the first S tokens; the window is the last W
@@ -44,7 +48,11 @@ float32; softmax scale is 1/sqrt(d) and scores carry no scale; query head h
 reads kv head h // G; several representatives combine by max; the selection
 is per query head for dot scores and per sequence for cosine scores; local
 and retrieved tokens share one softmax with no gate; query j of n sits at
-position N - n + j; the cosine of a zero vector is 0.
+position N - n + j; the cosine of a zero vector is 0; a token's attention
+score for choosing representatives is the softmax weight it receives while
+in the local window, summed over the query heads of its kv head and over
+queries; a block's representatives are chosen when the block becomes a
+candidate, from the mass accumulated up to then.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against brute force, exact rational arithmetic, closed forms or independent
@@ -228,6 +236,72 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, T: np.ndarray, scale:
         z = scale * (K[sel] @ Q[j])
         w = np.exp(z - z.max())
         out[j] = (w / w.sum()) @ V[sel]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O7: attention mass of the window tokens, and representatives chosen by it
+# (InfLLM "method": a memory unit is represented by its tokens that received
+# the highest attention scores in earlier attention computations)
+
+
+def attention_weights(Q: np.ndarray, K: np.ndarray, T: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax weights [n][N] of the attention in ``attention`` (0 off each query's visible set)."""
+    n, N = Q.shape[0], K.shape[0]
+    P = np.zeros((n, N))
+    pos = np.arange(N)
+    for j in range(n):
+        sel = T & (pos <= N - n + j)
+        if not sel.any():
+            raise ValueError(f"query {j}: empty attended set")
+        z = scale * (K[sel] @ Q[j])
+        w = np.exp(z - z.max())
+        P[j, sel] = w / w.sum()
+    return P
+
+
+def attention_lse(Q: np.ndarray, K: np.ndarray, T: np.ndarray, scale: float) -> np.ndarray:
+    """Natural log of each query's softmax denominator: log of the sum of exp(scale q.k) over its visible set."""
+    n, N = Q.shape[0], K.shape[0]
+    out = np.empty(n)
+    pos = np.arange(N)
+    for j in range(n):
+        sel = T & (pos <= N - n + j)
+        if not sel.any():
+            out[j] = -np.inf
+            continue
+        z = scale * (K[sel] @ Q[j])
+        m = z.max()
+        out[j] = m + math.log(np.exp(z - m).sum())
+    return out
+
+
+def window_mass(Qg: np.ndarray, K: np.ndarray, T: np.ndarray, scale: float, W: int) -> np.ndarray:
+    """Attention that each token of the local window received in one call: [N].
+
+    Qg [G][n][d] holds the query heads of one kv head.  The mass of token t is
+    the sum, over those heads and the n queries, of its softmax weight; tokens
+    before the window [N - W, N) get 0 (their memory units are already built).
+    """
+    N = K.shape[0]
+    m = np.zeros(N)
+    for h in range(Qg.shape[0]):
+        m += attention_weights(Qg[h], K, T, scale).sum(axis=0)
+    m[: max(N - W, 0)] = 0.0
+    return m
+
+
+def reps_attnscore(K: np.ndarray, mass: np.ndarray, B: int, R: int, blocks) -> np.ndarray:
+    """For each listed block, its R keys with the largest accumulated mass: [len(blocks)][R][d].
+
+    Order is (mass descending, token index ascending); the keys are copied
+    unchanged, in that order.
+    """
+    out = np.empty((len(blocks), R, K.shape[1]))
+    for i, b in enumerate(blocks):
+        toks = range(b * B, (b + 1) * B)
+        order = sorted(toks, key=lambda t: (-mass[t], t))
+        out[i] = K[order[:R]]
     return out
 
 

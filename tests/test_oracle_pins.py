@@ -384,11 +384,103 @@ def check_step_cosine_chunks():
             assert np.allclose(res["out"][(0, h)][j], V[0, h, toks].mean(axis=0), atol=1e-13)
 
 
+def _tiny_attn_case(rng, n=3, N=11, d=5):
+    Q = rng.normal(size=(n, d))
+    K = rng.normal(size=(N, d))
+    T = rng.random(N) < 0.7
+    T[N - n:] = True  # every query sees at least its own token
+    return Q, K, T
+
+
+def check_weights_and_lse_library():
+    """Weights are scipy's softmax of the visible logits (zero elsewhere); lse is scipy's logsumexp."""
+    from scipy.special import logsumexp, softmax
+
+    rng = np.random.default_rng(71)
+    for _ in range(20):
+        Q, K, T = _tiny_attn_case(rng)
+        n, N = Q.shape[0], K.shape[0]
+        scale = float(rng.uniform(0.2, 1.5))
+        P = O.attention_weights(Q, K, T, scale)
+        L = O.attention_lse(Q, K, T, scale)
+        for j in range(n):
+            vis = [t for t in range(N) if T[t] and t <= N - n + j]
+            z = scale * np.array([K[t] @ Q[j] for t in vis])
+            want = np.zeros(N)
+            want[vis] = softmax(z)
+            assert np.allclose(P[j], want, atol=1e-15, rtol=1e-12)
+            assert math.isclose(L[j], float(logsumexp(z)), rel_tol=1e-13, abs_tol=1e-13)
+            # a weight is exp(logit - lse)
+            assert np.allclose(P[j, vis], np.exp(z - L[j]), rtol=1e-12)
+
+
+def check_window_mass_zero_query():
+    """q = 0: every visible token weighs 1/|visible|, so the mass is a count (closed form)."""
+    N, d, G, n, W = 13, 4, 3, 4, 7
+    K = np.random.default_rng(5).normal(size=(N, d))
+    T = np.zeros(N, dtype=bool)
+    T[:2] = True
+    T[N - W:] = True
+    T[4:6] = True
+    Qg = np.zeros((G, n, d))
+    m = O.window_mass(Qg, K, T, 0.7, W)
+    want = np.zeros(N)
+    for j in range(n):
+        vis = [t for t in range(N) if T[t] and t <= N - n + j]
+        for t in vis:
+            if t >= N - W:
+                want[t] += G * Fraction(1, len(vis))
+    assert np.allclose(m, want.astype(float), atol=1e-15)
+
+
+def check_window_mass_conservation_and_range():
+    """With the window over every token, the mass sums to heads x queries; outside the window it is 0."""
+    rng = np.random.default_rng(9)
+    G, n, N, d = 2, 3, 12, 4
+    Qg = rng.normal(size=(G, n, d))
+    K = rng.normal(size=(N, d))
+    T = np.ones(N, dtype=bool)
+    m = O.window_mass(Qg, K, T, 0.5, N)
+    assert math.isclose(m.sum(), G * n, rel_tol=1e-13)
+    assert (m > 0).all()
+    W = 5
+    mw = O.window_mass(Qg, K, T, 0.5, W)
+    assert (mw[: N - W] == 0).all()
+    assert np.allclose(mw[N - W:], m[N - W:], rtol=1e-14)
+    # the last query's own token is seen by that query only
+    Qa = rng.normal(size=(1, n, d))
+    last = O.window_mass(Qa, K, T, 0.5, N)[N - 1]
+    z = 0.5 * (K @ Qa[0, n - 1])
+    assert math.isclose(last, math.exp(z[-1]) / np.exp(z).sum(), rel_tol=1e-12)
+
+
+def check_reps_attnscore_bruteforce():
+    """Largest mass first, ties to the lower token, keys copied; checked with an independent lexsort."""
+    rng = np.random.default_rng(13)
+    for _ in range(30):
+        B, R, nb, d = 6, 3, 4, 3
+        K = rng.normal(size=(nb * B, d))
+        mass = rng.integers(0, 4, size=nb * B).astype(float)  # many ties
+        blocks = [int(b) for b in rng.permutation(nb)[:3]]
+        got = O.reps_attnscore(K, mass, B, R, blocks)
+        for i, b in enumerate(blocks):
+            toks = np.arange(b * B, (b + 1) * B)
+            order = toks[np.lexsort((toks, -mass[toks]))][:R]
+            assert np.array_equal(got[i], K[order])
+    # one token far above the rest stands first
+    K = np.arange(12.0).reshape(4, 3)
+    mass = np.array([0.1, 5.0, 0.1, 0.2])
+    got = O.reps_attnscore(K, mass, 4, 2, [0])
+    assert np.array_equal(got[0], K[[1, 3]])
+
+
 CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_eligible_workloads,
           check_mean_exact, check_topnorm_bruteforce, check_dot_exact_mips, check_cosine,
           check_topk_bruteforce, check_topk_ties_and_nan, check_attention_full_causal,
           check_attention_set_by_zero_query, check_attention_properties, check_gqa_is_replicated_mha,
-          check_planted_recall, check_hand_worked_fixture, check_step_cosine_chunks]
+          check_planted_recall, check_hand_worked_fixture, check_step_cosine_chunks,
+          check_weights_and_lse_library, check_window_mass_zero_query, check_window_mass_conservation_and_range,
+          check_reps_attnscore_bruteforce]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -578,7 +670,47 @@ def _mut_kv_head_mod(h, Hq, Hkv):
     return h % Hkv
 
 
+def _mut_weights_no_causal(Q, K, T, scale):
+    n, N = Q.shape[0], K.shape[0]
+    P = np.zeros((n, N))
+    for j in range(n):
+        z = scale * (K[T] @ Q[j])
+        w = np.exp(z - z.max())
+        P[j, T] = w / w.sum()
+    return P
+
+
+def _mut_lse_log2(Q, K, T, scale):
+    return _orig_lse(Q, K, T, scale) / math.log(2.0)
+
+
+def _mut_mass_no_window(Qg, K, T, scale, W):
+    return _orig_mass(Qg, K, T, scale, K.shape[0])
+
+
+def _mut_mass_mean_heads(Qg, K, T, scale, W):
+    return _orig_mass(Qg, K, T, scale, W) / Qg.shape[0]
+
+
+def _mut_reps_attn_tie_high(K, mass, B, R, blocks):
+    out = np.empty((len(blocks), R, K.shape[1]))
+    for i, b in enumerate(blocks):
+        order = sorted(range(b * B, (b + 1) * B), key=lambda t: (-mass[t], -t))
+        out[i] = K[order[:R]]
+    return out
+
+
+def _mut_reps_attn_smallest(K, mass, B, R, blocks):
+    out = np.empty((len(blocks), R, K.shape[1]))
+    for i, b in enumerate(blocks):
+        order = sorted(range(b * B, (b + 1) * B), key=lambda t: (mass[t], t))
+        out[i] = K[order[:R]]
+    return out
+
+
 _orig_attention = O.attention
+_orig_lse = O.attention_lse
+_orig_mass = O.window_mass
 
 MUTANTS = [
     ("round_to_dtype", _mut_round_trunc),
@@ -601,6 +733,12 @@ MUTANTS = [
     ("attention", _mut_attention_transposed),
     ("attention", _mut_attention_query_first),
     ("kv_head_of", _mut_kv_head_mod),
+    ("attention_weights", _mut_weights_no_causal),
+    ("attention_lse", _mut_lse_log2),
+    ("window_mass", _mut_mass_no_window),
+    ("window_mass", _mut_mass_mean_heads),
+    ("reps_attnscore", _mut_reps_attn_tie_high),
+    ("reps_attnscore", _mut_reps_attn_smallest),
 ]
 
 
