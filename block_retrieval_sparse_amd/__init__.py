@@ -113,8 +113,10 @@ class KVMemory:
 
     def retrieval_attention(self, q: torch.Tensor, idx: torch.Tensor | None, n_sink: int, window: int,
                             scale: float | None = None, out: torch.Tensor | None = None,
-                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        """q ``[batch][Hq][n_q][d]``, idx ``[batch][1 or Hq][k]`` int32 -> fp32 ``[batch][Hq][n_q][d]``."""
+                            workspace: torch.Tensor | None = None, stream=None,
+                            lse: torch.Tensor | None = None) -> torch.Tensor:
+        """q ``[batch][Hq][n_q][d]``, idx ``[batch][1 or Hq][k]`` int32 -> fp32 ``[batch][Hq][n_q][d]``;
+        lse, if given, ``[batch][Hq][n_q]`` fp32 receives each query's log-sum-exp."""
         q = q.contiguous()
         bt, hq, n_q, d = q.shape
         if idx is None:
@@ -129,9 +131,29 @@ class KVMemory:
         if out is None:
             out = torch.empty((bt, hq, n_q, d), dtype=torch.float32, device=q.device)
         check(lib.brs_retrieval_attention(self.desc, q.data_ptr(), hq, n_q, iptr, idx_heads, k, n_sink, window,
-                                          scale, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                          _stream(stream)))
+                                          scale, out.data_ptr(), _ptr(lse), workspace.data_ptr(),
+                                          workspace.numel(), _stream(stream)))
         return out
+
+    def window_mass(self, q: torch.Tensor, lse: torch.Tensor, window: int, mass: torch.Tensor,
+                    scale: float | None = None, stream=None) -> torch.Tensor:
+        """Add the softmax weight every window token received from q (``[batch][Hq][n_q][d]``, with the
+        log-sum-exp ``lse`` its attention call wrote) to ``mass`` ``[batch][n_kv_heads][capacity]`` fp32."""
+        q = q.contiguous()
+        bt, hq, n_q, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        check(lib.brs_window_mass(self.desc, q.data_ptr(), hq, n_q, lse.data_ptr(), window, scale, mass.data_ptr(),
+                                  _stream(stream)))
+        return mass
+
+    def new_mass(self) -> torch.Tensor:
+        """A zeroed attention-mass buffer ``[batch][n_kv_heads][capacity]`` fp32."""
+        return torch.zeros((self.batch, self.n_kv_heads, self.k.shape[2]), dtype=torch.float32,
+                           device=self.k.device)
+
+    def reps_from_mass(self, mass: torch.Tensor, b0: int, b1: int, stream=None) -> None:
+        """Build the representatives of blocks [b0, b1) from the accumulated mass (attnscore memories)."""
+        check(lib.brs_reps_from_mass(self.desc, mass.data_ptr(), b0, b1, _stream(stream)))
 
 
 def select_topk(scores: torch.Tensor, lo: int, hi: int, k: int, want_vals: bool = True, stream=None):

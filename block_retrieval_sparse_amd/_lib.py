@@ -13,15 +13,17 @@ from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 LIB_PATH = os.environ.get("BRS_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbrs.so")
 
 BRS_F32, BRS_BF16 = 0, 1
-REP_MEAN, REP_TOPNORM, REP_GIVEN, REP_EMBED = 0, 1, 2, 3
-REP_MODES = {"mean": REP_MEAN, "topnorm": REP_TOPNORM, "given": REP_GIVEN, "embed": REP_EMBED}
+REP_MEAN, REP_TOPNORM, REP_GIVEN, REP_EMBED, REP_ATTNSCORE = 0, 1, 2, 3, 4
+REP_MODES = {"mean": REP_MEAN, "topnorm": REP_TOPNORM, "given": REP_GIVEN, "embed": REP_EMBED,
+             "attnscore": REP_ATTNSCORE}
 ERRORS = {0: "BRS_OK", -1: "BRS_E_INVAL", -2: "BRS_E_CAPACITY", -3: "BRS_E_UNSUPPORTED",
           -4: "BRS_E_HIP", -5: "BRS_E_EMPTY", -6: "BRS_E_WORKSPACE"}
 
 # every symbol include/brs.h declares
 EXPORTS = ["brs_version", "brs_last_error", "brs_memory_check", "brs_mem_append", "brs_eligible_range",
            "brs_score_blocks", "brs_select_topk", "brs_attention_workspace_bytes",
-           "brs_retrieval_attention", "brs_retrieval_step", "brs_profile_next_attention"]
+           "brs_retrieval_attention", "brs_retrieval_step", "brs_window_mass", "brs_reps_from_mass",
+           "brs_profile_next_attention"]
 
 
 class brs_memory(ctypes.Structure):
@@ -57,10 +59,14 @@ def _load():
         "brs_attention_workspace_bytes": (c_int, [P, c_int32, c_int32, c_int32, c_int32, c_int64, c_int64,
                                                   POINTER(c_size_t)]),
         "brs_retrieval_attention": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
-                                            c_int64, c_int64, c_float, c_void_p, c_void_p, c_size_t,
+                                            c_int64, c_int64, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                             c_void_p]),
         "brs_retrieval_step": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int64, c_int64, c_float,
-                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                       c_void_p]),
+        "brs_window_mass": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int64, c_float, c_void_p,
+                                    c_void_p]),
+        "brs_reps_from_mass": (c_int, [P, c_void_p, c_int64, c_int64, c_void_p]),
         "brs_profile_next_attention": (c_int, [c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():

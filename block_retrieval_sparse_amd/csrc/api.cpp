@@ -37,7 +37,7 @@ int check_memory(const brs_memory* m) {
   if (m->dtype != BRS_F32 && m->dtype != BRS_BF16) return fail(BRS_E_INVAL, "dtype %d", m->dtype);
   if (m->rep_dtype != BRS_F32 && m->rep_dtype != BRS_BF16)
     return fail(BRS_E_INVAL, "rep_dtype %d", m->rep_dtype);
-  if (m->rep_mode < BRS_REP_MEAN || m->rep_mode > BRS_REP_EMBED)
+  if (m->rep_mode < BRS_REP_MEAN || m->rep_mode > BRS_REP_ATTNSCORE)
     return fail(BRS_E_INVAL, "rep_mode %d", m->rep_mode);
   if (m->reserved != 0) return fail(BRS_E_INVAL, "reserved field must be 0");
   if (m->batch < 1 || m->n_kv_heads < 1 || m->head_dim < 1 || m->block_size < 1 ||
@@ -55,10 +55,11 @@ int check_memory(const brs_memory* m) {
     return fail(BRS_E_INVAL, "rep_dim/rep_dtype must equal head_dim/dtype unless rep_mode is EMBED");
   if ((m->rep_mode == BRS_REP_MEAN || embed) && m->reps_per_block != 1)
     return fail(BRS_E_INVAL, "reps_per_block must be 1 for MEAN and EMBED");
-  if (m->rep_mode == BRS_REP_TOPNORM && (m->reps_per_block > m->block_size || m->reps_per_block > 64))
-    return fail(BRS_E_INVAL, "TOPNORM needs reps_per_block <= min(block_size, 64)");
-  if (m->rep_mode == BRS_REP_TOPNORM && m->block_size > 1024)
-    return fail(BRS_E_UNSUPPORTED, "TOPNORM supports block_size <= 1024");
+  const bool ranked = m->rep_mode == BRS_REP_TOPNORM || m->rep_mode == BRS_REP_ATTNSCORE;
+  if (ranked && (m->reps_per_block > m->block_size || m->reps_per_block > 64))
+    return fail(BRS_E_INVAL, "TOPNORM and ATTNSCORE need reps_per_block <= min(block_size, 64)");
+  if (ranked && m->block_size > 1024)
+    return fail(BRS_E_UNSUPPORTED, "TOPNORM and ATTNSCORE support block_size <= 1024");
   if (!m->k || !m->v || !m->reps) return fail(BRS_E_INVAL, "k, v and reps must be non-NULL");
   if (!aligned(m->k, 16) || !aligned(m->v, 16) || !aligned(m->reps, 16))
     return fail(BRS_E_INVAL, "k, v and reps must be 16-byte aligned");
@@ -126,7 +127,7 @@ int brs_mem_append(brs_memory* m, const void* k_new, const void* v_new, int64_t 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = brs::launch_kv_append(*m, k_new, v_new, n_new, s);
   if (e != hipSuccess) return hip_fail(e, "kv_append");
-  if (b1 > b0) {
+  if (b1 > b0 && m->rep_mode != BRS_REP_ATTNSCORE) {  // ATTNSCORE: built by brs_reps_from_mass
     brs_memory after = *m;
     after.length = m->length + n_new;
     e = brs::launch_rep_build(after, b0, b1, reps_new, s);
@@ -228,7 +229,7 @@ int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_
 
 // plan (unless the split kernels build it themselves), then the attention kernels
 static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void* q, const int32_t* idx,
-                         float* out, void* workspace, hipStream_t s) {
+                         float* out, float* lse, void* workspace, hipStream_t s) {
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   hipError_t e;
@@ -237,20 +238,21 @@ static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void
     if (e != hipSuccess) return hip_fail(e, "attn_plan");
   }
   if (g.prefill) {
-    e = brs::launch_attn_prefill(g, m->k, m->v, q, workspace, out, s, e0, e1);
+    e = brs::launch_attn_prefill(g, m->k, m->v, q, workspace, out, lse, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "attn_prefill");
     return ok();
   }
   e = brs::launch_attn_split(g, m->k, m->v, q, idx, workspace, out, s, e0, e1);
   if (e != hipSuccess) return hip_fail(e, "attn_split");
-  e = brs::launch_attn_merge(g, workspace, out, s);
+  e = brs::launch_attn_merge(g, workspace, out, lse, s);
   if (e != hipSuccess) return hip_fail(e, "attn_merge");
   return ok();
 }
 
 static int check_attention_buffers(const brs::AttnGeom& g, const void* q, const int32_t* idx, int32_t k, float* out,
-                                   void* workspace, size_t workspace_bytes) {
+                                   float* lse, void* workspace, size_t workspace_bytes) {
   if (!q || !out) return fail(BRS_E_INVAL, "q/out must be non-NULL");
+  if (lse && !aligned(lse, 4)) return fail(BRS_E_INVAL, "lse misaligned");
   if (k > 0 && !idx) return fail(BRS_E_INVAL, "idx must be non-NULL when k > 0");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(BRS_E_INVAL, "q/out must be 16-byte aligned");
   if (idx && !aligned(idx, 4)) return fail(BRS_E_INVAL, "idx misaligned");
@@ -262,19 +264,20 @@ static int check_attention_buffers(const brs::AttnGeom& g, const void* q, const 
 
 int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
                             const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
-                            int64_t window, float scale, float* out, void* workspace,
+                            int64_t window, float scale, float* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream) {
   brs::AttnGeom g;
   int rc = attn_setup(m, n_q_heads, n_q, idx_heads, k, n_sink, window, scale, g);
   if (rc) return rc;
-  rc = check_attention_buffers(g, q, idx, k, out, workspace, workspace_bytes);
+  rc = check_attention_buffers(g, q, idx, k, out, lse, workspace, workspace_bytes);
   if (rc) return rc;
-  return run_attention(g, m, q, idx, out, workspace, (hipStream_t)stream);
+  return run_attention(g, m, q, idx, out, lse, workspace, (hipStream_t)stream);
 }
 
 int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const void* qrep,
                        int32_t k, int64_t n_sink, int64_t window, float scale, float* scores, int32_t* idx,
-                       float* vals, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                       float* vals, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   int rc = check_memory(m);
   if (rc) return rc;
   const bool cosine = m->rep_mode == BRS_REP_EMBED;
@@ -285,7 +288,7 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
   brs::AttnGeom g;
   rc = attn_setup(m, n_q_heads, n_q, hs, k, n_sink, window, scale, g);
   if (rc) return rc;
-  rc = check_attention_buffers(g, q, idx, k, out, workspace, workspace_bytes);
+  rc = check_attention_buffers(g, q, idx, k, out, lse, workspace, workspace_bytes);
   if (rc) return rc;
   if (k > 2048) return fail(BRS_E_UNSUPPORTED, "k must be at most 2048");
   if (k > 0) {
@@ -308,14 +311,44 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
       g_prof_start = g_prof_stop = nullptr;
       e = brs::launch_attn_step(g, m->k, m->v, q, scores, stride, lo, hi, idx, vals, workspace, out, s, e0, e1);
       if (e != hipSuccess) return hip_fail(e, "select_topk + attention");
-      e = brs::launch_attn_merge(g, workspace, out, s);
+      e = brs::launch_attn_merge(g, workspace, out, lse, s);
       if (e != hipSuccess) return hip_fail(e, "attn_merge");
       return ok();
     }
     e = brs::launch_select_topk(scores, m->batch, hs, stride, lo, hi, k, idx, vals, s);
     if (e != hipSuccess) return hip_fail(e, "select_topk");
   }
-  return run_attention(g, m, q, k > 0 ? idx : nullptr, out, workspace, s);
+  return run_attention(g, m, q, k > 0 ? idx : nullptr, out, lse, workspace, s);
+}
+
+int brs_window_mass(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const float* lse,
+                    int64_t window, float scale, float* mass, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (n_q_heads < 1 || n_q_heads % m->n_kv_heads != 0)
+    return fail(BRS_E_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q < 1 || n_q > m->length) return fail(BRS_E_INVAL, "need 1 <= n_q <= length");
+  if (window < 1) return fail(BRS_E_INVAL, "window must be >= 1");
+  if (!isfinite(scale)) return fail(BRS_E_INVAL, "scale must be finite");
+  if (!q || !lse || !mass) return fail(BRS_E_INVAL, "q, lse and mass must be non-NULL");
+  if (!aligned(q, brs::elem_bytes(m->dtype)) || !aligned(lse, 4) || !aligned(mass, 4))
+    return fail(BRS_E_INVAL, "misaligned pointer");
+  const int64_t w0 = window < m->length ? m->length - window : 0;
+  hipError_t e = brs::launch_window_mass(*m, q, n_q_heads, n_q, lse, w0, scale, mass, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "window_mass");
+}
+
+int brs_reps_from_mass(const brs_memory* m, const float* mass, int64_t b0, int64_t b1, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (m->rep_mode != BRS_REP_ATTNSCORE) return fail(BRS_E_INVAL, "rep_mode must be ATTNSCORE");
+  const int64_t nb = m->length / m->block_size;
+  if (b0 < 0 || b1 < b0 || b1 > nb)
+    return fail(BRS_E_INVAL, "need 0 <= b0 <= b1 <= %lld (complete blocks)", (long long)nb);
+  if (!mass || !aligned(mass, 4)) return fail(BRS_E_INVAL, "mass must be non-NULL and 4-byte aligned");
+  if (b1 == b0) return ok();
+  hipError_t e = brs::launch_reps_from_mass(*m, mass, b0, b1, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "reps_from_mass");
 }
 
 int brs_profile_next_attention(void* start_event, void* stop_event) {

@@ -406,10 +406,16 @@ __device__ int chunk_plan(const SplitArgs& a, int b, int g, int c, int rg, int4*
 // loads of eight chunks at once and keeps a running log-sum-exp; the runs
 // are combined in increasing slice order (deterministic).
 
+// lse (optional): the row's log-sum-exp of its scaled logits in natural
+// units, ln(2^M * L) with M the log2-domain reference and L the sum.
+__device__ __forceinline__ float row_lse(float M, float L) {
+  return L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+}
+
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict__ hdr, const float2* __restrict__ ml,
-                                                        const float* __restrict__ o, float* __restrict__ out, int hq,
-                                                        int hkv, int n_q, int d, int chunk_tokens, int max_chunks,
-                                                        int used_chunks) {
+                                                        const float* __restrict__ o, float* __restrict__ out,
+                                                        float* __restrict__ lse, int hq, int hkv, int n_q, int d,
+                                                        int chunk_tokens, int max_chunks, int used_chunks) {
   __shared__ float4 s_acc[256];
   __shared__ float2 s_ml[256];
   const int64_t row = blockIdx.x;  // ((b * hq + h) * n_q + i)
@@ -421,7 +427,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict_
   int n_chunks = used_chunks;
   if (chunk_tokens > 0) {
     const int n_tokens = hdr[bg].y;
-    if (n_tokens == 0) return;  // the plan kernel wrote zeros
+    if (n_tokens == 0) {  // the plan kernel wrote zeros
+      if (lse && threadIdx.x == 0) lse[row] = -INFINITY;
+      return;
+    }
     n_chunks = min((n_tokens + chunk_tokens - 1) / chunk_tokens, max_chunks);
   }
   const float2* mlr = ml + row * max_chunks;
@@ -492,6 +501,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict_
       }
       const float inv = L > 0.f ? 1.f / L : 0.f;
       reinterpret_cast<float4*>(out + row * d)[threadIdx.x] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+      if (lse && threadIdx.x == 0) lse[row] = row_lse(M, L);
     }
     return;
   }
@@ -512,6 +522,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int4* __restrict_
     }
     out[row * d + e] = acc;
   }
+  if (lse && threadIdx.x == 0) lse[row] = row_lse(M, L);
 }
 
 // Fast path: D = head_dim, rows 16-byte aligned.  L = D / DPL lanes share a
@@ -1848,11 +1859,11 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s) {
+hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, float* lse, hipStream_t s) {
   const int64_t rows = (int64_t)g.batch * g.hq * g.n_q;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows), dim3(256), 0, s, (const int4*)((char*)ws + g.hdr_off),
-                     (const float2*)((char*)ws + g.ml_off), (const float*)((char*)ws + g.o_off), out, g.hq, g.hkv,
-                     g.n_q, g.d, g.slot ? 0 : g.chunk_tokens, g.max_chunks, g.max_chunks);
+                     (const float2*)((char*)ws + g.ml_off), (const float*)((char*)ws + g.o_off), out, lse, g.hq,
+                     g.hkv, g.n_q, g.d, g.slot ? 0 : g.chunk_tokens, g.max_chunks, g.max_chunks);
   return hipGetLastError();
 }
 

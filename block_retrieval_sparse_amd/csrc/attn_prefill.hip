@@ -58,6 +58,7 @@ struct PrefillArgs {
   const uint16_t* v;
   const uint16_t* q;
   float* out;
+  float* lse;  // per query row, ln of the softmax denominator (may be null)
   const int4* hdr;
   const int4* items;
   int64_t max_items;
@@ -446,6 +447,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     const float f1 = exp2_fast(mref - M), f2 = exp2_fast(m2 - M);
     const float L = lpart * f1 + l2 * f2;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
+    if (a.lse && g4 == 0 && q0 + 16 * qg + n < a.n_q)
+      a.lse[(int64_t)bh * a.n_q + q0 + 16 * qg + n] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
     const float c1 = f1 * inv, c2 = f2 * inv;
     float* orow = a.out + ((int64_t)bh * a.n_q + q0 + 16 * qg) * a.d;
 #pragma unroll
@@ -473,8 +476,9 @@ bool prefill_supported(const AttnGeom& g) {
 }
 
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws, float* out,
-                               hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                               float* lse, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   PrefillArgs a;
+  a.lse = lse;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.q = (const uint16_t*)q;

@@ -125,7 +125,8 @@ hipError_t launch_attn_plan(const AttnGeom& g, const int32_t* idx, void* ws, flo
 
 hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
                              void* ws, float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
-hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, hipStream_t s);
+// lse (may be null): per query row, the natural log of the softmax denominator
+hipError_t launch_attn_merge(const AttnGeom& g, void* ws, float* out, float* lse, hipStream_t s);
 // Whole decode step after scoring in one attention launch, the selection
 // made inside it (slot layout): same partials as launch_attn_split given
 // that selection.
@@ -135,7 +136,7 @@ hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, con
                             hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 // Chunked prefill on the matrix cores (reads the plan's segments from ws).
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
-                               float* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+                               float* out, float* lse, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 bool prefill_supported(const AttnGeom& g);
 
 // ---------------------------------------------------------------------------
@@ -143,6 +144,9 @@ bool prefill_supported(const AttnGeom& g);
 
 hipError_t launch_kv_append(const brs_memory& m, const void* k_new, const void* v_new, int64_t n_new,
                             hipStream_t s);
+hipError_t launch_reps_from_mass(const brs_memory& m, const float* mass, int64_t b0, int64_t b1, hipStream_t s);
+hipError_t launch_window_mass(const brs_memory& m, const void* q, int hq, int n_q, const float* lse, int64_t w0,
+                              float scale, float* mass, hipStream_t s);
 hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new,
                             hipStream_t s);
 hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi,

@@ -71,6 +71,28 @@ __global__ __launch_bounds__(256) void rep_mean_kernel(const T* __restrict__ K, 
 // TOPNORM: the R keys with the largest squared norm (float64 sums), ties to
 // the lower token, copied unchanged in that order.
 
+// Ranks the block's B keys in `key` (largest first, ties to the lower token)
+// and copies the rows of the first R into dst, in rank order.  `chosen`
+// starts as 0..R-1 so every slot names a valid token even for NaN keys.
+template <typename T>
+__device__ void rank_and_copy(const double* key, int* chosen, const T* base, T* dst, int B, int R, int d,
+                              int rs) {
+  for (int t = threadIdx.x; t < B; t += blockDim.x) {
+    const double mine = key[t];
+    int rank = 0;
+    for (int u = 0; u < B; ++u) {
+      const double o = key[u];
+      rank += (o > mine) || (o == mine && u < t);
+    }
+    if (rank < R) chosen[rank] = t;  // ranks are distinct for finite keys
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R * d; i += blockDim.x) {
+    const int r = i / d, c = i - r * d;
+    dst[i] = base[(int64_t)chosen[r] * rs + c];
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rep_topnorm_kernel(const T* __restrict__ K, T* __restrict__ reps,
                                                           int64_t b0, int B, int R, int d, int rs, int64_t cap,
@@ -81,7 +103,7 @@ __global__ __launch_bounds__(256) void rep_topnorm_kernel(const T* __restrict__ 
   const int64_t bg = blockIdx.y;
   const T* base = K + (bg * cap + blk * B) * (int64_t)rs;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  if (threadIdx.x < R) chosen[threadIdx.x] = threadIdx.x;  // every slot names a valid token even for NaN norms
+  if (threadIdx.x < R) chosen[threadIdx.x] = threadIdx.x;
   for (int t = wave; t < B; t += nwaves) {
     double s = 0.0;
     for (int c = lane; c < d; c += 64) {
@@ -92,21 +114,26 @@ __global__ __launch_bounds__(256) void rep_topnorm_kernel(const T* __restrict__ 
     if (lane == 0) n2[t] = s;
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < B; t += blockDim.x) {
-    const double mine = n2[t];
-    int rank = 0;
-    for (int u = 0; u < B; ++u) {
-      const double o = n2[u];
-      rank += (o > mine) || (o == mine && u < t);
-    }
-    if (rank < R) chosen[rank] = t;  // ranks are distinct for finite norms
-  }
+  rank_and_copy(n2, chosen, base, reps + (bg * capB + blk) * (int64_t)R * d, B, R, d, rs);
+}
+
+// ---------------------------------------------------------------------------
+// ATTNSCORE: the R keys with the largest accumulated attention mass (InfLLM
+// "method"), ties to the lower token, copied unchanged in that order.
+
+template <typename T>
+__global__ __launch_bounds__(256) void rep_mass_kernel(const T* __restrict__ K, T* __restrict__ reps,
+                                                       const float* __restrict__ mass, int64_t b0, int B, int R,
+                                                       int d, int rs, int64_t cap, int64_t capB) {
+  __shared__ double key[1024];
+  __shared__ int chosen[64];
+  const int64_t blk = b0 + blockIdx.x;
+  const int64_t bg = blockIdx.y;
+  const T* base = K + (bg * cap + blk * B) * (int64_t)rs;
+  if (threadIdx.x < R) chosen[threadIdx.x] = threadIdx.x;
+  for (int t = threadIdx.x; t < B; t += blockDim.x) key[t] = (double)mass[bg * cap + blk * B + t];
   __syncthreads();
-  T* dst = reps + (bg * capB + blk) * (int64_t)R * d;
-  for (int i = threadIdx.x; i < R * d; i += blockDim.x) {
-    const int r = i / d, c = i - r * d;
-    dst[i] = base[(int64_t)chosen[r] * rs + c];
-  }
+  rank_and_copy(key, chosen, base, reps + (bg * capB + blk) * (int64_t)R * d, B, R, d, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -151,6 +178,25 @@ hipError_t launch_kv_append(const brs_memory& m, const void* k_new, const void* 
                        m.n_kv_heads, n_new, m.capacity, m.length, src_bytes / 2, dst_bytes / 2);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_reps_from_mass(const brs_memory& m, const float* mass, int64_t b0, int64_t b1, hipStream_t s) {
+  const int64_t capB = m.capacity / m.block_size;
+  const int64_t heads = (int64_t)m.batch * m.n_kv_heads;
+  for (int64_t done = 0; done < b1 - b0; done += 65535) {
+    const int64_t n = b1 - b0 - done < 65535 ? b1 - b0 - done : 65535;
+    const dim3 grid((unsigned)n, (unsigned)heads);
+    if (m.dtype == BRS_F32)
+      hipLaunchKernelGGL(rep_mass_kernel<float>, grid, dim3(256), 0, s, (const float*)m.k, (float*)m.reps, mass,
+                         b0 + done, m.block_size, m.reps_per_block, m.head_dim, m.row_stride, m.capacity, capB);
+    else
+      hipLaunchKernelGGL(rep_mass_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)m.k,
+                         (uint16_t*)m.reps, mass, b0 + done, m.block_size, m.reps_per_block, m.head_dim,
+                         m.row_stride, m.capacity, capB);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new, hipStream_t s) {

@@ -10,12 +10,12 @@ import math
 
 import torch
 
-from . import KVMemory, _lib, _stream, check, lib
+from . import KVMemory, _lib, _ptr, _stream, check, lib
 
 
 class RetrievalStep:
     def __init__(self, mem: KVMemory, n_q_heads: int, n_q: int, k: int, n_sink: int, window: int,
-                 scale: float | None = None):
+                 scale: float | None = None, want_lse: bool = False):
         self.mem = mem
         self.n_q_heads, self.n_q, self.k = n_q_heads, n_q, k
         self.n_sink, self.window = n_sink, window
@@ -28,6 +28,8 @@ class RetrievalStep:
         self.idx = torch.full((mem.batch, self.score_heads, k), -1, dtype=torch.int32, device=dev)
         self.vals = torch.empty((mem.batch, self.score_heads, k), dtype=torch.float32, device=dev)
         self.out = torch.empty((mem.batch, n_q_heads, n_q, mem.head_dim), dtype=torch.float32, device=dev)
+        # each query's log-sum-exp (needed to accumulate window attention mass)
+        self.lse = torch.empty((mem.batch, n_q_heads, n_q), dtype=torch.float32, device=dev) if want_lse else None
         nbytes = mem.workspace_bytes(n_q_heads, n_q, self.score_heads, k, n_sink, window)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.lo, self.hi = mem.eligible_range(n_sink, window)
@@ -50,7 +52,8 @@ class RetrievalStep:
         check(lib.brs_retrieval_attention(self.mem.desc, q.data_ptr(), self.n_q_heads, self.n_q,
                                           self.idx.data_ptr() if self.k else None, self.score_heads, self.k,
                                           self.n_sink, self.window, self.scale, self.out.data_ptr(),
-                                          self.workspace.data_ptr(), self.workspace.numel(), _stream(stream)))
+                                          _ptr(self.lse), self.workspace.data_ptr(), self.workspace.numel(),
+                                          _stream(stream)))
         return self.out
 
     def run(self, q: torch.Tensor, qrep: torch.Tensor | None = None, stream=None, profile_events=None):
@@ -67,7 +70,8 @@ class RetrievalStep:
         check(lib.brs_retrieval_step(self.mem.desc, q.data_ptr(), self.n_q_heads, self.n_q, qrep.data_ptr(), self.k,
                                      self.n_sink, self.window, self.scale, self.scores.data_ptr(),
                                      self.idx.data_ptr(), self.vals.data_ptr(), self.out.data_ptr(),
-                                     self.workspace.data_ptr(), self.workspace.numel(), _stream(stream)))
+                                     _ptr(self.lse), self.workspace.data_ptr(), self.workspace.numel(),
+                                     _stream(stream)))
         return self.out
 
     def run_separate(self, q: torch.Tensor, qrep: torch.Tensor | None = None, stream=None, profile_events=None):
@@ -79,3 +83,34 @@ class RetrievalStep:
         self.score(qrep, stream)
         self.select(stream)
         return self.attend(q, stream, profile_events)
+
+
+class AttnScoreMemory:
+    """Decode loop state for attention-score representatives (InfLLM "method":
+    a memory unit is represented by the tokens that received the most
+    attention while they were in the local window).
+
+    After each attention call (made with ``want_lse``), ``accumulate`` adds
+    the window tokens' softmax weights to the mass buffer; ``refresh`` builds
+    the representatives of the blocks that became candidates since the last
+    refresh (their first token left the window), from the mass so far.
+    """
+
+    def __init__(self, mem: KVMemory, n_sink: int, window: int):
+        if mem.rep_mode != "attnscore":
+            raise ValueError("the memory's rep_mode must be 'attnscore'")
+        self.mem, self.n_sink, self.window = mem, n_sink, window
+        self.mass = mem.new_mass()
+        self.built = mem.eligible_range(n_sink, window)[0]  # blocks below lo are never candidates
+
+    def accumulate(self, q: torch.Tensor, lse: torch.Tensor, scale: float | None = None, stream=None) -> None:
+        self.mem.window_mass(q, lse, self.window, self.mass, scale, stream)
+
+    def refresh(self, stream=None) -> tuple[int, int]:
+        """Build the representatives of newly eligible blocks; returns the block range built."""
+        lo, hi = self.mem.eligible_range(self.n_sink, self.window)
+        b0 = max(self.built, lo)
+        if hi > b0:
+            self.mem.reps_from_mass(self.mass, b0, hi, stream)
+        self.built = max(self.built, hi)
+        return b0, max(b0, hi)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BRS_VERSION 1
+#define BRS_VERSION 2
 
 /* Storage types. */
 typedef enum { BRS_F32 = 0, BRS_BF16 = 1 } brs_dtype;
@@ -70,12 +70,21 @@ typedef enum { BRS_F32 = 0, BRS_BF16 = 1 } brs_dtype;
  *   BRS_REP_GIVEN   caller-supplied vectors of head_dim (Landmark keys);
  *   BRS_REP_EMBED   caller-supplied chunk embeddings of rep_dim, one per block
  *                   for the whole sequence (rep_heads = 1), scored by cosine
- *                   (MemLong's retriever embeddings). */
+ *                   (MemLong's retriever embeddings);
+ *   BRS_REP_ATTNSCORE the R keys of the block that received the most
+ *                   attention while they were in the local window (InfLLM
+ *                   "method": representative tokens chosen by their
+ *                   attention scores).  brs_mem_append builds nothing; the
+ *                   caller accumulates the attention with brs_window_mass
+ *                   after each attention call and builds a block's
+ *                   representatives with brs_reps_from_mass when the block
+ *                   becomes a candidate. */
 typedef enum {
   BRS_REP_MEAN = 0,
   BRS_REP_TOPNORM = 1,
   BRS_REP_GIVEN = 2,
-  BRS_REP_EMBED = 3
+  BRS_REP_EMBED = 3,
+  BRS_REP_ATTNSCORE = 4
 } brs_rep_mode;
 
 enum {
@@ -92,10 +101,11 @@ enum {
  * layout is fixed for foreign-function callers.  Constraints (checked by
  * every call): batch, n_kv_heads, head_dim, block_size, reps_per_block,
  * rep_dim >= 1; row_stride >= head_dim; 0 <= length <= capacity;
- * rep_heads = n_kv_heads for MEAN/TOPNORM/GIVEN and 1 for EMBED; rep_dim =
- * head_dim and rep_dtype = dtype unless rep_mode is EMBED; reps_per_block = 1
- * for MEAN and EMBED; row_stride * element size is a multiple of 4 bytes;
- * k, v, reps non-NULL and 16-byte aligned. */
+ * rep_heads = n_kv_heads for MEAN/TOPNORM/GIVEN/ATTNSCORE and 1 for EMBED;
+ * rep_dim = head_dim and rep_dtype = dtype unless rep_mode is EMBED;
+ * reps_per_block = 1 for MEAN and EMBED; reps_per_block <= min(block_size,
+ * 64) for TOPNORM and ATTNSCORE; row_stride * element size is a multiple of 4
+ * bytes; k, v, reps non-NULL and 16-byte aligned. */
 typedef struct brs_memory {
   int32_t dtype;           /* brs_dtype of k, v and the queries            */
   int32_t batch;
@@ -131,7 +141,8 @@ int brs_memory_check(const brs_memory* m);
  *                  append completes, [batch][rep_heads][n_done][R][rep_dim]
  *                  rep_dtype, n_done = (length+n_new)/B - length/B; may be
  *                  NULL when n_done = 0; ignored for MEAN/TOPNORM, whose
- *                  representatives are computed from the stored keys.
+ *                  representatives are computed from the stored keys, and
+ *                  for ATTNSCORE, whose are built by brs_reps_from_mass.
  * On success enqueues the copies and representative builds and sets
  * m->length += n_new (host side).  BRS_E_CAPACITY if length + n_new >
  * capacity.  n_new = 0 is a no-op. */
@@ -204,13 +215,16 @@ int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_
  *          empty at run time (possible only when n_sink = window = 0 and
  *          every idx entry is skipped) gets zeros; when that is certain
  *          from the arguments alone the call returns BRS_E_EMPTY.
+ *   lse  : [batch][n_q_heads][n_q] float32 or NULL: the natural log of each
+ *          query's softmax denominator, log sum_t exp(scale * q.k_t) over
+ *          its attended set (-inf for an empty set).
  *   workspace : device scratch of at least brs_attention_workspace_bytes()
  *          bytes, 256-byte aligned; its contents on entry do not matter.
  * n_q = 1 (decode) runs a split-K flash-decode; n_q > 1 with bf16 runs the
  * matrix-core prefill kernel. */
 int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
                             const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
-                            int64_t window, float scale, float* out, void* workspace,
+                            int64_t window, float scale, float* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
 /* One whole step (score_blocks, select_topk, retrieval_attention) in one
@@ -218,8 +232,8 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
  * identical results to the three calls made in turn, and the same
  * selection semantics (per query head for dot scores, per sequence for
  * cosine).
- *   q, out    : as brs_retrieval_attention (idx_heads = n_q_heads for dot
- *               scores, 1 for cosine);
+ *   q, out, lse : as brs_retrieval_attention (idx_heads = n_q_heads for
+ *               dot scores, 1 for cosine);
  *   qrep      : as brs_score_blocks (unused when k = 0);
  *   scores    : [batch][n_score_heads][capacity / block_size] float32;
  *   idx, vals : [batch][n_score_heads][k] as brs_select_topk (vals may be
@@ -229,8 +243,37 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
  * Errors as the separate calls; nothing is enqueued on error. */
 int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
                        const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
-                       float* scores, int32_t* idx, float* vals, float* out, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       float* scores, int32_t* idx, float* vals, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention mass of the local window (InfLLM "method": the attention scores
+ * each token receives decide which tokens represent its memory unit).  After
+ * an attention call with queries q (same n_q_heads, n_q, scale) that wrote
+ * lse, adds to every token t of the window [length - window, length)
+ *     mass[b][g][t] += sum over the query heads h of kv head g and the
+ *                      queries j that see t of exp(scale * q.k_t - lse)
+ * -- the softmax weight t received, summed over the group's heads and the
+ * call's queries.  Query j sits at position length - n_q + j and sees
+ * positions <= its own (the window is always attended in full).
+ *   q    : [batch][n_q_heads][n_q][head_dim] dtype, 16-byte aligned.
+ *   lse  : [batch][n_q_heads][n_q] float32 from that attention call.
+ *   mass : [batch][n_kv_heads][capacity] float32, caller-owned, zeroed by
+ *          the caller once before the first token; read and written only
+ *          at window tokens.
+ * Weights are float32 (products of stored values summed in float32); a call
+ * adds each token's sum once, in a fixed order (deterministic).  Any rep_mode;
+ * window >= 1; n_q <= length. */
+int brs_window_mass(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const float* lse,
+                    int64_t window, float scale, float* mass, void* stream);
+
+/* Representatives of blocks [b0, b1) from the accumulated mass (ATTNSCORE
+ * memories): the R keys of each block with the largest mass, ties to the
+ * lower token, copied unchanged, largest first, into reps (as TOPNORM does
+ * with norms).  mass as in brs_window_mass; requires 0 <= b0 <= b1 <=
+ * length / block_size.  The reading used by this library: a block's
+ * representatives are built when it becomes a candidate (its first token
+ * leaves the window), from the mass accumulated up to then. */
+int brs_reps_from_mass(const brs_memory* m, const float* mass, int64_t b0, int64_t b1, void* stream);
 
 /* Measurement hook: the next brs_retrieval_attention call on this thread
  * records `start_event` and `stop_event` (hipEvent_t, passed as void*) at the

@@ -33,7 +33,7 @@ class Workload:
     n_tokens: int              # tokens in memory when the step runs
     block: int                 # tokens per block
     reps_per_block: int
-    rep_mode: str              # "mean" | "topnorm" | "given" | "embed"
+    rep_mode: str              # "mean" | "topnorm" | "given" | "embed" | "attnscore"
     rep_dim: int
     k: int                     # blocks retrieved per score head
     window: int                # local window, last tokens of memory

@@ -35,7 +35,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version(L):
-    assert L.lib.brs_version() == 1
+    assert L.lib.brs_version() == 2
 
 
 def desc(L, **kw):
@@ -109,13 +109,13 @@ def test_score_select_attention_reject(L):
     assert n.value > 0
     assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 0, 0, 0, ctypes.byref(n)) == -5
     assert L.lib.brs_attention_workspace_bytes(m, 7, 1, 7, 4, 0, 0, ctypes.byref(n)) == -1
-    args = dict(q=0x1000, hq=8, nq=1, idx=0x2000, ih=8, k=32, S=128, Wn=1024, sc=0.1, out=0x3000)
+    args = dict(q=0x1000, hq=8, nq=1, idx=0x2000, ih=8, k=32, S=128, Wn=1024, sc=0.1, out=0x3000, lse=None)
 
     def call(ws_ptr=0x100000, ws_bytes=ws, **kw):
         a = dict(args)
         a.update(kw)
         return L.lib.brs_retrieval_attention(m, a["q"], a["hq"], a["nq"], a["idx"], a["ih"], a["k"], a["S"],
-                                             a["Wn"], a["sc"], a["out"], ws_ptr, ws_bytes, None)
+                                             a["Wn"], a["sc"], a["out"], a["lse"], ws_ptr, ws_bytes, None)
 
     assert call(hq=7) == -1
     assert call(ih=3) == -1
@@ -126,6 +126,7 @@ def test_score_select_attention_reject(L):
     assert call(sc=float("inf")) == -1
     assert call(idx=None) == -1
     assert call(q=0x1004) == -1
+    assert call(lse=0x7002) == -1                 # misaligned
 
 
 def test_retrieval_step_rejects_before_device_work(L):
@@ -134,13 +135,14 @@ def test_retrieval_step_rejects_before_device_work(L):
     assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 32, 128, 1024, ctypes.byref(n)) == 0
     ws = n.value
     args = dict(q=0x1000, hq=8, nq=1, qrep=0x4000, k=32, S=128, Wn=1024, sc=0.1, scores=0x40000, idx=0x2000,
-                vals=0x6000, out=0x3000)
+                vals=0x6000, out=0x3000, lse=None)
 
     def call(ws_ptr=0x100000, ws_bytes=ws, mem=m, **kw):
         a = dict(args)
         a.update(kw)
         return L.lib.brs_retrieval_step(mem, a["q"], a["hq"], a["nq"], a["qrep"], a["k"], a["S"], a["Wn"],
-                                        a["sc"], a["scores"], a["idx"], a["vals"], a["out"], ws_ptr, ws_bytes, None)
+                                        a["sc"], a["scores"], a["idx"], a["vals"], a["out"], a["lse"], ws_ptr,
+                                        ws_bytes, None)
 
     assert call(hq=7) == -1                       # not a multiple of the kv heads
     assert call(nq=5000) == -1
@@ -158,3 +160,25 @@ def test_retrieval_step_rejects_before_device_work(L):
     e = desc(L, rep_mode=L.REP_EMBED, rep_heads=1, rep_dim=768)
     assert L.lib.brs_attention_workspace_bytes(e, 8, 1, 1, 32, 128, 1024, ctypes.byref(n)) == 0
     assert call(mem=e, ws_bytes=n.value, qrep=0x4001) == -1   # cosine query misaligned
+
+
+def test_window_mass_and_reps_from_mass_reject_before_device_work(L):
+    m = desc(L)
+    wm = L.lib.brs_window_mass
+    assert wm(m, 0x1000, 8, 1, 0x2000, 0, 0.1, 0x3000, None) == -1          # window < 1
+    assert wm(m, 0x1000, 7, 1, 0x2000, 64, 0.1, 0x3000, None) == -1         # heads not a multiple of kv heads
+    assert wm(m, 0x1000, 8, 0, 0x2000, 64, 0.1, 0x3000, None) == -1         # n_q < 1
+    assert wm(m, None, 8, 1, 0x2000, 64, 0.1, 0x3000, None) == -1
+    assert wm(m, 0x1000, 8, 1, None, 64, 0.1, 0x3000, None) == -1
+    assert wm(m, 0x1000, 8, 1, 0x2000, 64, 0.1, 0x3002, None) == -1         # misaligned mass
+    assert wm(m, 0x1000, 8, 1, 0x2000, 64, float("nan"), 0x3000, None) == -1
+    rf = L.lib.brs_reps_from_mass
+    assert rf(m, 0x3000, 0, 1, None) == -1                                  # not an ATTNSCORE memory
+    a = desc(L, rep_mode=L.REP_ATTNSCORE, reps_per_block=4)
+    assert L.lib.brs_memory_check(a) == 0
+    nb = a.length // a.block_size
+    assert rf(a, 0x3000, 0, nb + 1, None) == -1                             # past the complete blocks
+    assert rf(a, 0x3000, 3, 2, None) == -1
+    assert rf(a, None, 0, 1, None) == -1
+    assert rf(a, 0x3000, 2, 2, None) == 0                                   # empty range: nothing to do
+    assert L.lib.brs_memory_check(desc(L, rep_mode=L.REP_ATTNSCORE, reps_per_block=65)) == -1
