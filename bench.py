@@ -150,6 +150,11 @@ def build_layers(w, n_layers, dev):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         mem.append(x["k"], x["v"], given)
+        if w.rep_mode == "attnscore":
+            # no attention history before the first step: every candidate's
+            # representatives come from a zero mass (its first R tokens)
+            lo, hi = mem.eligible_range(w.sinks, w.window)
+            mem.reps_from_mass(mem.new_mass(), lo, hi)
         torch.cuda.synchronize()
         t_build += time.perf_counter() - t0
         built_bytes += 2 * x["k"].numel() * x["k"].element_size()
@@ -218,6 +223,7 @@ def cpu_baseline(w, layer0, budget_s: float, cache_bytes: float = 4e9) -> dict:
     ``budget_s`` seconds of oracle work are done.  Converting a (batch, kv
     head) slice to float64 and building its representatives are untimed; up
     to ``cache_bytes`` of converted slices are kept for later cycles."""
+    import numpy as np
     import torch
 
     import oracle.brs_oracle as O
@@ -238,6 +244,10 @@ def cpu_baseline(w, layer0, budget_s: float, cache_bytes: float = 4e9) -> dict:
         if w.rep_mode in ("given", "embed"):
             src = x["given_reps"] if w.rep_mode == "given" else x["embeds"]
             reps = f(src[b0:b0 + 1, :1] if w.rep_mode == "embed" else src[b0:b0 + 1, g0:g0 + 1])
+        elif w.rep_mode == "attnscore":  # zero mass before the first step, as the GPU side builds them
+            nb = K.shape[2] // w.block
+            reps = O.reps_attnscore(K[0, 0], np.zeros(K.shape[2]), w.block, w.reps_per_block,
+                                    list(range(nb)))[None, None]
         else:
             reps = O.build_reps(K[0, 0], w.rep_mode, w.block, w.reps_per_block, w.dtype)[None, None]
         rq = f(x["rq"]).reshape(w.batch, -1)[b0:b0 + 1] if w.rep_mode == "embed" else None
@@ -348,6 +358,48 @@ def run(args):
         stage["select"] += ev[4 * i + 1].elapsed_time(ev[4 * i + 2]) / n_c
         stage["attend"] += ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) / n_c
 
+    # pass D: attention-score representatives (InfLLM "method"): the window
+    # mass of one call, and one block's representatives from the mass
+    mass_res = None
+    if w.rep_mode != "embed":
+        from block_retrieval_sparse_amd.pipeline import RetrievalStep
+
+        n_d = min(args.steps, 50)
+        mem0, st0, keep0 = layers[0]
+        st_l = RetrievalStep(mem0, w.n_q_heads, w.n_q, w.k, w.sinks, w.window, want_lse=True)
+        mass = mem0.new_mass()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_d)]
+        kev = [(he.create(), he.create()) for _ in range(n_d)]
+        b_last = mem0.n_blocks - 1
+        for i in range(n_d):
+            st_l.run(keep0["q"], keep0["qrep"])
+            _lib.check(_lib.lib.brs_profile_next_attention(kev[i][0], kev[i][1]))  # the mass kernel's own events
+            mem0.window_mass(keep0["q"], st_l.lse, w.window, mass)
+            if w.rep_mode == "attnscore":
+                torch.cuda.synchronize()
+                ev[2 * i].record()
+                mem0.reps_from_mass(mass, b_last, b_last + 1)
+                ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        wm_us = sum(he.elapsed_ms(a_, b_) for (a_, b_) in kev) / n_d * 1e3
+        for a_, b_ in kev:
+            he.destroy(a_)
+            he.destroy(b_)
+        W_eff = min(w.window, w.n_tokens)
+        es_ = 4 if w.dtype == "f32" else 2
+        wm_bytes = w.batch * w.n_kv_heads * W_eff * (w.head_dim * es_ + 8) + \
+            w.batch * w.n_q_heads * w.n_q * (w.head_dim * es_ + 4)
+        mass_res = {"window_mass_us": wm_us, "window_mass_bytes": wm_bytes,
+                    "window_mass_GB/s": wm_bytes / (wm_us * 1e-6) / 1e9,
+                    "window_mass_frac": wm_bytes / (wm_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "note": "HIP events attached to the brs_window_mass kernel launch (after an attention call "
+                            "with lse); bytes = window K rows + mass read/write + queries + lse"}
+        if w.rep_mode == "attnscore":
+            mass_res["reps_from_mass_us"] = sum(ev[2 * i].elapsed_time(ev[2 * i + 1])
+                                                for i in range(n_d)) / n_d * 1e3
+            mass_res["reps_from_mass_note"] = "one block per call, events around the call after a synchronize"
+        del st_l, mass
+
     split_bytes = avg["kv"] + avg["q"]
     cfg = {"workload": w.name, "batch": w.batch, "context_tokens": w.n_tokens, "q_heads": w.n_q_heads,
            "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block, "reps_per_block": w.reps_per_block,
@@ -392,6 +444,7 @@ def run(args):
                      "frac": avg["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, "parts": avg},
         "stage_us": {k: v * 1e3 for k, v in stage.items()},
         "append_build": {"bytes": built_bytes, "s": t_build, "GB/s": built_bytes / max(t_build, 1e-9) / 1e9},
+        "attnscore_reps": mass_res,
         "lib_version": _lib.lib.brs_version(),
     })
     if not args.no_cpu_baseline:

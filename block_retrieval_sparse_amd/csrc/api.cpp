@@ -334,7 +334,9 @@ int brs_window_mass(const brs_memory* m, const void* q, int32_t n_q_heads, int32
   if (!aligned(q, brs::elem_bytes(m->dtype)) || !aligned(lse, 4) || !aligned(mass, 4))
     return fail(BRS_E_INVAL, "misaligned pointer");
   const int64_t w0 = window < m->length ? m->length - window : 0;
-  hipError_t e = brs::launch_window_mass(*m, q, n_q_heads, n_q, lse, w0, scale, mass, (hipStream_t)stream);
+  hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  hipError_t e = brs::launch_window_mass(*m, q, n_q_heads, n_q, lse, w0, scale, mass, (hipStream_t)stream, e0, e1);
   return e == hipSuccess ? ok() : hip_fail(e, "window_mass");
 }
 

@@ -146,7 +146,8 @@ hipError_t launch_kv_append(const brs_memory& m, const void* k_new, const void* 
                             hipStream_t s);
 hipError_t launch_reps_from_mass(const brs_memory& m, const float* mass, int64_t b0, int64_t b1, hipStream_t s);
 hipError_t launch_window_mass(const brs_memory& m, const void* q, int hq, int n_q, const float* lse, int64_t w0,
-                              float scale, float* mass, hipStream_t s);
+                              float scale, float* mass, hipStream_t s, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
 hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new,
                             hipStream_t s);
 hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi,

@@ -275,10 +275,11 @@ int brs_window_mass(const brs_memory* m, const void* q, int32_t n_q_heads, int32
  * leaves the window), from the mass accumulated up to then. */
 int brs_reps_from_mass(const brs_memory* m, const float* mass, int64_t b0, int64_t b1, void* stream);
 
-/* Measurement hook: the next brs_retrieval_attention call on this thread
- * records `start_event` and `stop_event` (hipEvent_t, passed as void*) at the
- * begin and end of its main attention kernel on its stream, then forgets
- * them.  Pass NULLs to cancel. */
+/* Measurement hook: the next brs_retrieval_attention, brs_retrieval_step or
+ * brs_window_mass call on this thread records `start_event` and `stop_event`
+ * (hipEvent_t, passed as void*) at the begin and end of its main kernel (the
+ * attention kernel; the mass kernel) on its stream, then forgets them.  Pass
+ * NULLs to cancel. */
 int brs_profile_next_attention(void* start_event, void* stop_event);
 
 #ifdef __cplusplus

@@ -1,4 +1,4 @@
-"""Workload table: the five synthetic block-retrieval workloads, by shape only.
+"""Workload table: the synthetic block-retrieval workloads, by shape only.
 
 Each entry names what the workload stands in for on the pages:
 
@@ -14,6 +14,9 @@ Each entry names what the workload stands in for on the pages:
   heads (H = 32, d = 100), 512-token chunks over an 80k-token memory.
 * ``retrievalattn_gqa_decode_1m_b8`` -- RetrievalAttention (method section:
   out-of-distribution queries, a ~2% retrieval budget), batch 8 at 1M tokens.
+* ``infllm_attnscore_decode_128k`` -- the InfLLM shape with representatives
+  chosen by the attention the tokens received in the window (InfLLM method
+  section) instead of by key norm.
 
 No arithmetic of the method lives here; this module only fixes sizes.
 """
@@ -88,6 +91,10 @@ WORKLOADS = {
                  head_dim=128, dtype="bf16", n_tokens=131072, block=128,
                  reps_per_block=4, rep_mode="topnorm", rep_dim=128, k=32,
                  window=4096, sinks=128, planted_per_head=8, seed=1003),
+        Workload("infllm_attnscore_decode_128k", batch=1, n_q_heads=32, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", n_tokens=131072, block=128,
+                 reps_per_block=4, rep_mode="attnscore", rep_dim=128, k=32,
+                 window=4096, sinks=128, planted_per_head=8, seed=1006),
         Workload("memlong_chunk_prefill_80k", batch=1, n_q_heads=32, n_kv_heads=32,
                  head_dim=100, dtype="bf16", n_tokens=81920 + 512, block=512,
                  reps_per_block=1, rep_mode="embed", rep_dim=768, k=5, window=512,
