@@ -38,6 +38,8 @@ softmax attention over the local context plus the selected blocks.
   ``attention_lse``, ``window_mass``, ``reps_attnscore``): InfLLM "method"
   (a memory unit's representative tokens are those that received the most
   attention in earlier attention computations).
+* O8 retrieval counters and pruning (``count_hits``, ``prune_plan``,
+  ``compact``): MemLong section 2.3.2, dynamic memory update.
 
 Readings where the pages are silent (the same list is kept with the design
 notes): attention sinks are the first S tokens; the window is the last W
@@ -52,7 +54,11 @@ position N - n + j; the cosine of a zero vector is 0; a token's attention
 score for choosing representatives is the softmax weight it receives while
 in the local window, summed over the query heads of its kv head and over
 queries; a block's representatives are chosen when the block becomes a
-candidate, from the mass accumulated up to then.
+candidate, from the mass accumulated up to then; a retrieval count is one per
+selection-list entry (per query head for dot scores); pruning makes one
+decision for the whole memory from the counts summed over its rows, with
+10% = floor(nb / 10) blocks, 50% = capacity // 2 tokens, ties evicting the
+older block, and the partial tail block always kept.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against brute force, exact rational arithmetic, closed forms or independent
@@ -303,6 +309,58 @@ def reps_attnscore(K: np.ndarray, mass: np.ndarray, B: int, R: int, blocks) -> n
         order = sorted(toks, key=lambda t: (-mass[t], t))
         out[i] = K[order[:R]]
     return out
+
+
+# ---------------------------------------------------------------------------
+# O8: retrieval counters and pruning (MemLong 2.3.2, dynamic memory update:
+# on overflow keep the newest 10%, drop the oldest 10%, and evict the least
+# retrieved of the middle 80% until half the memory is used)
+
+
+def count_hits(hits: np.ndarray, idx: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Add one hit per valid entry of a selection list idx [k] to hits [n_blocks] (a copy is returned)."""
+    out = hits.copy()
+    for b in idx:
+        b = int(b)
+        if 0 <= b < n_blocks:
+            out[b] += 1
+    return out
+
+
+def prune_plan(n_tokens: int, B: int, capacity: int, hits: np.ndarray) -> np.ndarray:
+    """New block index of every complete block after pruning, -1 if evicted: [nb].
+
+    nb = n_tokens // B complete blocks; the partial tail block is always kept,
+    after them.  The oldest floor(nb / 10) blocks are dropped and the newest
+    floor(nb / 10) kept; the middle blocks are evicted in order of (hits
+    ascending, block index ascending) until the kept tokens (tail included)
+    fit in capacity // 2, or no middle block is left.  Kept blocks keep their
+    order.  ``hits`` [nb] are the retrieval counts summed over every row of
+    the memory (one decision for the whole memory).
+    """
+    nb = n_tokens // B
+    tail = n_tokens - nb * B
+    n10 = nb // 10
+    mid = list(range(n10, nb - n10))
+    budget = max((capacity // 2 - tail) // B, 0)  # blocks that fit in half the memory
+    keep_mid = max(min(len(mid), budget - n10), 0)
+    order = sorted(mid, key=lambda b: (int(hits[b]), b))
+    evicted = set(order[: len(mid) - keep_mid]) | set(range(n10))
+    new = np.full(nb, -1, dtype=np.int64)
+    j = 0
+    for b in range(nb):
+        if b not in evicted:
+            new[b] = j
+            j += 1
+    return new
+
+
+def compact(K: np.ndarray, plan: np.ndarray, B: int, n_tokens: int) -> np.ndarray:
+    """Token rows [N'][...] after pruning: kept blocks in order, then the tail."""
+    nb = n_tokens // B
+    rows = [K[b * B:(b + 1) * B] for b in range(nb) if plan[b] >= 0]
+    rows.append(K[nb * B:n_tokens])
+    return np.concatenate(rows, axis=0)
 
 
 # ---------------------------------------------------------------------------

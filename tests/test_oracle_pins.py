@@ -474,13 +474,78 @@ def check_reps_attnscore_bruteforce():
     assert np.array_equal(got[0], K[[1, 3]])
 
 
+def check_count_hits_bincount():
+    """Counts equal numpy's bincount over the valid entries (-1 and out-of-range skipped)."""
+    rng = np.random.default_rng(21)
+    for _ in range(20):
+        nb = int(rng.integers(1, 40))
+        h0 = rng.integers(0, 5, size=nb)
+        idx = rng.integers(-3, nb + 3, size=int(rng.integers(0, 12)))
+        got = O.count_hits(h0, idx, nb)
+        ok = idx[(idx >= 0) & (idx < nb)]
+        assert np.array_equal(got, h0 + np.bincount(ok, minlength=nb))
+
+
+def _prune_case(rng):
+    B = int(rng.integers(1, 9))
+    nb = int(rng.integers(0, 60))
+    tail = int(rng.integers(0, B))
+    cap = int(rng.integers(nb * B + tail, 2 * (nb * B + tail) + 2 * B + 1))
+    hits = rng.integers(0, 4, size=nb)
+    return B, nb, tail, cap, hits
+
+
+def check_prune_characterisation():
+    """Oldest tenth gone, newest tenth kept, order kept, half the memory (or no middle left),
+    and every evicted middle block ranks at or below every kept one by (hits, index)."""
+    rng = np.random.default_rng(33)
+    for _ in range(300):
+        B, nb, tail, cap, hits = _prune_case(rng)
+        plan = O.prune_plan(nb * B + tail, B, cap, hits)
+        n10 = nb // 10
+        assert (plan[:n10] == -1).all()
+        assert (plan[nb - n10:] >= 0).all()
+        kept = [b for b in range(nb) if plan[b] >= 0]
+        assert [int(plan[b]) for b in kept] == list(range(len(kept)))
+        mid = list(range(n10, nb - n10))
+        kmid = [b for b in mid if plan[b] >= 0]
+        emid = [b for b in mid if plan[b] < 0]
+        if emid:
+            assert len(kept) * B + tail <= cap // 2
+            # one block fewer evicted would not fit
+            assert (len(kept) + 1) * B + tail > cap // 2
+        if kmid:
+            assert (len(kept) * B + tail <= cap // 2) or not emid
+        for e in emid:
+            for k in kmid:
+                assert (hits[e], e) < (hits[k], k)
+
+
+def check_prune_equal_hits_and_tail():
+    """Equal counts evict the oldest middle blocks first; the tail moves behind the kept blocks."""
+    B, nb, tail, cap = 4, 40, 3, 200
+    N = nb * B + tail
+    plan = O.prune_plan(N, B, cap, np.zeros(nb, dtype=int))
+    budget = (cap // 2 - tail) // B  # 24 blocks
+    first = nb - budget
+    assert (plan[:first] == -1).all() and list(plan[first:]) == list(range(budget))
+    K = np.arange(N * 2, dtype=float).reshape(N, 2)
+    assert np.array_equal(O.compact(K, plan, B, N), K[first * B:])
+    # a hit on an old middle block saves it ahead of newer ones without hits
+    hits = np.zeros(nb, dtype=int)
+    hits[5] = 1
+    plan2 = O.prune_plan(N, B, cap, hits)
+    assert plan2[5] == 0 and plan2[first] == -1 and (plan2[first + 1:] >= 0).all()
+
+
 CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_eligible_workloads,
           check_mean_exact, check_topnorm_bruteforce, check_dot_exact_mips, check_cosine,
           check_topk_bruteforce, check_topk_ties_and_nan, check_attention_full_causal,
           check_attention_set_by_zero_query, check_attention_properties, check_gqa_is_replicated_mha,
           check_planted_recall, check_hand_worked_fixture, check_step_cosine_chunks,
           check_weights_and_lse_library, check_window_mass_zero_query, check_window_mass_conservation_and_range,
-          check_reps_attnscore_bruteforce]
+          check_reps_attnscore_bruteforce, check_count_hits_bincount, check_prune_characterisation,
+          check_prune_equal_hits_and_tail]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -708,9 +773,47 @@ def _mut_reps_attn_smallest(K, mass, B, R, blocks):
     return out
 
 
+def _mut_hits_count_invalid(hits, idx, n_blocks):
+    out = hits.copy()
+    for b in idx:
+        out[int(b) % n_blocks] += 1
+    return out
+
+
+def _mut_prune_tie_newer(n_tokens, B, capacity, hits):
+    return _orig_prune(n_tokens, B, capacity, hits, key=lambda b: (int(hits[b]), -b))
+
+
+def _mut_prune_most_hits(n_tokens, B, capacity, hits):
+    return _orig_prune(n_tokens, B, capacity, hits, key=lambda b: (-int(hits[b]), b))
+
+
+def _mut_prune_no_tail(n_tokens, B, capacity, hits):
+    return _orig_prune((n_tokens // B) * B, B, capacity, hits)
+
+
 _orig_attention = O.attention
 _orig_lse = O.attention_lse
 _orig_mass = O.window_mass
+
+
+def _orig_prune(n_tokens, B, capacity, hits, key=None):
+    # the oracle's plan with its eviction order replaced (for the planted mistakes)
+    nb = n_tokens // B
+    tail = n_tokens - nb * B
+    n10 = nb // 10
+    mid = list(range(n10, nb - n10))
+    budget = max((capacity // 2 - tail) // B, 0)
+    keep_mid = max(min(len(mid), budget - n10), 0)
+    order = sorted(mid, key=key or (lambda b: (int(hits[b]), b)))
+    evicted = set(order[: len(mid) - keep_mid]) | set(range(n10))
+    new = np.full(nb, -1, dtype=np.int64)
+    j = 0
+    for b in range(nb):
+        if b not in evicted:
+            new[b] = j
+            j += 1
+    return new
 
 MUTANTS = [
     ("round_to_dtype", _mut_round_trunc),
@@ -739,6 +842,10 @@ MUTANTS = [
     ("window_mass", _mut_mass_mean_heads),
     ("reps_attnscore", _mut_reps_attn_tie_high),
     ("reps_attnscore", _mut_reps_attn_smallest),
+    ("count_hits", _mut_hits_count_invalid),
+    ("prune_plan", _mut_prune_tie_newer),
+    ("prune_plan", _mut_prune_most_hits),
+    ("prune_plan", _mut_prune_no_tail),
 ]
 
 
