@@ -151,6 +151,34 @@ class KVMemory:
         return torch.zeros((self.batch, self.n_kv_heads, self.k.shape[2]), dtype=torch.float32,
                            device=self.k.device)
 
+    def new_hits(self) -> torch.Tensor:
+        """A zeroed retrieval-count buffer ``[batch][capacity // block]`` int32."""
+        return torch.zeros((self.batch, self.blocks_stride), dtype=torch.int32, device=self.k.device)
+
+    def count_hits(self, idx: torch.Tensor, hits: torch.Tensor, stream=None) -> torch.Tensor:
+        """Add one to ``hits`` for every valid entry of the selection ``idx`` ``[batch][heads][k]``."""
+        idx = idx.contiguous()
+        check(lib.brs_count_hits(self.desc, idx.data_ptr(), idx.shape[1], idx.shape[2], hits.data_ptr(),
+                                 _stream(stream)))
+        return hits
+
+    def like(self) -> "KVMemory":
+        """An empty memory with this one's geometry and buffers of its own."""
+        d = self.desc
+        return KVMemory(d.batch, d.n_kv_heads, d.head_dim, d.capacity, d.block_size, dtype=self.dtype,
+                        rep_mode=self.rep_mode, reps_per_block=d.reps_per_block, rep_dim=d.rep_dim,
+                        rep_dtype=self.reps.dtype, row_stride=d.row_stride, device=self.k.device)
+
+    def prune_into(self, hits: torch.Tensor, dst: "KVMemory", dst_hits: torch.Tensor | None = None,
+                   plan: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Copy what survives pruning into ``dst`` (see brs_mem_prune); returns the plan (new block
+        index per old complete block, -1 if evicted)."""
+        if plan is None:
+            plan = torch.empty(self.blocks_stride, dtype=torch.int32, device=self.k.device)
+        check(lib.brs_mem_prune(self.desc, hits.data_ptr(), dst.desc, _ptr(dst_hits), plan.data_ptr(),
+                                _stream(stream)))
+        return plan
+
     def reps_from_mass(self, mass: torch.Tensor, b0: int, b1: int, stream=None) -> None:
         """Build the representatives of blocks [b0, b1) from the accumulated mass (attnscore memories)."""
         check(lib.brs_reps_from_mass(self.desc, mass.data_ptr(), b0, b1, _stream(stream)))

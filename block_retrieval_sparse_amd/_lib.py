@@ -23,7 +23,7 @@ ERRORS = {0: "BRS_OK", -1: "BRS_E_INVAL", -2: "BRS_E_CAPACITY", -3: "BRS_E_UNSUP
 EXPORTS = ["brs_version", "brs_last_error", "brs_memory_check", "brs_mem_append", "brs_eligible_range",
            "brs_score_blocks", "brs_select_topk", "brs_attention_workspace_bytes",
            "brs_retrieval_attention", "brs_retrieval_step", "brs_window_mass", "brs_reps_from_mass",
-           "brs_profile_next_attention"]
+           "brs_count_hits", "brs_mem_prune", "brs_profile_next_attention"]
 
 
 class brs_memory(ctypes.Structure):
@@ -67,6 +67,8 @@ def _load():
         "brs_window_mass": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int64, c_float, c_void_p,
                                     c_void_p]),
         "brs_reps_from_mass": (c_int, [P, c_void_p, c_int64, c_int64, c_void_p]),
+        "brs_count_hits": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+        "brs_mem_prune": (c_int, [P, c_void_p, P, c_void_p, c_void_p, c_void_p]),
         "brs_profile_next_attention": (c_int, [c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():

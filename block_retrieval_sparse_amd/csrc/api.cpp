@@ -353,6 +353,55 @@ int brs_reps_from_mass(const brs_memory* m, const float* mass, int64_t b0, int64
   return e == hipSuccess ? ok() : hip_fail(e, "reps_from_mass");
 }
 
+int brs_count_hits(const brs_memory* m, const int32_t* idx, int32_t idx_heads, int32_t k, int32_t* hits,
+                   void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (idx_heads < 1 || k < 0) return fail(BRS_E_INVAL, "need idx_heads >= 1 and k >= 0");
+  if (k == 0) return ok();
+  if (!idx || !hits || !aligned(idx, 4) || !aligned(hits, 4))
+    return fail(BRS_E_INVAL, "idx/hits must be non-NULL and 4-byte aligned");
+  hipError_t e = brs::launch_count_hits(*m, idx, idx_heads, k, hits, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "count_hits");
+}
+
+int brs_mem_prune(const brs_memory* src, const int32_t* hits, brs_memory* dst, int32_t* dst_hits, int32_t* plan,
+                  void* stream) {
+  int rc = check_memory(src);
+  if (rc) return rc;
+  if (!dst) return fail(BRS_E_INVAL, "dst is NULL");
+  brs_memory probe = *dst;
+  probe.length = 0;
+  rc = check_memory(&probe);
+  if (rc) return rc;
+  if (dst->dtype != src->dtype || dst->batch != src->batch || dst->n_kv_heads != src->n_kv_heads ||
+      dst->head_dim != src->head_dim || dst->row_stride != src->row_stride || dst->block_size != src->block_size ||
+      dst->reps_per_block != src->reps_per_block || dst->rep_dim != src->rep_dim ||
+      dst->rep_heads != src->rep_heads || dst->rep_mode != src->rep_mode || dst->rep_dtype != src->rep_dtype ||
+      dst->capacity != src->capacity)
+    return fail(BRS_E_INVAL, "dst must have the geometry of src");
+  if (dst->k == src->k || dst->v == src->v || dst->reps == src->reps)
+    return fail(BRS_E_INVAL, "dst buffers must be distinct from src buffers");
+  if (!hits || !plan || !aligned(hits, 4) || !aligned(plan, 4) || (dst_hits && !aligned(dst_hits, 4)))
+    return fail(BRS_E_INVAL, "hits/plan must be non-NULL and 4-byte aligned");
+  const int64_t B = src->block_size;
+  const int64_t nb = src->length / B, tail = src->length - nb * B;
+  const int64_t n10 = nb / 10, n_mid = nb - 2 * n10;
+  int64_t budget = (src->capacity / 2 - tail) / B;
+  if (budget < 0) budget = 0;
+  int64_t keep_mid = budget - n10;
+  keep_mid = keep_mid < 0 ? 0 : (keep_mid > n_mid ? n_mid : keep_mid);
+  const int64_t n_evict = n_mid - keep_mid;
+  const int64_t kept = nb - n10 - n_evict;
+  if (n_mid > brs::prune_max_middle() || nb > brs::prune_max_blocks())
+    return fail(BRS_E_UNSUPPORTED, "pruning supports up to %d middle blocks", brs::prune_max_middle());
+  hipError_t e = brs::launch_prune(*src, *dst, hits, dst_hits, plan, (int)nb, (int)n10, (int)n_evict, (int)kept,
+                                   (int)tail, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prune");
+  dst->length = kept * B + tail;
+  return ok();
+}
+
 int brs_profile_next_attention(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr))
     return fail(BRS_E_INVAL, "pass both events or neither");

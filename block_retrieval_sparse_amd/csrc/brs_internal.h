@@ -148,6 +148,12 @@ hipError_t launch_reps_from_mass(const brs_memory& m, const float* mass, int64_t
 hipError_t launch_window_mass(const brs_memory& m, const void* q, int hq, int n_q, const float* lse, int64_t w0,
                               float scale, float* mass, hipStream_t s, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr);
+hipError_t launch_count_hits(const brs_memory& m, const int32_t* idx, int idx_heads, int k, int32_t* hits,
+                             hipStream_t s);
+int prune_max_middle();
+int prune_max_blocks();
+hipError_t launch_prune(const brs_memory& src, const brs_memory& dst, const int32_t* hits, int32_t* dst_hits,
+                        int32_t* plan, int nb, int n10, int n_evict, int kept, int tail, hipStream_t s);
 hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new,
                             hipStream_t s);
 hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi,

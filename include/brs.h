@@ -275,6 +275,42 @@ int brs_window_mass(const brs_memory* m, const void* q, int32_t n_q_heads, int32
  * leaves the window), from the mass accumulated up to then. */
 int brs_reps_from_mass(const brs_memory* m, const float* mass, int64_t b0, int64_t b1, void* stream);
 
+/* Retrieval counters (MemLong 2.3.2, dynamic memory update: memory entries
+ * are ranked by how often they are retrieved).  For every entry of
+ * idx [batch][idx_heads][k] (a selection as brs_select_topk writes it)
+ * naming a complete block, adds 1 to hits[b][block]:
+ *   hits : [batch][capacity / block_size] int32, caller-owned, zeroed by the
+ *          caller once; a count per block per sequence, summed over the
+ *          selection lists (one per query head for dot scores).
+ * Entries < 0 or >= length / block_size are skipped.  Integer atomics, so the
+ * result does not depend on their order. */
+int brs_count_hits(const brs_memory* m, const int32_t* idx, int32_t idx_heads, int32_t k, int32_t* hits,
+                   void* stream);
+
+/* Pruning on overflow (MemLong 2.3.2, dynamic memory update): copies what
+ * survives of src into dst, which must have src's geometry (every field but
+ * the pointers and length) and buffers of its own.  With nb = length / B
+ * complete blocks and a partial tail of length - nb*B tokens:
+ *   - the oldest floor(nb / 10) blocks are dropped and the newest floor(nb /
+ *     10) kept;
+ *   - blocks of the middle are evicted in order of (hits summed over the
+ *     batch rows ascending, block index ascending) -- ties evict the older
+ *     block -- until the kept blocks plus the tail fit in capacity / 2
+ *     tokens, or none of the middle is left;
+ *   - kept blocks keep their order; the tail follows them.
+ * One decision is made for the whole memory (every batch row and head keeps
+ * the same blocks, since all rows share one length).
+ *   hits     : [batch][capacity / B] int32 counts of src (brs_count_hits).
+ *   dst_hits : [batch][capacity / B] int32 or NULL: the kept blocks' counts
+ *              at their new indices.
+ *   plan     : [capacity / B] int32 scratch; on completion plan[b] is block
+ *              b's new index, -1 if evicted (b < nb).
+ * K, V, representatives and counts of the kept blocks are copied bit for bit;
+ * dst's rows past its new length are left as they were.  Sets dst->length
+ * (host side) on success.  BRS_E_UNSUPPORTED above 16384 middle blocks. */
+int brs_mem_prune(const brs_memory* src, const int32_t* hits, brs_memory* dst, int32_t* dst_hits, int32_t* plan,
+                  void* stream);
+
 /* Measurement hook: the next brs_retrieval_attention, brs_retrieval_step or
  * brs_window_mass call on this thread records `start_event` and `stop_event`
  * (hipEvent_t, passed as void*) at the begin and end of its main kernel (the

@@ -182,3 +182,21 @@ def test_window_mass_and_reps_from_mass_reject_before_device_work(L):
     assert rf(a, None, 0, 1, None) == -1
     assert rf(a, 0x3000, 2, 2, None) == 0                                   # empty range: nothing to do
     assert L.lib.brs_memory_check(desc(L, rep_mode=L.REP_ATTNSCORE, reps_per_block=65)) == -1
+
+
+def test_count_hits_and_prune_reject_before_device_work(L):
+    m = desc(L)
+    ch = L.lib.brs_count_hits
+    assert ch(m, 0x1000, 0, 4, 0x2000, None) == -1          # idx_heads < 1
+    assert ch(m, 0x1000, 2, -1, 0x2000, None) == -1         # k < 0
+    assert ch(m, 0x1000, 2, 0, 0x2000, None) == 0           # nothing to count
+    assert ch(m, None, 2, 4, 0x2000, None) == -1
+    assert ch(m, 0x1000, 2, 4, 0x2002, None) == -1          # misaligned
+    pr = L.lib.brs_mem_prune
+    d = desc(L, k=0x90000, v=0xa0000, reps=0xb0000)
+    assert pr(m, 0x1000, d, None, None, None) == -1         # no plan buffer
+    assert pr(m, None, d, None, 0x3000, None) == -1         # no counts
+    assert pr(m, 0x1000, desc(L, capacity=8192, k=0x90000, v=0xa0000, reps=0xb0000), None, 0x3000, None) == -1
+    assert pr(m, 0x1000, desc(L, block_size=32, k=0x90000, v=0xa0000, reps=0xb0000), None, 0x3000, None) == -1
+    assert pr(m, 0x1000, desc(L), None, 0x3000, None) == -1  # same buffers
+    assert pr(m, 0x1000, None, None, 0x3000, None) == -1
