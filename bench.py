@@ -400,6 +400,36 @@ def run(args):
             mass_res["reps_from_mass_note"] = "one block per call, events around the call after a synchronize"
         del st_l, mass
 
+    # pass E: pruning on overflow (MemLong dynamic memory update) of layer 0's
+    # memory into a second memory, with seeded random retrieval counts
+    prune_res = None
+    if w.batch * w.n_kv_heads * w.n_tokens * w.stride * (4 if w.dtype == "f32" else 2) * 2 <= 8e9:
+        mem0 = layers[0][0]
+        g_ = torch.Generator(device="cpu").manual_seed(w.seed + 17)
+        hits = mem0.new_hits()
+        hits[:, : mem0.n_blocks] = torch.randint(0, 8, (w.batch, mem0.n_blocks), generator=g_,
+                                                 dtype=torch.int32).to(hits.device)
+        dst = mem0.like()
+        plan = torch.empty(mem0.blocks_stride, dtype=torch.int32, device=hits.device)
+        ts = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mem0.prune_into(hits, dst, plan=plan)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        es_ = 4 if w.dtype == "f32" else 2
+        kept_tokens = dst.length
+        pb = 2 * (w.batch * w.n_kv_heads * kept_tokens * w.stride * es_ * 2)  # K and V, read + write
+        p_us = min(ts) * 1e3
+        prune_res = {"us": p_us, "kept_tokens": kept_tokens, "of_tokens": mem0.length, "bytes": pb,
+                     "GB/s": pb / (p_us * 1e-6) / 1e9, "frac": pb / (p_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "note": "events around brs_mem_prune (plan kernel + copy kernel) after a synchronize, best of 3; "
+                             "bytes = kept K/V rows read and written"}
+        del dst, hits, plan
+
     split_bytes = avg["kv"] + avg["q"]
     cfg = {"workload": w.name, "batch": w.batch, "context_tokens": w.n_tokens, "q_heads": w.n_q_heads,
            "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block": w.block, "reps_per_block": w.reps_per_block,
@@ -445,6 +475,7 @@ def run(args):
         "stage_us": {k: v * 1e3 for k, v in stage.items()},
         "append_build": {"bytes": built_bytes, "s": t_build, "GB/s": built_bytes / max(t_build, 1e-9) / 1e9},
         "attnscore_reps": mass_res,
+        "prune": prune_res,
         "lib_version": _lib.lib.brs_version(),
     })
     if not args.no_cpu_baseline:

@@ -95,6 +95,8 @@ struct PruneArgs {
   int batch, hkv, rep_heads;
 };
 
+// VEC: token rows are whole 16-byte units (row_words % 4 == 0): copy uint4s
+template <bool VEC>
 __global__ __launch_bounds__(256) void prune_copy_kernel(PruneArgs a) {
   const int i = blockIdx.x;  // old block; i == nb is the partial tail
   const int y = blockIdx.y;  // (batch, kv head)
@@ -104,9 +106,21 @@ __global__ __launch_bounds__(256) void prune_copy_kernel(PruneArgs a) {
   const int64_t src0 = ((int64_t)y * a.cap + (int64_t)i * a.B) * a.row_words;
   const int64_t dst0 = ((int64_t)y * a.cap + (int64_t)nb_new * a.B) * a.row_words;
   const int64_t n = (int64_t)rows * a.row_words;
-  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
-    a.dk[dst0 + e] = a.sk[src0 + e];
-    a.dv[dst0 + e] = a.sv[src0 + e];
+  if constexpr (VEC) {
+    const uint4* sk = reinterpret_cast<const uint4*>(a.sk + src0);
+    const uint4* sv = reinterpret_cast<const uint4*>(a.sv + src0);
+    uint4* dk = reinterpret_cast<uint4*>(a.dk + dst0);
+    uint4* dv = reinterpret_cast<uint4*>(a.dv + dst0);
+    for (int64_t e = threadIdx.x; e < n / 4; e += blockDim.x) {
+      const uint4 x = sk[e], z = sv[e];
+      dk[e] = x;
+      dv[e] = z;
+    }
+  } else {
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+      a.dk[dst0 + e] = a.sk[src0 + e];
+      a.dv[dst0 + e] = a.sv[src0 + e];
+    }
   }
   if (i == a.nb) return;
   if (y < a.batch * a.rep_heads) {
@@ -163,7 +177,11 @@ hipError_t launch_prune(const brs_memory& src, const brs_memory& dst, const int3
   a.hkv = src.n_kv_heads;
   a.rep_heads = src.rep_heads;
   const dim3 grid((unsigned)(nb + 1), (unsigned)(src.batch * src.n_kv_heads));
-  hipLaunchKernelGGL(prune_copy_kernel, grid, dim3(256), 0, s, a);
+  // k, v are 16-byte aligned (memory check), so whole-unit rows keep uint4 alignment
+  if (a.row_words % 4 == 0)
+    hipLaunchKernelGGL(prune_copy_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prune_copy_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
