@@ -41,6 +41,31 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Minimum and maximum over the wave: DPP moves within 16-lane rows, then the
+// gfx950 row swaps (every lane gets the result; no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ void wave_minmax_u32(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, dpp_u32<0xb1>(mn));  // quad_perm [1,0,3,2]
+  mx = max(mx, dpp_u32<0xb1>(mx));
+  mn = min(mn, dpp_u32<0x4e>(mn));  // quad_perm [2,3,0,1]
+  mx = max(mx, dpp_u32<0x4e>(mx));
+  mn = min(mn, dpp_u32<0x141>(mn));  // row_half_mirror
+  mx = max(mx, dpp_u32<0x141>(mx));
+  mn = min(mn, dpp_u32<0x140>(mn));  // row_mirror
+  mx = max(mx, dpp_u32<0x140>(mx));
+  auto a = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+  mn = min(a[0], a[1]);
+  mx = max(b[0], b[1]);
+  a = __builtin_amdgcn_permlane32_swap(mn, mn, false, false);
+  b = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+  mn = min(a[0], a[1]);
+  mx = max(b[0], b[1]);
+}
+
 // Inclusive prefix sum over the wave with DPP moves: shifts within each
 // 16-lane row, then the row totals broadcast to the following rows.
 __device__ __forceinline__ int wave_scan_incl(int v) {
@@ -252,6 +277,7 @@ __device__ void group_topk_raw(const uint32_t (&raw)[KPT], int lo, int hi, int k
 // scores); the radix select then does the work.  sel / selv: cap words.
 constexpr int kBisect = 10;  // halvings of the lane-maximum range in wave_topk_filter
 
+// sel / selv hold cap + 1 entries: entry cap is scratch.
 template <int KPT>
 __device__ bool wave_topk_filter(const uint32_t (&raw)[KPT], int lo, int hi, int k, int cap, uint64_t* sel,
                                  uint32_t* selv, int32_t* gidx, float* gvals, int32_t* lidx) {
@@ -273,10 +299,7 @@ __device__ bool wave_topk_filter(const uint32_t (&raw)[KPT], int lo, int hi, int
     // "at least k maxima >= tau" true; stopped after kBisect halvings (a
     // lower bound is all that is needed: a few more keys pass it)
     uint32_t lo_t = mx, hi_t = mx;
-    for (int off = 32; off >= 1; off >>= 1) {
-      lo_t = min(lo_t, (uint32_t)__shfl_xor((int)lo_t, off));
-      hi_t = max(hi_t, (uint32_t)__shfl_xor((int)hi_t, off));
-    }
+    wave_minmax_u32(lo_t, hi_t);
     lo_t = __builtin_amdgcn_readfirstlane(lo_t);
     hi_t = __builtin_amdgcn_readfirstlane(hi_t);
 #pragma unroll
@@ -289,17 +312,17 @@ __device__ bool wave_topk_filter(const uint32_t (&raw)[KPT], int lo, int hi, int
     }
     tau = lo_t;
   }
-  // the keys at or above tau, gathered in LDS (in order of i, then lane)
+  // the keys at or above tau, gathered in LDS (in order of i, then lane);
+  // lanes with nothing to store write slot cap, a scratch slot (no branch)
   int total = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const bool take = ((vmask >> i) & 1u) && keys[i] >= tau;
     const uint64_t m = __ballot(take);
     const int p = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (take && p < cap) {
-      sel[p] = ((uint64_t)keys[i] << 32) | (uint64_t)(0xffffffffu - (uint32_t)(lo + 64 * i + lane));
-      selv[p] = raw[i];
-    }
+    const int dst = (take && p < cap) ? p : cap;
+    sel[dst] = ((uint64_t)keys[i] << 32) | (uint64_t)(0xffffffffu - (uint32_t)(lo + 64 * i + lane));
+    selv[dst] = raw[i];
     total += (int)__popcll(m);
   }
   if (total > cap) return false;

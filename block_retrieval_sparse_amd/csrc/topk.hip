@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   topk_load_raw<KPT>(scores + row * stride, (int)lo, (int)hi, 64, raw);
   int32_t* gi = idx + row * k;
   float* gv = vals ? vals + row * k : nullptr;
-  if (wave_topk_filter<KPT>(raw, (int)lo, (int)hi, k, kWaveCand, sel[wave], selv[wave], gi, gv, nullptr)) return;
+  if (wave_topk_filter<KPT>(raw, (int)lo, (int)hi, k, kWaveCand - 1, sel[wave], selv[wave], gi, gv, nullptr)) return;
 #pragma unroll
   for (int j = 0; j < 4; ++j) sh[wave].hist[lane + 64 * j] = 0u;
   if (lane == 0) {
