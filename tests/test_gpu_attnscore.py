@@ -33,6 +33,13 @@ CASES = {
                                                       n_q=100, planted_per_head=0),
     "decode_f32": W["tiny_decode"].scaled(rep_mode="attnscore", reps_per_block=3, n_q_heads=4, n_kv_heads=2,
                                           n_tokens=3000, block=50, k=5, window=200, sinks=10),
+    # a window shorter than the query chunk (early queries see none of it beyond their own position)
+    "prefill_short_window": W["retrievalattn_gqa_decode_1m_b8"].scaled(
+        rep_mode="attnscore", reps_per_block=2, batch=2, n_q_heads=4, n_kv_heads=4, head_dim=64, rep_dim=64,
+        n_tokens=4000, block=32, k=10, window=40, n_q=150),
+    # the window covers the whole memory (no candidates, k = 0 path)
+    "window_all": W["tiny_decode"].scaled(rep_mode="attnscore", reps_per_block=2, n_q_heads=2, n_kv_heads=1,
+                                          n_tokens=700, block=64, k=0, window=4096, sinks=0),
 }
 MASS_RTOL, MASS_ATOL = 1e-4, 1e-6
 
@@ -47,7 +54,7 @@ def _step(mem, w, x, want_lse=True):
 
 def _oracle_sets(w, step):
     """The GPU's selection turned into each (batch, head)'s attended set."""
-    idx = step.idx.cpu().numpy()
+    idx = step.idx.cpu().numpy() if w.k else np.full((w.batch, w.n_q_heads, 1), -1)
     return {(b, h): O.attended_mask(w.n_tokens, w.block, w.sinks, w.window, idx[b, h])
             for b in range(w.batch) for h in range(w.n_q_heads)}
 
@@ -78,7 +85,7 @@ def test_lse_and_window_mass(name):
             got = mass[b, g, : w.n_tokens]
             assert np.allclose(got, want_m, rtol=MASS_RTOL, atol=MASS_ATOL), \
                 (b, g, np.abs(got - want_m).max())
-            assert (got[: w.n_tokens - w.window] == 0).all()
+            assert (got[: max(w.n_tokens - w.window, 0)] == 0).all()
     # mass of a decode call: each head's window weights sum to at most 1
     if w.n_q == 1:
         tot = mass.sum(axis=2)

@@ -87,3 +87,40 @@ def test_prune_matches_oracle(case):
     old = [i for i in range(nb) if want[i] >= 0]
     assert torch.equal(dst.reps[:, :, :kept], mem.reps[:, :, old])
     assert torch.equal(dst_hits[:, :kept], hits[:, old])
+
+
+def test_prune_small_and_saturated():
+    """Fewer than ten blocks (no tenth to drop or keep) and a capacity that fits everything: the plan is the
+    identity.  Counts that fall with age: the newest middle blocks (fewest hits) are the ones evicted."""
+    # identity: 7 blocks and a tail, half the capacity holds them all
+    mem, g = _memory("bf16", "mean", 1, 2, 64, 16, 1, 16 * 7 + 3, 16 * 20, 3)
+    hits = mem.new_hits()
+    dst = mem.like()
+    plan = mem.prune_into(hits, dst)
+    torch.cuda.synchronize()
+    assert plan.cpu().numpy()[:7].tolist() == list(range(7))
+    assert dst.length == mem.length
+    assert torch.equal(dst.k[:, :, :mem.length], mem.k[:, :, :mem.length])
+    # 100 blocks, capacity 2000 tokens: half holds 62 blocks, so 52 of the 80 middle blocks stay
+    mem2, g2 = _memory("bf16", "mean", 1, 1, 64, 16, 1, 16 * 100, 16 * 125, 4)
+    hits2 = mem2.new_hits()
+    hits2[0, :100] = torch.arange(100, 0, -1, dtype=torch.int32, device=hits2.device)  # older = more hits
+    dst2 = mem2.like()
+    plan2 = mem2.prune_into(hits2, dst2).cpu().numpy()[:100]
+    torch.cuda.synchronize()
+    want = O.prune_plan(1600, 16, 2000, hits2.cpu().numpy()[0, :100])
+    assert np.array_equal(plan2, want)
+    assert (plan2[:10] == -1).all() and (plan2[10:62] >= 0).all() and (plan2[62:90] == -1).all()
+
+
+def test_count_hits_broadcast_lists():
+    """One selection list per sequence (idx_heads = 1)."""
+    mem, g = _memory("f32", "mean", 3, 1, 64, 16, 1, 16 * 30, 16 * 32, 6)
+    hits = mem.new_hits()
+    idx = torch.tensor([[[0, 5, 5, 29, -1]], [[30, 1, 1, 1, 2]], [[7, 7, 7, 7, 7]]], dtype=torch.int32)
+    mem.count_hits(idx.cuda(), hits)
+    torch.cuda.synchronize()
+    got = hits.cpu().numpy()[:, :30]
+    assert got[0, 0] == 1 and got[0, 5] == 2 and got[0, 29] == 1 and got[0].sum() == 4
+    assert got[1, 1] == 3 and got[1, 2] == 1 and got[1].sum() == 4  # block 30 is not complete
+    assert got[2, 7] == 5 and got[2].sum() == 5
