@@ -361,7 +361,7 @@ def run(args):
     # pass D: attention-score representatives (InfLLM "method"): the window
     # mass of one call, and one block's representatives from the mass
     mass_res = None
-    if w.rep_mode != "embed":
+    if w.rep_mode != "embed" and w.window > 0:
         from block_retrieval_sparse_amd.pipeline import RetrievalStep
 
         n_d = min(args.steps, 50)
