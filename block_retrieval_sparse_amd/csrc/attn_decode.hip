@@ -1013,7 +1013,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a
 // selected in the kernel itself (attn_step_kernel: wave w takes the top-k of
 // its kv slice's score row w) -- while waves 4-7 run the sink/window tiles,
 // which need none (the slice's waves 4-7 take them in turn: tiles gw, gw + W,
-// ...).  After one barrier every wave runs its equal share of slot tiles.
+// ...).  After one barrier every wave runs its equal share of slot tiles,
+// dealt from the slice's last wave backwards.
 // K and V come through buffer loads with one 32-bit offset per token;
 // invalid tokens get an offset past the slice and read zeros without
 // touching memory.
@@ -1101,7 +1102,10 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   const int tA = a.len_a >> 5, tB = a.len_b >> 5;
   const int wf_all = a.max_chunks * kFixWaves, gwf = c * kFixWaves + (wave - kSelWaves);
   const int fa = fixw && tA > gwf ? (tA - 1 - gwf) / wf_all + 1 : 0;
-  const int wt_all = a.max_chunks * kSlotWaves, gw = c * kSlotWaves + wave;
+  // slot runs are dealt from the slice's last wave backwards: the fixed
+  // tiles that do not divide evenly land on the first chunks, so a short slot
+  // list (few selections) goes to chunks without an extra fixed tile
+  const int wt_all = a.max_chunks * kSlotWaves, gw = wt_all - 1 - (c * kSlotWaves + wave);
   const int qB = (tB + wt_all - 1) / wt_all, b0 = gw * qB;
   const int n_tiles = fa + max(0, min(b0 + qB, tB) - b0);
 
