@@ -299,16 +299,29 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (k > 0) {
+    const bool step = brs::step_supported(g, lo, hi, k);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (step) {
+      e0 = g_prof_start;
+      e1 = g_prof_stop;
+      g_prof_start = g_prof_stop = nullptr;
+    }
     if (hi > lo) {
+      // measurement: the step kernel's interval starts when the score kernel
+      // completes (an event attached to the step launch itself is stamped
+      // when its dispatch is processed, while the score kernel may still run)
+      if (e0) {
+        brs::set_score_stop_event(e0);
+        e0 = nullptr;
+      }
       e = cosine ? brs::launch_score_cosine(*m, qrep, lo, hi, scores, s)
                  : brs::launch_score_dot(*m, qrep, hs, lo, hi, scores, s);
+      brs::set_score_stop_event(nullptr);
       if (e != hipSuccess) return hip_fail(e, "score_blocks");
     }
     const int64_t stride = m->capacity / m->block_size;
-    if (brs::step_supported(g, lo, hi, k)) {
+    if (step) {
       // selection and attention in one launch, then the merge
-      hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
-      g_prof_start = g_prof_stop = nullptr;
       e = brs::launch_attn_step(g, m->k, m->v, q, scores, stride, lo, hi, idx, vals, workspace, out, s, e0, e1);
       if (e != hipSuccess) return hip_fail(e, "select_topk + attention");
       e = brs::launch_attn_merge(g, workspace, out, lse, s);

@@ -1780,7 +1780,7 @@ hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, con
   const int64_t n = hi - lo;
 #define BRS_LAUNCH_STEP1(DD, KP, DEP)                                                               \
   if (g.d == DD && g.depth == DEP) {                                                                \
-    if (ev0)                                                                                        \
+    if (ev0 || ev1)                                                                                 \
       hipExtLaunchKernelGGL((attn_step_kernel<DD, KP, DEP>), grid, block, 0, s, ev0, ev1, 0, a);    \
     else                                                                                            \
       hipLaunchKernelGGL((attn_step_kernel<DD, KP, DEP>), grid, block, 0, s, a);                    \

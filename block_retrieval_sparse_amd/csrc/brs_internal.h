@@ -156,6 +156,8 @@ hipError_t launch_prune(const brs_memory& src, const brs_memory& dst, const int3
                         int32_t* plan, int nb, int n10, int n_evict, int kept, int tail, hipStream_t s);
 hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const void* reps_new,
                             hipStream_t s);
+// the next score launch on this thread records e when its kernel completes
+void set_score_stop_event(hipEvent_t e);
 hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi,
                             float* scores, hipStream_t s);
 hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, int64_t hi,

@@ -12,9 +12,34 @@
 // the representative bytes are read once per kv head, not once per query
 // head).  L lanes share one row (16-byte loads, coalesced); each lane holds
 // its slice of the G queries in float64 registers.
+#include <hip/hip_ext.h>
+
 #include "brs_internal.h"
 
 namespace brs {
+
+namespace {
+thread_local hipEvent_t g_score_stop = nullptr;  // stamped when the next score kernel completes
+
+hipEvent_t take_score_stop() {
+  hipEvent_t e = g_score_stop;
+  g_score_stop = nullptr;
+  return e;
+}
+}  // namespace
+
+void set_score_stop_event(hipEvent_t e) { g_score_stop = e; }
+
+// a score launch, with the pending stop event attached when there is one
+#define BRS_SCORE_LAUNCH(K, GRID, BLOCK, S, ...)                                      \
+  do {                                                                                \
+    hipEvent_t ev_ = take_score_stop();                                               \
+    if (ev_)                                                                          \
+      hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, S, nullptr, ev_, 0, __VA_ARGS__);      \
+    else                                                                              \
+      hipLaunchKernelGGL(K, GRID, BLOCK, 0, S, __VA_ARGS__);                          \
+  } while (0)
+
 namespace {
 
 template <typename T>
@@ -326,7 +351,7 @@ hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, f
   int bps = (int)((nblk * bg) / (slots * 2048));
   bps = bps < 1 ? 1 : (bps > 8 ? 8 : bps);
   const int64_t gx = (nblk + (int64_t)slots * bps - 1) / ((int64_t)slots * bps);
-  hipLaunchKernelGGL((score_dot_kernel<T, EPL, G>), dim3((unsigned)gx, (unsigned)bg), dim3(256), 0, s,
+  BRS_SCORE_LAUNCH((score_dot_kernel<T, EPL, G>), dim3((unsigned)gx, (unsigned)bg), dim3(256), s,
                      (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads,
                      m.capacity / m.block_size, lo, hi, bps);
   return hipGetLastError();
@@ -342,17 +367,17 @@ hipError_t run_rows(const brs_memory& m, const void* q, int64_t lo, int64_t hi, 
   const int64_t capB = m.capacity / m.block_size;
   if (want >= 4) {
     const int64_t gx = (rows + slots * 4 - 1) / (slots * 4);
-    hipLaunchKernelGGL((score_dot_rows_kernel<T, EPL, G, L, 4>), dim3((unsigned)gx, (unsigned)bg), block, 0, s,
+    BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 4>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
                        hi);
   } else if (want >= 2) {
     const int64_t gx = (rows + slots * 2 - 1) / (slots * 2);
-    hipLaunchKernelGGL((score_dot_rows_kernel<T, EPL, G, L, 2>), dim3((unsigned)gx, (unsigned)bg), block, 0, s,
+    BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 2>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
                        hi);
   } else {
     const int64_t gx = (rows + slots - 1) / slots;
-    hipLaunchKernelGGL((score_dot_rows_kernel<T, EPL, G, L, 1>), dim3((unsigned)gx, (unsigned)bg), block, 0, s,
+    BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 1>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
                        hi);
   }
@@ -394,7 +419,7 @@ hipError_t dispatch_dot(const brs_memory& m, const void* q, int G, int64_t lo, i
   }
   const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
   const int64_t gx = (hi - lo + 3) / 4;
-  hipLaunchKernelGGL(score_dot_generic_kernel<T>, dim3((unsigned)gx, (unsigned)bg), dim3(256), 0, s, (const T*)q,
+  BRS_SCORE_LAUNCH(score_dot_generic_kernel<T>, dim3((unsigned)gx, (unsigned)bg), dim3(256), s, (const T*)q,
                      (const T*)m.reps, scores, d, m.reps_per_block, m.n_kv_heads, G, m.capacity / m.block_size,
                      lo, hi);
   return hipGetLastError();
@@ -413,11 +438,11 @@ hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, 
                                hipStream_t s) {
   const int64_t gx = (hi - lo + 3) / 4;
   if (m.rep_dtype == BRS_F32)
-    hipLaunchKernelGGL(score_cosine_kernel<float>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), 0, s,
+    BRS_SCORE_LAUNCH(score_cosine_kernel<float>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), s,
                        (const float*)rq, (const float*)m.reps, scores, m.rep_dim, m.capacity / m.block_size, lo,
                        hi);
   else
-    hipLaunchKernelGGL(score_cosine_kernel<uint16_t>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), 0, s,
+    BRS_SCORE_LAUNCH(score_cosine_kernel<uint16_t>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), s,
                        (const uint16_t*)rq, (const uint16_t*)m.reps, scores, m.rep_dim,
                        m.capacity / m.block_size, lo, hi);
   return hipGetLastError();

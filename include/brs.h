@@ -314,8 +314,9 @@ int brs_mem_prune(const brs_memory* src, const int32_t* hits, brs_memory* dst, i
 /* Measurement hook: the next brs_retrieval_attention, brs_retrieval_step or
  * brs_window_mass call on this thread records `start_event` and `stop_event`
  * (hipEvent_t, passed as void*) at the begin and end of its main kernel (the
- * attention kernel; the mass kernel) on its stream, then forgets them.  Pass
- * NULLs to cancel. */
+ * attention kernel; the mass kernel) on its stream, then forgets them.  In
+ * the one-launch decode step the start is recorded when the score kernel
+ * before it completes.  Pass NULLs to cancel. */
 int brs_profile_next_attention(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
