@@ -99,8 +99,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   constexpr int BUF = kStage * KP;                      // halves per stage buffer
   // stage buffers: K in [0, 3 BUF), V in [3 BUF, 6 BUF)
   __shared__ __align__(16) uint16_t s_kv[2 * kBufs * BUF];
-  __shared__ int2 s_tab[kTabTokens];
-  __shared__ uint4 s_junk[256];  // (position, K/V row byte offset) of stream tokens, a ring
+  __shared__ int2 s_tab[kTabTokens];  // (position, K/V row byte offset) of stream tokens, a ring
+  __shared__ uint4 s_junk[256];
   __shared__ int4 s_items[kPrefItems];
   __shared__ int wave_tot[16];
   __shared__ int sh_tot[4];
@@ -127,13 +127,44 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   // The segments of this head clipped to positions <= pmax, in position
   // order: the plan lists sinks, window, then blocks in block order, and
   // the blocks lie between sinks and window, so the window goes last.
+  // The header and every slot of the segment list are requested at once
+  // (slots past the header's count are ignored), then the query rows, so
+  // that the three loads overlap; the memory counter waits in issue order.
   const int4 hd = a.hdr[bg];
+  int4 it;
+  {
+    const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.items + (int64_t)bg * a.max_items), (short)0, (int)a.max_items * 16, kBufferFlags);
+    it = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(irs, tid * 16, 0, 0));
+  }
+
+  // query rows of this wave as the B operand of S^T = K Q^T: lane (g4, n)
+  // holds row q0 + 16 qg + n, columns 32 kk + 8 g4 .. + 7, as 32-bit pairs
+  // (d is even).  Unconditional buffer loads: columns past d and rows past
+  // n_q take an offset past the end of the rows and read zeros.
+  const int qi = q0 + 16 * qg + n;
+  const bool act = qi < a.n_q;
+  uint4 qb[KC];
+  {
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.q + (int64_t)bh * a.n_q * a.d), (short)0, a.n_q * a.d * 2, kBufferFlags);
+    uint32_t w[KC][4];
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int e0 = 32 * kk + 8 * g4 + 2 * p;
+        const int off = (act && e0 < a.d) ? (qi * a.d + e0) * 2 : kOutOfRange;
+        w[kk][p] = __builtin_amdgcn_raw_buffer_load_b32(qrs, off, 0, 0);
+      }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) qb[kk] = make_uint4(w[kk][0], w[kk][1], w[kk][2], w[kk][3]);
+  }
+
   const int n_in = hd.x;
-  int4 it = make_int4(0, 0, 0, 0);
   int keep = 0, len = 0;
   bool is_win = false;
   if (tid < n_in) {
-    it = a.items[(int64_t)bg * a.max_items + tid];
     is_win = tid <= 1 && it.x == a.win_start && it.x + it.y == a.N;
     if ((uint32_t)it.z & headbit) {
       len = min(it.x + it.y, pmax + 1) - it.x;
@@ -154,11 +185,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     s_items[sh_tot[0]] = make_int4(it.x, len, 0, sh_tot[1]);
     sh_tot[2] = 1;
   }
-  // pad columns of K and V: zero, except V's column of ones
-  for (int i = tid; i < 2 * kBufs * kStage; i += 512) {
-    uint16_t* row = s_kv + i * KP;
-    const bool isv = i >= kBufs * kStage;
-    for (int c = 8 * a.nvec; c < KP; ++c) row[c] = (ONES && isv && c == 8 * a.nvec) ? 0x3f80 : 0;
+  // pad columns of K and V (columns 8 nvec .. DP - 1, which the products
+  // read): zero, except V's column of ones.  Rows and pads are whole
+  // 16-byte units.
+  {
+    const int npad = DP / 8 - a.nvec;
+    for (int e = tid; e < 2 * kBufs * kStage * npad; e += 512) {
+      const int i = e / npad, c = e - i * npad;
+      const bool ones = ONES && i >= kBufs * kStage && c == 0;
+      *reinterpret_cast<uint4*>(s_kv + i * KP + 8 * (a.nvec + c)) = make_uint4(ones ? 0x3f80u : 0u, 0u, 0u, 0u);
+    }
   }
   __syncthreads();
   const int ns = sh_tot[0] + sh_tot[2];
@@ -167,17 +203,21 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 
   // token table: stream offset tau -> (position, byte offset), kNoPos past the end
   const int row_bytes = a.row_stride * 2;
+  // (count a multiple of 512: each thread fills a run of count / 512
+  // consecutive entries, with one search for the run's first segment)
   auto fill = [&](int tau0, int count) {
-    for (int i = tid; i < count; i += 512) {
-      const int tau = tau0 + i;
+    const int per = count / 512, t0 = tau0 + tid * per;
+    int lo = 0, hi = ns - 1;  // last item with w <= t0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_items[mid].w <= t0) lo = mid; else hi = mid - 1;
+    }
+    int4 c = s_items[lo];
+    for (int j = 0; j < per; ++j) {
+      const int tau = t0 + j;
       int2 e = make_int2(kNoPos, kOutOfRange);
       if (tau < n_tok) {
-        int lo = 0, hi = ns - 1;  // last item with w <= tau
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_items[mid].w <= tau) lo = mid; else hi = mid - 1;
-        }
-        const int4 c = s_items[lo];
+        while (tau >= c.w + c.y) c = s_items[++lo];  // segments are contiguous in the stream
         const int pos = c.x + (tau - c.w);
         e = make_int2(pos, pos * row_bytes);
       }
@@ -234,28 +274,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // query rows of this wave as the B operand of S^T = K Q^T.  Rows past the
-  // last query compute unused values (rows never mix in either product).
-  const int qi = q0 + 16 * qg + n;
-  const bool act = qi < a.n_q;
+  // Rows past the last query compute unused values (rows never mix in
+  // either product).
   const int plim = a.N - a.n_q + qi;                // last visible position of this lane's row
   const int plim_min = a.N - a.n_q + q0 + 16 * qg;  // the wave's smallest one
-  uint4 qb[KC];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)bh * a.n_q + (act ? qi : 0)) * a.d;
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      uint32_t w[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int e0 = 32 * kk + 8 * g4 + 2 * p;
-        const uint32_t lo = (act && e0 < a.d) ? qrow[e0] : 0u;
-        const uint32_t hi = (act && e0 + 1 < a.d) ? qrow[e0 + 1] : 0u;
-        w[p] = lo | (hi << 16);
-      }
-      qb[kk] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
   // a negative scale is taken as |scale| with the query negated (exact in
   // bf16), so the logits below are always scaled by a positive factor
   const float qs = fabsf(a.qscale);
@@ -470,9 +492,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 
 bool prefill_supported(const AttnGeom& g) {
   if (env_flag("BRS_PREFILL", 1) == 0) return false;
-  return g.dtype == BRS_BF16 && g.n_q >= kPrefQ && g.d <= 128 && g.row_stride % 8 == 0 &&
+  return g.dtype == BRS_BF16 && g.n_q >= kPrefQ && g.d <= 128 && g.d % 2 == 0 && g.row_stride % 8 == 0 &&
          ((g.d + 7) / 8) * 8 <= g.row_stride && g.max_items <= kPrefItems &&
-         g.head_stride * 2 < (int64_t)kOutOfRange - 4096;
+         g.head_stride * 2 < (int64_t)kOutOfRange - 4096 && (int64_t)g.n_q * g.d * 2 < (int64_t)kOutOfRange - 4096;
 }
 
 hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws, float* out,
