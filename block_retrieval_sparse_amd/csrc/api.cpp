@@ -233,12 +233,12 @@ static int run_attention(const brs::AttnGeom& g, const brs_memory* m, const void
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   hipError_t e;
-  if (!g.local_plan && !g.slot) {
+  if (!g.local_plan && !g.slot && !g.prefill) {
     e = brs::launch_attn_plan(g, idx, workspace, out, s);
     if (e != hipSuccess) return hip_fail(e, "attn_plan");
   }
   if (g.prefill) {
-    e = brs::launch_attn_prefill(g, m->k, m->v, q, workspace, out, lse, s, e0, e1);
+    e = brs::launch_attn_prefill(g, m->k, m->v, q, idx, out, lse, s, e0, e1);
     if (e != hipSuccess) return hip_fail(e, "attn_prefill");
     return ok();
   }

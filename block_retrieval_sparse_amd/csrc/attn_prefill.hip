@@ -59,9 +59,8 @@ struct PrefillArgs {
   const uint16_t* q;
   float* out;
   float* lse;  // per query row, ln of the softmax denominator (may be null)
-  const int4* hdr;
-  const int4* items;
-  int64_t max_items;
+  const int32_t* idx;  // selections, [batch][idx_heads][kk]
+  int kk, idx_heads, B, nb, sink_end;
   int64_t head_stride;
   int row_stride, hq, hkv, G, n_q, N, d, nvec, nj;
   int slice_bytes;  // bytes of one (batch, kv head) slice of k / v (buffer range)
@@ -102,6 +101,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   __shared__ int2 s_tab[kTabTokens];  // (position, K/V row byte offset) of stream tokens, a ring
   __shared__ uint4 s_junk[256];
   __shared__ int4 s_items[kPrefItems];
+  __shared__ int s_blk[kPrefItems];
   __shared__ int wave_tot[16];
   __shared__ int sh_tot[4];
   __shared__ float s_ml[4][16][2];
@@ -119,23 +119,23 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   const int b = bh / a.hq, h = bh - b * a.hq;
   const int g = h / a.G;
   const int bg = b * a.hkv + g;
-  const uint32_t headbit = 1u << (h - g * a.G);
   const int q0 = tile * kPrefQ;
   const int qlast = min(q0 + kPrefQ, a.n_q) - 1;
   const int pmax = a.N - a.n_q + qlast;
 
-  // The segments of this head clipped to positions <= pmax, in position
-  // order: the plan lists sinks, window, then blocks in block order, and
-  // the blocks lie between sinks and window, so the window goes last.
-  // The header and every slot of the segment list are requested at once
-  // (slots past the header's count are ignored), then the query rows, so
-  // that the three loads overlap; the memory counter waits in issue order.
-  const int4 hd = a.hdr[bg];
-  int4 it;
+  // The segments of this head in position order, clipped to positions
+  // <= pmax: the sinks [0, S'), the blocks its score head selected, in block
+  // order, then the window [win_start, N).  A selected block contributes
+  // [max(blk B, S'), min((blk + 1) B, win_start)); invalid entries, blocks
+  // that lie inside the sinks or the window, and repeats are dropped.  The
+  // selection row is requested before the query rows so that the two loads
+  // overlap (the memory counter waits in issue order).
+  int blk;
   {
+    const int row = a.idx_heads == 1 ? b : b * a.hq + h;
     const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.items + (int64_t)bg * a.max_items), (short)0, (int)a.max_items * 16, kBufferFlags);
-    it = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(irs, tid * 16, 0, 0));
+        (void*)(a.idx + (int64_t)row * a.kk), (short)0, a.kk * 4, kBufferFlags);
+    blk = (int)__builtin_amdgcn_raw_buffer_load_b32(irs, tid < a.kk ? tid * 4 : kOutOfRange, 0, 0);
   }
 
   // query rows of this wave as the B operand of S^T = K Q^T: lane (g4, n)
@@ -161,29 +161,43 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     for (int kk = 0; kk < KC; ++kk) qb[kk] = make_uint4(w[kk][0], w[kk][1], w[kk][2], w[kk][3]);
   }
 
-  const int n_in = hd.x;
-  int keep = 0, len = 0;
-  bool is_win = false;
-  if (tid < n_in) {
-    is_win = tid <= 1 && it.x == a.win_start && it.x + it.y == a.N;
-    if ((uint32_t)it.z & headbit) {
-      len = min(it.x + it.y, pmax + 1) - it.x;
-      len = len < 0 ? 0 : len;
-      keep = len > 0;
-    }
-  }
-  if (tid == 0) sh_tot[2] = 0;
-  const int inc_k = block_inclusive_scan(keep && !is_win ? 1 : 0, wave_tot);
-  const int inc_t = block_inclusive_scan(keep && !is_win ? len : 0, wave_tot);
-  if (tid == 511) {
-    sh_tot[0] = inc_k;
-    sh_tot[1] = inc_t;
+  const int S = a.sink_end;
+  if (tid < kPrefItems) {
+    const bool valid = tid < a.kk && blk >= 0 && blk < a.nb &&
+                       max(blk * a.B, S) < min((blk + 1) * a.B, a.win_start);
+    s_blk[tid] = valid ? blk : -1;
   }
   __syncthreads();
-  if (keep && !is_win) s_items[inc_k - 1] = make_int4(it.x, len, 0, inc_t - len);
-  if (keep && is_win) {
-    s_items[sh_tot[0]] = make_int4(it.x, len, 0, sh_tot[1]);
-    sh_tot[2] = 1;
+  bool dup = false;  // an earlier entry holds the same block
+  if (tid < a.kk && s_blk[tid] >= 0)
+    for (int j = 0; j < tid; ++j) dup |= s_blk[j] == s_blk[tid];
+  __syncthreads();
+  if (dup) s_blk[tid] = -1;
+  __syncthreads();
+  const int mine = tid < a.kk ? s_blk[tid] : -1;
+  int rank = 0;  // kept blocks below this one
+  if (mine >= 0)
+    for (int j = 0; j < a.kk; ++j) {
+      const int o = s_blk[j];
+      rank += o >= 0 && o < mine;
+    }
+  const int n_kept = __syncthreads_count(mine >= 0);
+  const int hs = S > 0 ? 1 : 0;
+  const int n_items = hs + n_kept + 1;
+  if (mine >= 0) {
+    const int lo_t = max(mine * a.B, S);
+    const int hi_t = min(min((mine + 1) * a.B, a.win_start), pmax + 1);
+    s_items[hs + rank] = make_int4(lo_t, max(hi_t - lo_t, 0), 0, 0);
+  }
+  if (tid == 0 && hs) s_items[0] = make_int4(0, min(S, pmax + 1), 0, 0);
+  if (tid == 0) s_items[hs + n_kept] = make_int4(a.win_start, max(min(a.N, pmax + 1) - a.win_start, 0), 0, 0);
+  __syncthreads();
+  // stream offsets (segments past pmax have length 0; they come last)
+  {
+    const int len = tid < n_items ? s_items[tid].y : 0;
+    const int inc = block_inclusive_scan(len, wave_tot);
+    if (tid < n_items) s_items[tid].w = inc - len;
+    if (tid == 511) sh_tot[0] = inc;
   }
   // pad columns of K and V (columns 8 nvec .. DP - 1, which the products
   // read): zero, except V's column of ones.  Rows and pads are whole
@@ -197,8 +211,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  const int ns = sh_tot[0] + sh_tot[2];
-  const int n_tok = ns > 0 ? s_items[ns - 1].w + s_items[ns - 1].y : 0;
+  const int ns = n_items;
+  const int n_tok = sh_tot[0];
   const int n_stages = (n_tok + kStage - 1) / kStage;
 
   // token table: stream offset tau -> (position, byte offset), kNoPos past the end
@@ -493,21 +507,24 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 bool prefill_supported(const AttnGeom& g) {
   if (env_flag("BRS_PREFILL", 1) == 0) return false;
   return g.dtype == BRS_BF16 && g.n_q >= kPrefQ && g.d <= 128 && g.d % 2 == 0 && g.row_stride % 8 == 0 &&
-         ((g.d + 7) / 8) * 8 <= g.row_stride && g.max_items <= kPrefItems &&
+         ((g.d + 7) / 8) * 8 <= g.row_stride && g.k + 2 <= kPrefItems &&
          g.head_stride * 2 < (int64_t)kOutOfRange - 4096 && (int64_t)g.n_q * g.d * 2 < (int64_t)kOutOfRange - 4096;
 }
 
-hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws, float* out,
-                               float* lse, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
+                               float* out, float* lse, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   PrefillArgs a;
   a.lse = lse;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.q = (const uint16_t*)q;
   a.out = out;
-  a.hdr = (const int4*)((char*)ws + g.hdr_off);
-  a.items = (const int4*)((char*)ws + g.items_off);
-  a.max_items = g.max_items;
+  a.idx = idx;
+  a.kk = idx ? g.k : 0;
+  a.idx_heads = g.idx_heads;
+  a.B = g.B;
+  a.nb = g.nb;
+  a.sink_end = g.sink_end;
   a.head_stride = g.head_stride;
   a.row_stride = g.row_stride;
   a.hq = g.hq;

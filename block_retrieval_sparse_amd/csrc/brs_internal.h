@@ -134,8 +134,9 @@ bool step_supported(const AttnGeom& g, int64_t lo, int64_t hi, int k);
 hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, const void* q, const float* scores,
                             int64_t stride, int64_t lo, int64_t hi, int32_t* idx, float* vals, void* ws, float* out,
                             hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
-// Chunked prefill on the matrix cores (reads the plan's segments from ws).
-hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, void* ws,
+// Chunked prefill on the matrix cores; each workgroup builds its head's
+// segments from idx itself (no plan kernel).
+hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, const void* q, const int32_t* idx,
                                float* out, float* lse, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 bool prefill_supported(const AttnGeom& g);
 

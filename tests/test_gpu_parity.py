@@ -160,22 +160,32 @@ def test_k_above_candidates_and_no_candidates():
     C.check_step(wn, mem, x, step)
 
 
-def test_caller_selection_with_duplicates_and_skips():
+@pytest.mark.parametrize("name", ["infllm", "prefill_gqa"])
+def test_caller_selection_with_duplicates_and_skips(name):
     """Selections from the caller: duplicates count once, -1 and out-of-range
-    entries are skipped, blocks overlapping sinks/window are deduplicated."""
-    w = SMALL["infllm"]
+    entries are skipped, blocks overlapping sinks/window are deduplicated
+    (decode, and the chunked prefill, whose workgroups build each head's
+    segments from the selection themselves; there the heads of a group get
+    different lists, with blocks across and inside the window)."""
+    w = SMALL[name]
     mem, x = C.load(w)
     nb = w.n_blocks
-    idx = torch.tensor([[[5, 5, -1, nb, nb + 100, 0, nb - 1, 3]] * w.n_q_heads] * w.batch, dtype=torch.int32,
-                       device="cuda")
+    base = [5, 5, -1, nb, nb + 100, 0, nb - 1, 3]
+    if w.n_q > 1:
+        wb = (w.n_tokens - w.window) // w.block  # the block the window starts in
+        base += [wb, wb + 1, wb - 1, wb - 1, nb - 2, 17, 2 ** 31 - 1, -7]
+    rows = [base[h % len(base):] + base[:h % len(base)] for h in range(w.n_q_heads)]
+    idx = torch.tensor([rows] * w.batch, dtype=torch.int32, device="cuda")
     out = mem.retrieval_attention(x["q"], idx, w.sinks, w.window)
     torch.cuda.synchronize()
     q, K, V = C.host(x["q"]), C.host(x["k"]), C.host(x["v"])
-    for h in range(w.n_q_heads):
-        g = h // w.group
-        T = O.attended_mask(w.n_tokens, w.block, w.sinks, w.window, [b for b in idx[0, h].tolist() if b < nb])
-        ref = O.attention(q[0, h], K[0, g], V[0, g], T, C.scale_of(w))
-        assert np.max(np.abs(out[0, h].cpu().numpy() - ref)) <= C.TOL[w.dtype]
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            g = h // w.group
+            T = O.attended_mask(w.n_tokens, w.block, w.sinks, w.window,
+                                [i for i in idx[b, h].tolist() if 0 <= i < nb])
+            ref = O.attention(q[b, h], K[b, g], V[b, g], T, C.scale_of(w))
+            assert np.max(np.abs(out[b, h].cpu().numpy() - ref)) <= C.TOL[w.dtype], (b, h)
 
 
 def test_empty_set_gives_zeros_and_static_empty_is_an_error():
@@ -192,9 +202,10 @@ def test_empty_set_gives_zeros_and_static_empty_is_an_error():
     assert e.value.code == -5
 
 
-def test_broadcast_selection_dot_mode():
+@pytest.mark.parametrize("name", ["infllm", "prefill_gqa"])
+def test_broadcast_selection_dot_mode(name):
     """One selection per sequence (idx_heads = 1) in dot mode."""
-    w = SMALL["infllm"]
+    w = SMALL[name]
     mem, x = C.load(w)
     idx = torch.tensor([[[7, 2, 40, 11]]] * w.batch, dtype=torch.int32, device="cuda")
     out = mem.retrieval_attention(x["q"], idx, w.sinks, w.window)
