@@ -160,6 +160,41 @@ def test_k_above_candidates_and_no_candidates():
     C.check_step(wn, mem, x, step)
 
 
+@pytest.mark.parametrize("case", ["many_blocks", "fewer_than_k", "all_equal"])
+def test_cosine_prefill_selection_cases(case):
+    """MemLong chunked prefill: scores bit-exact, selection and attention
+    against the oracle, with 700 candidate blocks; with fewer candidates than
+    k (-1 / -inf tail); with every embedding equal (all scores tied, more than
+    the fast selection ranks: the lowest block indices win)."""
+    from synth import inputs as I
+
+    base = W["memlong_chunk_prefill_80k"]
+    small = dict(n_q_heads=2, n_kv_heads=2, head_dim=64, row_stride=64, block=64, window=64, n_q=64)
+    if case == "many_blocks":
+        w = base.scaled(n_tokens=700 * 64 + 64, k=20, **small)
+    elif case == "fewer_than_k":
+        w = base.scaled(n_q_heads=2, n_kv_heads=2, n_tokens=4 * 512 + 512, k=5, n_q=64)
+    else:
+        w = base.scaled(n_tokens=400 * 64 + 64, k=16, **small)
+    x = I.make_all(w, "cuda")
+    if case == "all_equal":
+        x["embeds"][:] = x["embeds"][:, :, :1]
+        x["rq"] = x["embeds"][:, :, -1, 0, :].contiguous()
+    mem, x = C.load(w, x=x)
+    step = run_step(mem, w, x)
+    C.check_step(w, mem, x, step, query_rows=[0, 31, 63])
+    lo, hi = step.lo, step.hi
+    idx, vals, sc = step.idx.cpu().numpy(), step.vals.cpu().numpy(), step.scores.cpu().numpy()
+    m = min(w.k, hi - lo)
+    for b in range(w.batch):
+        assert np.array_equal(vals[b, 0, :m].view(np.uint32), sc[b, 0, idx[b, 0, :m]].view(np.uint32))
+        assert (idx[b, 0, m:] == -1).all() and np.isneginf(vals[b, 0, m:]).all()
+        if case == "all_equal":
+            assert np.array_equal(idx[b, 0], np.arange(lo, lo + w.k))
+    if case == "fewer_than_k":
+        assert hi - lo < w.k
+
+
 @pytest.mark.parametrize("name", ["infllm", "prefill_gqa"])
 def test_caller_selection_with_duplicates_and_skips(name):
     """Selections from the caller: duplicates count once, -1 and out-of-range
