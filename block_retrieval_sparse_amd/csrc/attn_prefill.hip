@@ -9,12 +9,13 @@
 //   - waves 0-3 and 4-7 own query rows 16w..16w+15 (w = wave % 4) and split
 //     the token stream between them (even / odd 32-token halves of each
 //     64-token stage); the two partial softmaxes are merged at the end;
-//   - the attended segments of the (batch, kv head) come from the plan
-//     kernel; the workgroup keeps those that hold its head, clips them to
-//     positions <= its last query (the causal limit), and flattens them;
+//   - the workgroup builds its head's attended segments from the selection
+//     row (sinks, the selected blocks in block order, window), clips them to
+//     positions <= its last query (the causal limit), and flattens them into
+//     a token stream with a position table in LDS;
 //   - each 64-token stage of K and V is staged once in LDS for all 8 waves,
-//     double buffered: the next stage's global loads are in flight while the
-//     current one is multiplied;
+//     in three buffers fed by a ring of loads four stages ahead, so global
+//     loads are in flight while earlier stages are multiplied;
 //   - S^T = K Q^T and O += P V on v_mfma_f32_16x16x32_bf16 with the layouts
 //     of the decode kernel (V read back transposed with ds_read_b64_tr_b16,
 //     P split into bf16 high and low parts so weights keep ~16 bits);
