@@ -47,6 +47,10 @@ SMALL = {
     "prefill_d64_short_window": W["retrievalattn_gqa_decode_1m_b8"].scaled(
         batch=2, n_q_heads=4, n_kv_heads=4, head_dim=64, rep_dim=64, n_tokens=4000, block=32, k=10, window=40,
         n_q=150),
+    # 250 selected 16-token blocks per head: 252 segments, the most one prefill workgroup holds
+    "prefill_many_segments": W["infllm_gqa_decode_128k"].scaled(n_q_heads=4, n_kv_heads=2, n_tokens=300 * 16 + 7,
+                                                                 block=16, window=64, sinks=8, k=250, n_q=64,
+                                                                 planted_per_head=0),
 }
 
 
