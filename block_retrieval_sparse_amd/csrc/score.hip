@@ -341,6 +341,55 @@ __global__ __launch_bounds__(256) void score_cosine_kernel(const T* __restrict__
   }
 }
 
+// Cosine with 16 lanes per embedding row (16-byte loads, lane l takes
+// units l, l + 16, ...; UPL units per lane), 4 rows per wave, the three sums
+// reduced over the 16 lanes with DPP moves.  Same products, float64 sums and
+// final rounding as score_cosine_kernel.
+constexpr int kCosLanes = 16;
+
+template <typename T, int UPL>
+__global__ __launch_bounds__(256) void score_cosine_rows_kernel(const T* __restrict__ rq, const T* __restrict__ emb,
+                                                                float* __restrict__ scores, int D, int64_t capB,
+                                                                int64_t lo, int64_t hi) {
+  constexpr int VN = Vec<T>::n;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & (kCosLanes - 1);
+  const int64_t blk = lo + (int64_t)blockIdx.x * (blockDim.x / kCosLanes) + (threadIdx.x / kCosLanes);
+  const int b = blockIdx.y;
+  const int units = D / VN;
+  const int64_t row = blk < hi ? blk : lo;  // rows past the range repeat row lo (nothing is stored)
+  const T* qrow = rq + (int64_t)b * D;
+  const T* erow = emb + ((int64_t)b * capB + row) * D;
+  uint4 qr[UPL], er[UPL];
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) {
+    const int un = min(sub + kCosLanes * u, units - 1);
+    qr[u] = *reinterpret_cast<const uint4*>(qrow + (int64_t)un * VN);
+    er[u] = *reinterpret_cast<const uint4*>(erow + (int64_t)un * VN);
+  }
+  double dot = 0.0, qq = 0.0, ee = 0.0;
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) {
+    if (sub + kCosLanes * u >= units) continue;  // a unit another lane already holds
+    double x[VN], y[VN];
+    Vec<T>::to_f64(qr[u], x);
+    Vec<T>::to_f64(er[u], y);
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      dot = fma(x[e], y[e], dot);
+      qq = fma(x[e], x[e], qq);
+      ee = fma(y[e], y[e], ee);
+    }
+  }
+  dot = group_sum_f64<kCosLanes>(dot);
+  qq = group_sum_f64<kCosLanes>(qq);
+  ee = group_sum_f64<kCosLanes>(ee);
+  if (sub == 0 && blk < hi) {
+    const double den = sqrt(qq) * sqrt(ee);
+    scores[(int64_t)b * capB + blk] = den != 0.0 ? (float)(dot / den) : 0.0f;
+  }
+}
+
 template <typename T, int EPL, int G>
 hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
   const int L = m.head_dim / EPL;
@@ -436,6 +485,28 @@ hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t 
 
 hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, int64_t hi, float* scores,
                                hipStream_t s) {
+  // whole 16-byte units, at most 8 per lane: the 16-lane rows
+  const int vn = m.rep_dtype == BRS_F32 ? 4 : 8;
+  const int upl = (m.rep_dim / vn + kCosLanes - 1) / kCosLanes;
+  if (m.rep_dim % vn == 0 && upl <= 8) {
+    const dim3 grid((unsigned)((hi - lo + 15) / 16), (unsigned)m.batch), block(256);
+    const int64_t capB = m.capacity / m.block_size;
+#define BRS_COS_ROWS(T, U)                                                                                 \
+  BRS_SCORE_LAUNCH((score_cosine_rows_kernel<T, U>), grid, block, s, (const T*)rq, (const T*)m.reps, scores, \
+                   m.rep_dim, capB, lo, hi)
+    if (m.rep_dtype == BRS_F32) {
+      if (upl <= 2) BRS_COS_ROWS(float, 2);
+      else if (upl <= 4) BRS_COS_ROWS(float, 4);
+      else BRS_COS_ROWS(float, 8);
+    } else {
+      if (upl <= 2) BRS_COS_ROWS(uint16_t, 2);
+      else if (upl <= 4) BRS_COS_ROWS(uint16_t, 4);
+      else if (upl <= 6) BRS_COS_ROWS(uint16_t, 6);
+      else BRS_COS_ROWS(uint16_t, 8);
+    }
+#undef BRS_COS_ROWS
+    return hipGetLastError();
+  }
   const int64_t gx = (hi - lo + 3) / 4;
   if (m.rep_dtype == BRS_F32)
     BRS_SCORE_LAUNCH(score_cosine_kernel<float>, dim3((unsigned)gx, (unsigned)m.batch), dim3(256), s,
