@@ -1023,7 +1023,7 @@ constexpr int kSlotRegs = 8;           // selection entries per lane: at most 51
 constexpr int kSlotOOR = 0x7ffff000;   // buffer offset past any slice
 constexpr int kSlotFlags = 0x00020000; // raw buffer resource word 3 (32-bit data, no swizzle)
 constexpr int kSlotWaves = 8;          // waves per slot workgroup
-constexpr int kSelWaves = 4;           // waves 0-3 select (at most four score rows); 4-7 take the sink/window tiles
+constexpr int kSelWaves = 4;           // waves 0..R-1 select (R <= 4 score rows); the others take the sink/window tiles
 constexpr int kStepK = 128;            // largest k selected inside the attention kernel
 constexpr int kStepCand = 256;         // candidates the fast selection ranks (else the radix select)
 constexpr int kWaitVm0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unconstrained
@@ -1095,12 +1095,15 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
     for (int kk = 0; kk < KC; ++kk) qb[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
 
-  // the wave's tiles: fa sink/window tiles (waves 4-7, strided over the
-  // slice's such waves), then its run of slot tiles
-  constexpr int kFixWaves = kSlotWaves - kSelWaves;
-  const bool fixw = wave >= kSelWaves;
+  // the wave's tiles: fa sink/window tiles, then its run of slot tiles.  The
+  // sink/window tiles are strided over the waves past the selection waves
+  // (waves nsel .. 7 of every chunk, nsel = the slice's score rows, at most
+  // kSelWaves), with the same dealing when the selections come from idx, so
+  // both kernels give the same partials.
+  const int nsel = min(R, kSelWaves), nfix = kSlotWaves - nsel;
+  const bool fixw = wave >= nsel;
   const int tA = a.len_a >> 5, tB = a.len_b >> 5;
-  const int wf_all = a.max_chunks * kFixWaves, gwf = c * kFixWaves + (wave - kSelWaves);
+  const int wf_all = a.max_chunks * nfix, gwf = c * nfix + (wave - nsel);
   const int fa = fixw && tA > gwf ? (tA - 1 - gwf) / wf_all + 1 : 0;
   // slot runs are dealt from the slice's last wave backwards: the fixed
   // tiles that do not divide evenly land on the first chunks, so a short slot
