@@ -1571,8 +1571,8 @@ bool launch_fast_d(const AttnGeom& g, dim3 grid, dim3 block, hipStream_t s, cons
   }
 #define BRS_LAUNCH_ROWS(R)                                                                                    \
   if (rows <= R) {                                                                                            \
-    if (u == 1) BRS_LAUNCH_U(R, 1)                                                                            \
-    if (u == 4) BRS_LAUNCH_U(R, 4)                                                                            \
+    if (u == 1) { BRS_LAUNCH_U(R, 1) }                                                                        \
+    if (u == 4) { BRS_LAUNCH_U(R, 4) }                                                                        \
     BRS_LAUNCH_U(R, 2)                                                                                        \
   }
   BRS_LAUNCH_ROWS(1)
