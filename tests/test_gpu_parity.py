@@ -263,7 +263,11 @@ def test_broadcast_selection_dot_mode(name):
                                       (5000, 2048, "normal"), (16384, 320, "ties"), (16384, 320, "zeros"),
                                       (20000, 100, "ties"), (700, 700, "normal"), (50, 64, "normal"),
                                       (1500, 100, "ties"), (2048, 512, "normal"), (2048, 513, "ties"),
-                                      (130, 33, "nan")])
+                                      (130, 33, "nan"),
+                                      # one 1024-thread workgroup per row (radix select), keys in registers
+                                      (3000, 100, "normal"), (3000, 64, "nan"), (10000, 512, "ties"),
+                                      (16384, 1, "normal"), (4096, 200, "zeros"), (12000, 333, "ties"),
+                                      (8000, 300, "mostly_nan")])
 def test_select_topk(n, k, kind):
     import block_retrieval_sparse_amd as brs
 
@@ -274,6 +278,8 @@ def test_select_topk(n, k, kind):
         s = np.round(s * 4) / 4
     if kind == "nan":
         s[:, rng.integers(0, stride, 40)] = np.nan
+    if kind == "mostly_nan":  # fewer numbers than k: the k-th key is NaN's
+        s[rng.random((rows, stride)) < 0.97] = np.nan
     if kind == "zeros":
         s = np.where(rng.random((rows, stride)) < 0.5, np.float32(0.0), np.float32(-0.0))
         s[rng.random((rows, stride)) < 0.01] = 1.0
