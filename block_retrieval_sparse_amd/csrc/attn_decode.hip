@@ -1020,6 +1020,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_split_mfma_kernel(SplitArgs a
 // touching memory.
 constexpr int kXcdCount = 8;           // XCDs; consecutive workgroups go to consecutive XCDs
 constexpr int kSlotRegs = 8;           // selection entries per lane: at most 512 per kv slice
+constexpr int kSlotRegsMax = 20;       // the wider instantiation (idx read by the split kernel): 1280
 constexpr int kSlotOOR = 0x7ffff000;   // buffer offset past any slice
 constexpr int kSlotFlags = 0x00020000; // raw buffer resource word 3 (32-bit data, no swizzle)
 constexpr int kSlotWaves = 8;          // waves per slot workgroup
@@ -1036,11 +1037,11 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
   return (void*)(((uint64_t)hi << 32) | lo);
 }
 
-template <int D>
+template <int D, int REGS = kSlotRegs>
 struct SlotLds {
   __align__(16) uint16_t v[kSlotWaves][32][D + 16];  // V rows padded by 32 bytes (conflict-free transposed reads)
   float m[kSlotWaves][16], l[kSlotWaves][16];
-  int ents[64 * kSlotRegs];  // the kv slice's selection entries, head-major
+  int ents[64 * REGS];  // the kv slice's selection entries, head-major
 };
 
 // In-kernel selection: one score row per selection wave.
@@ -1051,9 +1052,10 @@ struct StepLds {
   int flag[kSelWaves];
 };
 
-template <int D, int KPTW, int DEPTH>  // KPTW > 0: select in the kernel, KPTW scores per lane;
-                                        // DEPTH tiles of loads in flight per wave
-__device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<D>& sm, StepLds* st) {
+template <int D, int KPTW, int DEPTH, int REGS = kSlotRegs>  // KPTW > 0: select in the kernel, KPTW scores
+                                                            // per lane; DEPTH tiles of loads in flight per
+                                                            // wave; REGS selection entries per lane
+__device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<D, REGS>& sm, StepLds* st) {
   constexpr bool STEP = KPTW > 0;
   constexpr int KC = D / 32;  // 32-wide k chunks of the head dim
   constexpr int NJ = D / 16;  // 16-wide output column tiles
@@ -1116,10 +1118,10 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   const int E = a.n_ent, K = a.kk;
   const int nreg = (E + 63) >> 6;
   const uint32_t full = a.G >= 32 ? 0xffffffffu : ((1u << a.G) - 1u);
-  int ent[kSlotRegs];
+  int ent[REGS];
   if constexpr (!STEP) {
 #pragma unroll
-    for (int r = 0; r < kSlotRegs; ++r) {
+    for (int r = 0; r < REGS; ++r) {
       const int e = lane + 64 * r, ec = min(e, E - 1);
       const int j = ec / K;
       const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + j;
@@ -1140,7 +1142,7 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
     // entries naming the same block: the first one attends it for all their heads
     int first = 1 << 30, tot = 0;
 #pragma unroll
-    for (int rr = 0; rr < kSlotRegs; ++rr) {
+    for (int rr = 0; rr < REGS; ++rr) {
       if (rr < nreg) {
         const uint64_t m = __ballot(ent[rr] == X);
         tot += __popcll(m);
@@ -1154,7 +1156,7 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
       c_mk = 1u << (s / K);
     } else {
 #pragma unroll
-      for (int rr = 0; rr < kSlotRegs; ++rr) {
+      for (int rr = 0; rr < REGS; ++rr) {
         if (rr < nreg) {
           uint64_t m = __ballot(ent[rr] == X);
           while (m) {
@@ -1340,14 +1342,14 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kSlotRegs; ++r) {
+    for (int r = 0; r < REGS; ++r) {
       const int e = lane + 64 * r;
       ent[r] = e < E ? sm.ents[min(e, E - 1)] : -2;
     }
   } else {
     if (wave == 0) {
 #pragma unroll
-      for (int r = 0; r < kSlotRegs; ++r)
+      for (int r = 0; r < REGS; ++r)
         if (r < nreg) sm.ents[lane + 64 * r] = ent[r];
     }
     __syncthreads();
@@ -1403,12 +1405,12 @@ __device__ __forceinline__ int slot_unit_index(const SplitArgs& a) {
 }
 
 // Attention over the slot layout with the selections read from idx.
-template <int D, int DEPTH>
+template <int D, int DEPTH, int REGS>
 __global__ __launch_bounds__(64 * kSlotWaves) void attn_split_slot_kernel(SplitArgs a) {
-  __shared__ SlotLds<D> sm;
+  __shared__ SlotLds<D, REGS> sm;
   const int unit = slot_unit_index(a);
   if (unit >= a.n_units) return;
-  slot_unit<D, 0, DEPTH>(a, unit, sm, nullptr);
+  slot_unit<D, 0, DEPTH, REGS>(a, unit, sm, nullptr);
 }
 
 // The whole decode step after scoring: the selection of every score row of
@@ -1609,8 +1611,9 @@ bool attn_geometry(AttnGeom& g) {
   // the prefill kernel needs only the plan; the split path also keeps partials
   g.prefill = prefill_supported(g);
   // slot layout: every selection entry gets its own padded slot
-  g.slot = g.mfma && !g.prefill && E >= 1 && E <= 64 * kSlotRegs && E <= g.nb &&
+  g.slot = g.mfma && !g.prefill && E >= 1 && E <= 64 * kSlotRegsMax && E <= g.nb &&
            g.head_stride * 2 < (int64_t)kSlotOOR - 4096 && env_int("BRS_SLOT", 1) != 0;
+  g.slot_regs = E <= 64 * kSlotRegs ? kSlotRegs : kSlotRegsMax;
   if (g.slot) {
     auto pad32 = [](int64_t x) { return (x + 31) / 32 * 32; };
     g.slot_ps = (int)pad32(g.sink_end);
@@ -1765,7 +1768,8 @@ unsigned slot_grid(const SplitArgs& a) { return (unsigned)(a.xcd_map ? a.per_xcd
 
 bool step_supported(const AttnGeom& g, int64_t lo, int64_t hi, int k) {
   const int R = g.idx_heads == 1 ? 1 : g.group;
-  return g.slot && R <= kSelWaves && k >= 1 && k <= kStepK && hi - lo <= 64 * 32 && (g.d == 64 || g.d == 128) &&
+  return g.slot && g.slot_regs == kSlotRegs && R <= kSelWaves && k >= 1 && k <= kStepK && hi - lo <= 64 * 32 &&
+         (g.d == 64 || g.d == 128) &&
          env_int("BRS_STEP", 1) != 0;
 }
 
@@ -1814,18 +1818,22 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
   if (g.slot) {
     const dim3 grid1(slot_grid(a)), block(64 * kSlotWaves);
-#define BRS_LAUNCH_SLOT(DD, DEP)                                                                     \
-  if (g.d == DD && g.depth == DEP) {                                                                 \
-    if (ev0)                                                                                         \
-      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, DEP>), grid1, block, 0, s, ev0, ev1, 0, a);  \
-    else                                                                                             \
-      hipLaunchKernelGGL((attn_split_slot_kernel<DD, DEP>), grid1, block, 0, s, a);                  \
-    return hipGetLastError();                                                                        \
+#define BRS_LAUNCH_SLOT(DD, DEP, RG)                                                                     \
+  if (g.d == DD && g.depth == DEP && g.slot_regs == RG) {                                                \
+    if (ev0)                                                                                             \
+      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, DEP, RG>), grid1, block, 0, s, ev0, ev1, 0, a);  \
+    else                                                                                                 \
+      hipLaunchKernelGGL((attn_split_slot_kernel<DD, DEP, RG>), grid1, block, 0, s, a);                  \
+    return hipGetLastError();                                                                            \
   }
-    BRS_LAUNCH_SLOT(64, 1)
-    BRS_LAUNCH_SLOT(128, 1)
-    BRS_LAUNCH_SLOT(64, 2)
-    BRS_LAUNCH_SLOT(128, 2)
+    BRS_LAUNCH_SLOT(64, 1, kSlotRegs)
+    BRS_LAUNCH_SLOT(128, 1, kSlotRegs)
+    BRS_LAUNCH_SLOT(64, 2, kSlotRegs)
+    BRS_LAUNCH_SLOT(128, 2, kSlotRegs)
+    BRS_LAUNCH_SLOT(64, 1, kSlotRegsMax)
+    BRS_LAUNCH_SLOT(128, 1, kSlotRegsMax)
+    BRS_LAUNCH_SLOT(64, 2, kSlotRegsMax)
+    BRS_LAUNCH_SLOT(128, 2, kSlotRegsMax)
 #undef BRS_LAUNCH_SLOT
     return hipErrorInvalidValue;
   }

@@ -104,6 +104,7 @@ struct AttnGeom {
   bool local_plan;        // split workgroups build their segments from idx (no plan kernel)
   bool slot;              // split workgroups read the selections directly (slot layout, no plan)
   int slot_ps, slot_bs;   // slot layout: padded sinks, slot stride (tokens)
+  int slot_regs;          // slot layout: selection entries per lane (8, or 20 past 512 entries)
   int depth;              // slot layout: tiles of loads in flight per wave
   int len_a, len_b;       // slot layout: sink/window tokens, slot tokens (padded)
   int64_t max_items;      // segments per (batch, kv head)

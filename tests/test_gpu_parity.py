@@ -41,6 +41,9 @@ SMALL = {
                                                 block=40, k=6),
     "f32_topnorm": W["tiny_decode"].scaled(n_q_heads=4, n_kv_heads=2, rep_mode="topnorm", reps_per_block=3,
                                             n_tokens=3000, block=50, k=5, window=64, sinks=10),
+    # 800 selection entries per kv slice (4 heads x k = 200): the wide slot layout (up to 1280 entries)
+    "retrieval_wide": W["retrievalattn_gqa_decode_1m_b8"].scaled(batch=1, n_q_heads=8, n_kv_heads=2,
+                                                                  n_tokens=16384 + 5, block=16, k=200),
     # two query heads per kv head: two selecting waves, six taking the sink/window tiles
     "gqa2": W["infllm_gqa_decode_128k"].scaled(n_q_heads=4, n_kv_heads=2, n_tokens=5000 + 3, window=300, k=7,
                                                planted_per_head=2),
@@ -327,8 +330,8 @@ def test_full_size_memlong_prefill_sampled():
     print(f"memlong: max |err| {res['max_abs_err']:.3g}")
 
 
-@pytest.mark.parametrize("name", ["infllm", "gqa8", "gqa2", "landmark", "retrieval", "memlong", "multi_q",
-                                  "prefill_gqa"])
+@pytest.mark.parametrize("name", ["infllm", "gqa8", "gqa2", "landmark", "retrieval", "retrieval_wide", "memlong",
+                                  "multi_q", "prefill_gqa"])
 def test_step_call_matches_separate_calls(name):
     """brs_retrieval_step (one call; for decode the attention kernel makes the
     selection itself) gives the same scores, selection and attention bits as
