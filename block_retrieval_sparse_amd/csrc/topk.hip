@@ -10,7 +10,8 @@
 //   k <= 512, up to 2048 candidates: one 256-thread workgroup per row, radix
 //     select of the k-th key with a 256-bin histogram in LDS, ties at it to
 //     the lowest indices, rank sort of the winners;
-//   otherwise: the same with 1024 threads, keys in registers or re-read.
+//   otherwise: the same with 1024 threads, keys in registers or re-read,
+//     one histogram per wave (atomics never contend across waves).
 #include "brs_wave_topk.h"
 
 namespace brs {
@@ -20,6 +21,8 @@ template <int NT, int KPT>  // KPT = 0: keys re-read from global memory each pas
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
                                                   int64_t hi, int k, int32_t* __restrict__ idx,
                                                   float* __restrict__ vals) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t whist[NW][256];  // one histogram per wave (no atomics across waves)
   __shared__ uint32_t hist[256];
   __shared__ int wave_tot[16];
   __shared__ uint32_t sh_digit;
@@ -40,17 +43,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
     for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) keys[i] = (my0 + i < my1) ? topk_key(s[my0 + i]) : 0u;
   }
-  auto key_at = [&](int64_t i) -> uint32_t {  // i relative to my0
-    if (KPT > 0) {
-      uint32_t r = 0;
-#pragma unroll
-      for (int j = 0; j < (KPT > 0 ? KPT : 1); ++j)
-        if (j == i) r = keys[j];
-      return r;
-    }
-    return topk_key(s[my0 + i]);
-  };
   const int64_t mine = my1 > my0 ? my1 - my0 : 0;
+  // f(i, key) for this thread's keys in index order (register keys: the
+  // loop is unrolled, so no register array is indexed at run time)
+  auto for_keys = [&](auto&& f) {
+    if constexpr (KPT > 0) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (i < mine) f((int64_t)i, keys[i]);
+    } else {
+      for (int64_t i = 0; i < mine; ++i) f(i, topk_key(s[my0 + i]));
+    }
+  };
 
   if (tid == 0) sel_count = 0;
   uint32_t thresh = 0;
@@ -61,11 +65,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     int kk = k;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      for (int i = tid; i < NW * 256; i += NT) whist[i >> 8][i & 255] = 0u;
       __syncthreads();
-      for (int64_t i = 0; i < mine; ++i) {
-        const uint32_t x = key_at(i);
-        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+      const int wv = tid >> 6;
+      for_keys([&](int64_t, uint32_t x) {
+        if ((x & mask) == prefix) atomicAdd(&whist[wv][(x >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      for (int i = tid; i < 256; i += NT) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += whist[w][i];
+        hist[i] = t;
       }
       __syncthreads();
       if (tid < 64) {
@@ -104,12 +115,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 
   // count my keys equal to the threshold, in index order
   int eq = 0;
-  if (!all)
-    for (int64_t i = 0; i < mine; ++i) eq += key_at(i) == thresh;
+  if (!all) for_keys([&](int64_t, uint32_t x) { eq += x == thresh; });
   const int eq_incl = block_inclusive_scan(all ? 0 : eq, wave_tot);
   int rank_eq = eq_incl - eq;
-  for (int64_t i = 0; i < mine; ++i) {
-    const uint32_t x = key_at(i);
+  for_keys([&](int64_t i, uint32_t x) {
     bool take = all || x > thresh;
     if (!all && x == thresh) {
       take = rank_eq < take_eq;
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       const uint32_t b = (uint32_t)(my0 + i);
       if (p < k) sel_key[p] = ((uint64_t)x << 32) | (uint64_t)(0xffffffffu - b);
     }
-  }
+  });
   __syncthreads();
   const int cnt = min(sel_count, k);
   int32_t* orow = idx + row * k;
