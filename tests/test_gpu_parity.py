@@ -233,6 +233,28 @@ def test_caller_selection_with_duplicates_and_skips(name):
             assert np.max(np.abs(out[b, h].cpu().numpy() - ref)) <= C.TOL[w.dtype], (b, h)
 
 
+def test_wide_caller_selection_with_repeats():
+    """1000 caller-made entries per kv slice (4 heads x 250, the wide slot
+    layout): random blocks with repeats within and across heads, -1 and
+    out-of-range entries; each head's output against the oracle on its own
+    attended set."""
+    w = SMALL["retrieval_wide"]
+    mem, x = C.load(w)
+    nb = w.n_blocks
+    rng = np.random.default_rng(2024)
+    idx = torch.from_numpy(rng.integers(-3, nb + 3, size=(w.batch, w.n_q_heads, 250)).astype(np.int32)).cuda()
+    out = mem.retrieval_attention(x["q"], idx, w.sinks, w.window)
+    torch.cuda.synchronize()
+    q, K, V = C.host(x["q"]), C.host(x["k"]), C.host(x["v"])
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            g = h // w.group
+            T = O.attended_mask(w.n_tokens, w.block, w.sinks, w.window,
+                                [i for i in idx[b, h].tolist() if 0 <= i < nb])
+            ref = O.attention(q[b, h], K[b, g], V[b, g], T, C.scale_of(w))
+            assert np.max(np.abs(out[b, h].cpu().numpy() - ref)) <= C.TOL[w.dtype], (b, h)
+
+
 def test_empty_set_gives_zeros_and_static_empty_is_an_error():
     import block_retrieval_sparse_amd as brs
 
