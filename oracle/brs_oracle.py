@@ -68,6 +68,7 @@ pinned to a printed value.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -168,16 +169,60 @@ def scores_dot_max(q: np.ndarray, reps: np.ndarray) -> np.ndarray:
     return dots.max(axis=1).astype(np.float32)
 
 
+def _exact_ints(v: np.ndarray) -> list:
+    """Every float64 of v as the exact integer v * 2**1074 (float64 values are
+    integer multiples of 2**-1074)."""
+    m, e = np.frexp(np.asarray(v, dtype=np.float64))
+    mi = np.ldexp(m, 53).astype(np.int64)  # exact: m has 53 significant bits
+    return [int(a) << int(b - 53 + 1074) if a >= 0 else -((-int(a)) << int(b - 53 + 1074))
+            for a, b in zip(mi.tolist(), e.tolist())]
+
+
+def _f32_nearest_signed_root(dot: int, prod: int) -> float:
+    """The float32 nearest to dot / sqrt(prod) (prod > 0), ties to even.
+
+    A float64 estimate fixes the neighbourhood; the choice between the
+    estimate's float32 and its two neighbours is then made exactly, by
+    comparing dot**2 with m**2 * prod for the midpoints m between them."""
+    a2 = Fraction(dot * dot, prod)           # the exact square of the magnitude
+    est = np.float32(math.sqrt(float(a2)))   # within a few float64 ulps of the magnitude
+    lo_, hi_ = np.nextafter(est, np.float32(-np.inf)), np.nextafter(est, np.float32(np.inf))
+    cands = [c for c in (lo_, est, hi_) if c >= 0]
+
+    def above(mid: Fraction) -> int:        # sign of (magnitude - mid), exactly
+        return (a2 > mid * mid) - (a2 < mid * mid)
+
+    best = cands[0]
+    for c0, c1 in zip(cands, cands[1:]):
+        mid = (Fraction(float(c0)) + Fraction(float(c1))) / 2
+        side = above(mid)
+        if side > 0:
+            best = c1
+        elif side == 0:  # a tie: the even significand
+            best = c0 if (int(np.float32(c0).view(np.uint32)) & 1) == 0 else c1
+            break
+        else:
+            break
+    return -float(best) if dot < 0 else float(best)
+
+
 def scores_cosine(rq: np.ndarray, E: np.ndarray) -> np.ndarray:
-    """s_b = float32( rq . e_b / (|rq| |e_b|) ), 0 when a norm is 0; E [nb][D]."""
-    dot = E @ rq
-    nq = math.sqrt(float(rq @ rq))
-    ne = np.sqrt((E * E).sum(axis=1))
-    den = nq * ne
-    s = np.zeros_like(dot)
-    ok = den != 0
-    s[ok] = dot[ok] / den[ok]
-    return s.astype(np.float32)
+    """s_b = float32( rq . e_b / (|rq| |e_b|) ), 0 when a norm is 0; E [nb][D].
+
+    The cosine of the stored vectors is evaluated exactly (integer sums of
+    exact products) and rounded once to the nearest float32, ties to even --
+    the same single rounding the dot-product scores get."""
+    q = _exact_ints(rq)
+    qq = sum(x * x for x in q)
+    out = np.zeros(E.shape[0], dtype=np.float32)
+    for b in range(E.shape[0]):
+        e = _exact_ints(E[b])
+        dot = sum(x * y for x, y in zip(q, e))
+        ee = sum(y * y for y in e)
+        if qq == 0 or ee == 0 or dot == 0:
+            continue
+        out[b] = _f32_nearest_signed_root(dot, qq * ee)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -209,15 +254,20 @@ def select_topk(scores: np.ndarray, lo: int, hi: int, k: int):
 def attended_mask(N: int, B: int, S: int, W: int, idx) -> np.ndarray:
     """Boolean [N]: sinks [0, S), window [max(N - W, 0), N), and every selected block.
 
-    A set: a token counted by several parts is still one token.
+    A set: a token counted by several parts is still one token.  Only
+    complete blocks can be selected (a partial tail block is never a
+    candidate), so a selection entry outside [0, floor(N / B)) names no block
+    and adds nothing -- -1 padding, and also an entry equal to the index of a
+    partial tail block.
     """
+    nb = N // B
     T = np.zeros(N, dtype=bool)
     T[: min(S, N)] = True
     T[max(N - W, 0):] = True
     for b in idx:
         b = int(b)
-        if b >= 0:
-            T[b * B: min((b + 1) * B, N)] = True
+        if 0 <= b < nb:
+            T[b * B:(b + 1) * B] = True
     return T
 
 

@@ -17,6 +17,7 @@ from __future__ import annotations
 import itertools
 import math
 import random
+from decimal import Decimal, localcontext
 from fractions import Fraction
 
 import numpy as np
@@ -189,6 +190,96 @@ def check_cosine():
     assert np.max(np.abs(O.scores_cosine(u, V) - (V @ u))) < 1e-7
 
 
+def _f32_from_decimal(c):
+    """The float32 nearest to the Decimal c, ties to even, decided with Decimal midpoints."""
+    f0 = np.float32(float(c))
+    cands = [np.nextafter(f0, np.float32(-np.inf)), f0, np.nextafter(f0, np.float32(np.inf))]
+    best = cands[0]
+    for c0, c1 in zip(cands, cands[1:]):
+        mid = (Decimal(float(c0)) + Decimal(float(c1))) / 2
+        if c > mid:
+            best = c1
+        elif c == mid:
+            best = c0 if (int(np.float32(c0).view(np.uint32)) & 1) == 0 else c1
+            break
+        else:
+            break
+    return float(best)
+
+
+def cosine_decimal(rq, e):
+    """Cosine of two float64 vectors in 400-digit decimal arithmetic (their
+    products and sums exact at this precision), rounded once to float32."""
+    with localcontext() as ctx:
+        ctx.prec = 400
+        xs = [Decimal(float(v)) for v in rq]
+        ys = [Decimal(float(v)) for v in e]
+        dot = sum(x * y for x, y in zip(xs, ys))
+        qq = sum(x * x for x in xs)
+        ee = sum(y * y for y in ys)
+        if qq == 0 or ee == 0:
+            return 0.0
+        return _f32_from_decimal(dot / (qq.sqrt() * ee.sqrt()))
+
+
+def near_tie_cosine_cases(n_cases: int, seed: int):
+    """Vectors whose cosine lies within 2**-53 (relative) of a float32
+    rounding midpoint, so that float64 evaluations of the formula fall on
+    either side of it.  rq is 768 ones and e holds integers below 2**24 with
+    sum S1 and square sum S2, so cos = S1 / sqrt(768 S2) exactly; S2 is the
+    integer (of the parity of S1) nearest to S1**2 / (768 m**2) for a float32
+    midpoint m, with S2 about 2**52."""
+    rng = random.Random(seed)
+    n = 768
+    out = []
+    for _ in range(n_cases):
+        f = np.float32(rng.uniform(0.05, 0.95))
+        m = (Fraction(float(f)) + Fraction(float(np.nextafter(f, np.float32(2.0))))) / 2
+        S1 = int(m * math.isqrt(n << 52)) + rng.randint(-999, 999)
+        target = Fraction(S1 * S1) / (n * m * m)
+        S2 = round(target)
+        if (S2 - S1) % 2:
+            S2 += 1 if S2 < target else -1
+        v, r = divmod(S1, n)
+        e = [v + 1] * r + [v] * (n - r)
+        gap = S2 - sum(x * x for x in e)
+        assert gap >= 0 and gap % 2 == 0
+        i = 0
+        while gap:  # move pairs of equal entries apart: +d and -d add 2 d**2
+            assert e[i] == e[i + 1]
+            d = max(1, min(math.isqrt(gap // 2), (1 << 24) - 1 - abs(e[i])))
+            e[i] += d
+            e[i + 1] -= d
+            gap -= 2 * d * d
+            i += 2
+        assert sum(e) == S1 and sum(x * x for x in e) == S2 and max(abs(x) for x in e) < 1 << 24
+        out.append((np.ones(n), np.array(e, dtype=np.float64)))
+    return out
+
+
+def check_cosine_exact_rounding():
+    """The cosine is the exact value rounded once to float32: equal, bit for
+    bit, to a 400-digit decimal evaluation rounded to the nearest float32 --
+    on random bfloat16 vectors and on vectors whose cosine sits within 2**-53
+    of a float32 rounding midpoint, where float64 formulas disagree."""
+    rng = np.random.default_rng(16)
+    rq = bf16_values(rng, (768,))
+    E = bf16_values(rng, (12, 768))
+    got = O.scores_cosine(rq, E)
+    for b in range(E.shape[0]):
+        assert float(got[b]) == cosine_decimal(rq, E[b]), b
+    ties = near_tie_cosine_cases(24, 17)
+    wrong_a = wrong_b = 0
+    for (q, e) in ties:
+        want = cosine_decimal(q, e)
+        assert float(O.scores_cosine(q, e[None])[0]) == want
+        qq, ee, dot = float(q @ q), float(e @ e), float(q @ e)
+        wrong_a += float(np.float32(dot / (math.sqrt(qq) * math.sqrt(ee)))) != want
+        wrong_b += float(np.float32(dot / math.sqrt(qq * ee))) != want
+    # the cases separate the exact value from both float64 formulas
+    assert wrong_a > 0 and wrong_b > 0, (wrong_a, wrong_b)
+
+
 def _key(s, b):
     return (1, 0.0, b) if math.isnan(s) else (0, -s, b)
 
@@ -278,6 +369,23 @@ def check_attention_set_by_zero_query():
                 toks |= set(range(b * B, (b + 1) * B))
             toks = sorted(t for t in toks if t <= p)
             assert np.allclose(got[j], V[toks].mean(axis=0), atol=1e-13, rtol=0), (trial, j)
+
+
+def check_attention_skips_entries_outside_complete_blocks():
+    """Entries that name no complete block add nothing: -1, negatives, indices
+    past the memory, and nb itself when a partial tail block sits there
+    outside the window (q = 0: the output is the mean of V over the set)."""
+    rng = np.random.default_rng(12)
+    N, B, S, W = 70, 8, 3, 4  # nb = 8, tail = tokens 64..69, window = 66..69
+    V = rng.standard_normal((N, 2))
+    K = rng.standard_normal((N, 2))
+    for extra in ([8], [-1], [-5, 9], [8, 8, 1000]):
+        idx = np.array([2, 5] + extra, dtype=np.int64)
+        T = O.attended_mask(N, B, S, W, idx)
+        toks = sorted(set(range(S)) | set(range(N - W, N)) | set(range(16, 24)) | set(range(40, 48)))
+        assert np.flatnonzero(T).tolist() == toks, extra
+        got = O.attention(np.zeros((1, 2)), K, V, T, 1.0)
+        assert np.allclose(got[0], V[toks].mean(axis=0), atol=1e-14, rtol=0)
 
 
 def check_attention_properties():
@@ -540,8 +648,10 @@ def check_prune_equal_hits_and_tail():
 
 CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_eligible_workloads,
           check_mean_exact, check_topnorm_bruteforce, check_dot_exact_mips, check_cosine,
+          check_cosine_exact_rounding,
           check_topk_bruteforce, check_topk_ties_and_nan, check_attention_full_causal,
-          check_attention_set_by_zero_query, check_attention_properties, check_gqa_is_replicated_mha,
+          check_attention_set_by_zero_query, check_attention_skips_entries_outside_complete_blocks,
+          check_attention_properties, check_gqa_is_replicated_mha,
           check_planted_recall, check_hand_worked_fixture, check_step_cosine_chunks,
           check_weights_and_lse_library, check_window_mass_zero_query, check_window_mass_conservation_and_range,
           check_reps_attnscore_bruteforce, check_count_hits_bincount, check_prune_characterisation,
@@ -642,6 +752,26 @@ def _mut_cos_no_qnorm(rq, E):
     return s.astype(np.float32)
 
 
+def _mut_cos_f64_norm_product(rq, E):
+    # float64 formula with the norms multiplied after their square roots
+    dot = E @ rq
+    den = math.sqrt(float(rq @ rq)) * np.sqrt((E * E).sum(axis=1))
+    s = np.zeros_like(dot)
+    ok = den != 0
+    s[ok] = dot[ok] / den[ok]
+    return s.astype(np.float32)
+
+
+def _mut_cos_f64_root_of_product(rq, E):
+    # float64 formula with one square root of the product of the squared norms
+    dot = E @ rq
+    den = np.sqrt(float(rq @ rq) * (E * E).sum(axis=1))
+    s = np.zeros_like(dot)
+    ok = den != 0
+    s[ok] = dot[ok] / den[ok]
+    return s.astype(np.float32)
+
+
 def _mut_topk_tie_high(scores, lo, hi, k):
     def key(b):
         s = float(scores[b])
@@ -685,6 +815,17 @@ def _mut_mask_block_short(N, B, S, W, idx):
     for b in idx:
         if int(b) >= 0:
             T[int(b) * B: min((int(b) + 1) * B - 1, N)] = True
+    return T
+
+
+def _mut_mask_tail_entry(N, B, S, W, idx):
+    # an entry equal to nb attends the partial tail block
+    T = np.zeros(N, dtype=bool)
+    T[: min(S, N)] = True
+    T[max(N - W, 0):] = True
+    for b in idx:
+        if int(b) >= 0:
+            T[int(b) * B: min((int(b) + 1) * B, N)] = True
     return T
 
 
@@ -827,10 +968,13 @@ MUTANTS = [
     ("scores_dot_max", _mut_dot_f32_accum),
     ("scores_dot_max", _mut_dot_mean_reps),
     ("scores_cosine", _mut_cos_no_qnorm),
+    ("scores_cosine", _mut_cos_f64_norm_product),
+    ("scores_cosine", _mut_cos_f64_root_of_product),
     ("select_topk", _mut_topk_tie_high),
     ("select_topk", _mut_topk_nan_first),
     ("attended_mask", _mut_mask_window_off_by_one),
     ("attended_mask", _mut_mask_block_short),
+    ("attended_mask", _mut_mask_tail_entry),
     ("attention", _mut_attention_no_causal),
     ("attention", _mut_attention_no_scale),
     ("attention", _mut_attention_transposed),
