@@ -10,7 +10,8 @@ import ctypes
 import os
 from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.environ.get("BRS_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbrs.so")
+# always the in-tree build next to this file
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbrs.so")
 
 BRS_F32, BRS_BF16 = 0, 1
 REP_MEAN, REP_TOPNORM, REP_GIVEN, REP_EMBED, REP_ATTNSCORE = 0, 1, 2, 3, 4

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbrs.so")
-ARCH = os.environ.get("BRS_OFFLOAD_ARCH", "gfx950")
+ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "memory.hip", "score.hip", "topk.hip", "attn_decode.hip", "attn_prefill.hip",
            "mass.hip", "prune.hip"]

@@ -32,14 +32,9 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 constexpr int kItemsLds = 256;  // segments of one chunk staged in LDS
-constexpr int kTargetWaves = 2048;
-
-// Tuning knobs (shape of the decomposition only; results do not depend on
-// them beyond float32 summation order): BRS_TARGET_WAVES, BRS_NW, BRS_U.
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
+constexpr int kTargetWaves = 2048;  // waves the split decomposition aims for
+constexpr int kSplitU = 2;          // vector split kernel: token steps per group
+constexpr int kSlotWgs = 256;       // slot layout: workgroups aimed for (about one per CU)
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -224,7 +219,7 @@ struct SplitArgs {
   int sel_lo, sel_hi;
   int32_t* idx_out;
   float* vals_out;
-  int n_units, per_xcd, xcd_map;  // one-dimensional grid of units
+  int n_units;                   // one-dimensional grid of units
 };
 
 template <typename T>
@@ -1052,9 +1047,8 @@ struct StepLds {
   int flag[kSelWaves];
 };
 
-template <int D, int KPTW, int DEPTH, int REGS = kSlotRegs>  // KPTW > 0: select in the kernel, KPTW scores
-                                                            // per lane; DEPTH tiles of loads in flight per
-                                                            // wave; REGS selection entries per lane
+template <int D, int KPTW, int REGS = kSlotRegs>  // KPTW > 0: select in the kernel, KPTW scores per
+                                                  // lane; REGS selection entries per lane
 __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<D, REGS>& sm, StepLds* st) {
   constexpr bool STEP = KPTW > 0;
   constexpr int KC = D / 32;  // 32-wide k chunks of the head dim
@@ -1312,9 +1306,8 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
 
   // Phase 1: waves 4-7 run their sink/window tiles (the prefetch past the
   // last one stays empty); waves 0-3 obtain the selections.  Phase 2, after
-  // the barrier: every wave runs its slot tiles.  (DEPTH: tiles of loads in
-  // flight per wave in phase 2.)
-  Tile ta, tb;
+  // the barrier: every wave runs its slot tiles.
+  Tile ta;
   if (fixw && fa > 0) {
     load(ta, 0, false);
     for (int it = 0; it < fa; ++it) step(ta, it + 1, false);
@@ -1356,15 +1349,7 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   }
   const int ns = n_tiles - fa;  // slot tiles of this wave
   load(ta, fa, true);
-  if (DEPTH == 1) {
-    for (int it = 0; it < ns; ++it) step(ta, fa + it + 1, true);
-  } else {
-    load(tb, fa + 1, true);
-    for (int it = 0; it < (ns + 1) / 2; ++it) {
-      step(ta, fa + 2 * it + 2, true);
-      step(tb, fa + 2 * it + 3, true);
-    }
-  }
+  for (int it = 0; it < ns; ++it) step(ta, fa + it + 1, true);
 
   // row sums over the four lanes that share a query row
   lpart += __shfl_xor(lpart, 16);
@@ -1398,31 +1383,30 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   }
 }
 
-// units dealt to the XCDs in contiguous runs (workgroup w runs on XCD w % 8)
-__device__ __forceinline__ int slot_unit_index(const SplitArgs& a) {
-  const int xcd = blockIdx.x % kXcdCount, wslot = blockIdx.x / kXcdCount;
-  return a.xcd_map ? xcd * a.per_xcd + wslot : blockIdx.x;
-}
+// Units go out in dispatch order, which deals them round-robin over the 8
+// XCDs: every XCD gets an eighth of each kv slice's chunks, which balances
+// the slices' unequal work (measured 0.4-0.9 us faster per step than one
+// slice per XCD).
 
 // Attention over the slot layout with the selections read from idx.
-template <int D, int DEPTH, int REGS>
+template <int D, int REGS>
 __global__ __launch_bounds__(64 * kSlotWaves) void attn_split_slot_kernel(SplitArgs a) {
   __shared__ SlotLds<D, REGS> sm;
-  const int unit = slot_unit_index(a);
+  const int unit = blockIdx.x;
   if (unit >= a.n_units) return;
-  slot_unit<D, 0, DEPTH, REGS>(a, unit, sm, nullptr);
+  slot_unit<D, 0, REGS>(a, unit, sm, nullptr);
 }
 
 // The whole decode step after scoring: the selection of every score row of
 // the kv slice (written out by the slice's first workgroup), then the same
 // attention as attn_split_slot_kernel -- identical partials.
-template <int D, int KPTW, int DEPTH>
+template <int D, int KPTW>
 __global__ __launch_bounds__(64 * kSlotWaves) void attn_step_kernel(SplitArgs a) {
   __shared__ SlotLds<D> sm;
   __shared__ StepLds st;
-  const int unit = slot_unit_index(a);
+  const int unit = blockIdx.x;
   if (unit >= a.n_units) return;
-  slot_unit<D, KPTW, DEPTH>(a, unit, sm, &st);
+  slot_unit<D, KPTW>(a, unit, sm, &st);
 }
 
 // Any head_dim <= 512 and any row stride: one token at a time per wave,
@@ -1515,32 +1499,18 @@ __global__ __launch_bounds__(64) void attn_split_generic_kernel(SplitArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 
-template <typename T, int ROWS>
-constexpr int dpl_for() {
-  return ROWS <= 4 ? 32 / (int)sizeof(T) : 16 / (int)sizeof(T);
-}
-
 template <int D, int ROWS>
 constexpr int nwmax_for() {
   return ROWS * D <= 1024 ? 8 : 4;
 }
 
-// elements per lane for <= 4 rows: 16 bytes (16 lanes per 128-dim bf16 row:
-// fewer registers, more waves) by default; BRS_NARROW=0 uses 32 bytes
-bool split_narrow() { return env_int("BRS_NARROW", 1) == 1; }
-
-int split_u() {
-  const int u = env_int("BRS_U", 2);
-  return (u == 1 || u == 4) ? u : 2;
-}
-
-// tokens of one group of the vector kernel (TPS * U)
+// Each lane holds 16 bytes of a row (16 lanes per 128-dim bf16 row: fewer
+// registers and more waves than 32 bytes per lane, measured faster).
+// Tokens of one group of the vector kernel: TPS * U.
 int step_tokens(const AttnGeom& g) {
   const int es = elem_bytes(g.dtype);
-  const int rows = g.rows_per_group;
-  const int dpl = (rows <= 4 && !split_narrow()) ? 32 / es : 16 / es;
-  const int L = g.d / dpl;
-  return (64 / L) * split_u();
+  const int L = g.d / (16 / es);
+  return (64 / L) * kSplitU;
 }
 
 int nw_max(const AttnGeom& g) {
@@ -1552,37 +1522,21 @@ template <typename T, int D>
 bool launch_fast_d(const AttnGeom& g, dim3 grid, dim3 block, hipStream_t s, const SplitArgs& a, hipEvent_t ev0,
                    hipEvent_t ev1) {
   const int rows = g.rows_per_group;
-  const int u = split_u();
-#define BRS_LAUNCH_U(R, UU)                                                                                   \
-  if (R <= 4 && split_narrow()) {                                                                             \
-    constexpr int DPL = 16 / (int)sizeof(T);                                                                  \
-    constexpr int NWM = nwmax_for<D, R>();                                                                    \
-    if (ev0)                                                                                                  \
-      hipExtLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, ev0, ev1, 0, a);   \
-    else                                                                                                      \
-      hipLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, a);                   \
-    return true;                                                                                              \
-  } else {                                                                                                    \
-    constexpr int DPL = dpl_for<T, R>();                                                                      \
-    constexpr int NWM = nwmax_for<D, R>();                                                                    \
-    if (ev0)                                                                                                  \
-      hipExtLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, ev0, ev1, 0, a);   \
-    else                                                                                                      \
-      hipLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, UU, NWM>), grid, block, 0, s, a);                   \
-    return true;                                                                                              \
-  }
+  constexpr int DPL = 16 / (int)sizeof(T);
 #define BRS_LAUNCH_ROWS(R)                                                                                    \
   if (rows <= R) {                                                                                            \
-    if (u == 1) { BRS_LAUNCH_U(R, 1) }                                                                        \
-    if (u == 4) { BRS_LAUNCH_U(R, 4) }                                                                        \
-    BRS_LAUNCH_U(R, 2)                                                                                        \
+    constexpr int NWM = nwmax_for<D, R>();                                                                    \
+    if (ev0)                                                                                                  \
+      hipExtLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, kSplitU, NWM>), grid, block, 0, s, ev0, ev1, 0, a); \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attn_split_kernel<T, D, DPL, R, kSplitU, NWM>), grid, block, 0, s, a);             \
+    return true;                                                                                              \
   }
   BRS_LAUNCH_ROWS(1)
   BRS_LAUNCH_ROWS(2)
   BRS_LAUNCH_ROWS(4)
   BRS_LAUNCH_ROWS(8)
 #undef BRS_LAUNCH_ROWS
-#undef BRS_LAUNCH_U
   return false;
 }
 
@@ -1601,7 +1555,7 @@ bool attn_geometry(AttnGeom& g) {
   const int64_t uniq = E < g.nb ? E : g.nb;
   const int rows = g.group * g.n_q;
   g.fast = fast_supported(g);
-  g.mfma = g.fast && g.dtype == BRS_BF16 && g.d <= 128 && env_int("BRS_MFMA", 1) != 0;
+  g.mfma = g.fast && g.dtype == BRS_BF16 && g.d <= 128;
   const int rmax = g.mfma ? 16 : kRowsMax;
   g.row_groups = (rows + rmax - 1) / rmax;
   g.rows_per_group = rows < rmax ? rows : rmax;
@@ -1612,7 +1566,7 @@ bool attn_geometry(AttnGeom& g) {
   g.prefill = prefill_supported(g);
   // slot layout: every selection entry gets its own padded slot
   g.slot = g.mfma && !g.prefill && E >= 1 && E <= 64 * kSlotRegsMax && E <= g.nb &&
-           g.head_stride * 2 < (int64_t)kSlotOOR - 4096 && env_int("BRS_SLOT", 1) != 0;
+           g.head_stride * 2 < (int64_t)kSlotOOR - 4096;
   g.slot_regs = E <= 64 * kSlotRegs ? kSlotRegs : kSlotRegsMax;
   if (g.slot) {
     auto pad32 = [](int64_t x) { return (x + 31) / 32 * 32; };
@@ -1626,8 +1580,7 @@ bool attn_geometry(AttnGeom& g) {
   // tokens per wave: about kTargetWaves waves over the whole problem, in whole steps
   const int64_t total = g.max_tokens * bg * g.row_groups;
   const int st = g.mfma ? 32 : (g.fast ? step_tokens(g) : 1);
-  const int target = env_int("BRS_TARGET_WAVES", kTargetWaves);
-  int64_t wt = (total + target - 1) / target;
+  int64_t wt = (total + kTargetWaves - 1) / kTargetWaves;
   wt = ((wt + st - 1) / st) * st;
   const int64_t wmin = g.mfma ? 32 : (g.fast ? 2 * st : 16);
   wt = wt < wmin ? wmin : (wt > 4096 ? 4096 : wt);
@@ -1635,10 +1588,6 @@ bool attn_geometry(AttnGeom& g) {
   const int64_t waves = (total + wt - 1) / wt;
   const int nwm = g.mfma ? (g.d <= 128 ? 8 : 4) : nw_max(g);
   g.nw = !g.fast ? 1 : (waves >= 2048 ? nwm : (waves >= 1024 ? 4 : 1));
-  if (g.fast) {
-    const int nw_env = env_int("BRS_NW", 0);
-    if (nw_env == 1 || nw_env == 2 || nw_env == 4 || (nw_env == 8 && nwm == 8)) g.nw = nw_env;
-  }
   // a chunk meets at most chunk_tokens / B + 6 segments (sinks, window, the two
   // blocks cut by them, whole blocks, one more at each end): keep them in LDS
   if (!g.slot) {
@@ -1654,11 +1603,10 @@ bool attn_geometry(AttnGeom& g) {
     // about one four-wave workgroup per CU, each wave with at least one tile
     const int units = g.batch * g.hkv * g.row_groups;
     const int tiles = (int)(g.max_tokens / 32);
-    int nc = env_int("BRS_SLOT_WGS", 256) / units;
+    int nc = kSlotWgs / units;
     nc = nc > tiles / kSlotWaves ? tiles / kSlotWaves : nc;
     g.nw = kSlotWaves;
     g.max_chunks = nc < 1 ? 1 : nc;
-    g.depth = env_int("BRS_DEPTH", 1) == 2 ? 2 : 1;
   }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows_total = (size_t)g.batch * g.hq * g.n_q;
@@ -1670,7 +1618,7 @@ bool attn_geometry(AttnGeom& g) {
   {
     const int64_t W = ((int64_t)g.nb + 31) / 32;
     const int64_t hb = g.idx_heads == 1 ? 1 : g.group;
-    g.local_plan = !g.prefill && !g.slot && hb * W <= kPlanWords && env_int("BRS_LOCAL_PLAN", 1) != 0;
+    g.local_plan = !g.prefill && !g.slot && hb * W <= kPlanWords;
   }
   const size_t parts = g.prefill ? 0 : rows_total * g.max_chunks;
   g.o_off = g.ml_off + up(parts * sizeof(float2));
@@ -1756,21 +1704,15 @@ SplitArgs split_args(const AttnGeom& g, const void* k, const void* v, const void
   a.out = out;
   slot_args(g, a);
   a.n_units = g.max_chunks * g.batch * g.hkv * g.row_groups;
-  a.per_xcd = (a.n_units + kXcdCount - 1) / kXcdCount;
-  // units in dispatch order (round-robin over the XCDs): every XCD gets an
-  // eighth of each kv slice's chunks, which balances the slices' unequal work
-  // (measured 0.9 us faster per step than one slice per XCD)
-  a.xcd_map = env_int("BRS_XCD", 0) != 0;
   return a;
 }
-unsigned slot_grid(const SplitArgs& a) { return (unsigned)(a.xcd_map ? a.per_xcd * kXcdCount : a.n_units); }
+unsigned slot_grid(const SplitArgs& a) { return (unsigned)a.n_units; }
 }  // namespace
 
 bool step_supported(const AttnGeom& g, int64_t lo, int64_t hi, int k) {
   const int R = g.idx_heads == 1 ? 1 : g.group;
   return g.slot && g.slot_regs == kSlotRegs && R <= kSelWaves && k >= 1 && k <= kStepK && hi - lo <= 64 * 32 &&
-         (g.d == 64 || g.d == 128) &&
-         env_int("BRS_STEP", 1) != 0;
+         (g.d == 64 || g.d == 128);
 }
 
 hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, const void* q, const float* scores,
@@ -1785,15 +1727,14 @@ hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, con
   a.vals_out = vals;
   const dim3 grid(slot_grid(a)), block(64 * kSlotWaves);
   const int64_t n = hi - lo;
-#define BRS_LAUNCH_STEP1(DD, KP, DEP)                                                               \
-  if (g.d == DD && g.depth == DEP) {                                                                \
+#define BRS_LAUNCH_STEP(DD, KP)                                                                     \
+  if (g.d == DD) {                                                                                  \
     if (ev0 || ev1)                                                                                 \
-      hipExtLaunchKernelGGL((attn_step_kernel<DD, KP, DEP>), grid, block, 0, s, ev0, ev1, 0, a);    \
+      hipExtLaunchKernelGGL((attn_step_kernel<DD, KP>), grid, block, 0, s, ev0, ev1, 0, a);         \
     else                                                                                            \
-      hipLaunchKernelGGL((attn_step_kernel<DD, KP, DEP>), grid, block, 0, s, a);                    \
+      hipLaunchKernelGGL((attn_step_kernel<DD, KP>), grid, block, 0, s, a);                         \
     return hipGetLastError();                                                                       \
   }
-#define BRS_LAUNCH_STEP(DD, KP) BRS_LAUNCH_STEP1(DD, KP, 1) BRS_LAUNCH_STEP1(DD, KP, 2)
   if (n <= 256) {
     BRS_LAUNCH_STEP(64, 4)
     BRS_LAUNCH_STEP(128, 4)
@@ -1808,7 +1749,6 @@ hipError_t launch_attn_step(const AttnGeom& g, const void* k, const void* v, con
     BRS_LAUNCH_STEP(128, 32)
   }
 #undef BRS_LAUNCH_STEP
-#undef BRS_LAUNCH_STEP1
   return hipErrorInvalidValue;
 }
 
@@ -1818,22 +1758,18 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
   if (g.slot) {
     const dim3 grid1(slot_grid(a)), block(64 * kSlotWaves);
-#define BRS_LAUNCH_SLOT(DD, DEP, RG)                                                                     \
-  if (g.d == DD && g.depth == DEP && g.slot_regs == RG) {                                                \
+#define BRS_LAUNCH_SLOT(DD, RG)                                                                          \
+  if (g.d == DD && g.slot_regs == RG) {                                                                  \
     if (ev0)                                                                                             \
-      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, DEP, RG>), grid1, block, 0, s, ev0, ev1, 0, a);  \
+      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, RG>), grid1, block, 0, s, ev0, ev1, 0, a);       \
     else                                                                                                 \
-      hipLaunchKernelGGL((attn_split_slot_kernel<DD, DEP, RG>), grid1, block, 0, s, a);                  \
+      hipLaunchKernelGGL((attn_split_slot_kernel<DD, RG>), grid1, block, 0, s, a);                       \
     return hipGetLastError();                                                                            \
   }
-    BRS_LAUNCH_SLOT(64, 1, kSlotRegs)
-    BRS_LAUNCH_SLOT(128, 1, kSlotRegs)
-    BRS_LAUNCH_SLOT(64, 2, kSlotRegs)
-    BRS_LAUNCH_SLOT(128, 2, kSlotRegs)
-    BRS_LAUNCH_SLOT(64, 1, kSlotRegsMax)
-    BRS_LAUNCH_SLOT(128, 1, kSlotRegsMax)
-    BRS_LAUNCH_SLOT(64, 2, kSlotRegsMax)
-    BRS_LAUNCH_SLOT(128, 2, kSlotRegsMax)
+    BRS_LAUNCH_SLOT(64, kSlotRegs)
+    BRS_LAUNCH_SLOT(128, kSlotRegs)
+    BRS_LAUNCH_SLOT(64, kSlotRegsMax)
+    BRS_LAUNCH_SLOT(128, kSlotRegsMax)
 #undef BRS_LAUNCH_SLOT
     return hipErrorInvalidValue;
   }

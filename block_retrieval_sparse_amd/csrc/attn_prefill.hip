@@ -72,11 +72,6 @@ struct PrefillArgs {
 
 __device__ __forceinline__ bf16x8_p as_bf16x8_p(const uint4& u) { return __builtin_bit_cast(bf16x8_p, u); }
 
-int env_flag(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
-
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int CTRL>
@@ -506,7 +501,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_supported(const AttnGeom& g) {
-  if (env_flag("BRS_PREFILL", 1) == 0) return false;
   return g.dtype == BRS_BF16 && g.n_q >= kPrefQ && g.d <= 128 && g.d % 2 == 0 && g.row_stride % 8 == 0 &&
          ((g.d + 7) / 8) * 8 <= g.row_stride && g.k + 2 <= kPrefItems &&
          g.head_stride * 2 < (int64_t)kOutOfRange - 4096 && (int64_t)g.n_q * g.d * 2 < (int64_t)kOutOfRange - 4096;
