@@ -20,11 +20,11 @@ REP_MODES = {"mean": REP_MEAN, "topnorm": REP_TOPNORM, "given": REP_GIVEN, "embe
 ERRORS = {0: "BRS_OK", -1: "BRS_E_INVAL", -2: "BRS_E_CAPACITY", -3: "BRS_E_UNSUPPORTED",
           -4: "BRS_E_HIP", -5: "BRS_E_EMPTY", -6: "BRS_E_WORKSPACE"}
 
-# every symbol include/brs.h declares
+# every symbol include/brs.h and include/brs_measure.h declare
 EXPORTS = ["brs_version", "brs_last_error", "brs_memory_check", "brs_mem_append", "brs_eligible_range",
            "brs_score_blocks", "brs_select_topk", "brs_attention_workspace_bytes",
            "brs_retrieval_attention", "brs_retrieval_step", "brs_window_mass", "brs_reps_from_mass",
-           "brs_count_hits", "brs_mem_prune", "brs_profile_next_attention"]
+           "brs_count_hits", "brs_mem_prune", "brs_profile_next_attention", "brs_measure_read"]
 
 
 class brs_memory(ctypes.Structure):
@@ -71,6 +71,7 @@ def _load():
         "brs_count_hits": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
         "brs_mem_prune": (c_int, [P, c_void_p, P, c_void_p, c_void_p, c_void_p]),
         "brs_profile_next_attention": (c_int, [c_void_p, c_void_p]),
+        "brs_measure_read": (c_int, [c_void_p, c_int64, c_void_p, c_int64, ctypes.c_uint32, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

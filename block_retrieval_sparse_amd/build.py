@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libbrs.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "memory.hip", "score.hip", "topk.hip", "attn_decode.hip", "attn_prefill.hip",
-           "mass.hip", "prune.hip"]
+           "mass.hip", "prune.hip", "measure.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",

@@ -1,5 +1,5 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports
-every symbol include/brs.h declares, and rejects bad arguments on the host
+every symbol include/*.h declare, and rejects bad arguments on the host
 before any device work; brs_eligible_range matches the oracle's brute force.
 """
 from __future__ import annotations
@@ -11,7 +11,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "brs.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,7 +23,7 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(brs_\w+)\s*\(", text, flags=re.M)))
 
 
