@@ -5,7 +5,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "brs_internal.h"
+
+// Workspace of brs_retrieval_step_static: one array per GPU, held from the
+// library's load until the process ends.  Host code must not use this name as
+// an address (on the host it is only a stand-in for the symbol); the device
+// address comes from hipGetSymbolAddress, per device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -63,6 +72,29 @@ int check_memory(const brs_memory* m) {
   if (!m->k || !m->v || !m->reps) return fail(BRS_E_INVAL, "k, v and reps must be non-NULL");
   if (!aligned(m->k, 16) || !aligned(m->v, 16) || !aligned(m->reps, 16))
     return fail(BRS_E_INVAL, "k, v and reps must be 16-byte aligned");
+  return BRS_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(BRS_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(BRS_E_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return BRS_OK;
 }
 
@@ -333,6 +365,27 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
   }
   return run_attention(g, m, q, k > 0 ? idx : nullptr, out, lse, workspace, s);
 }
+
+int brs_retrieval_step_static(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
+                              const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
+                              float* scores, int32_t* idx, float* vals, float* out, float* lse, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  const int32_t hs = m->rep_mode == BRS_REP_EMBED ? 1 : n_q_heads;
+  brs::AttnGeom g;
+  rc = attn_setup(m, n_q_heads, n_q, hs, k, n_sink, window, scale, g);
+  if (rc) return rc;
+  if (g.total > kStaticScratchBytes)
+    return fail(BRS_E_UNSUPPORTED, "this step needs %zu bytes of workspace; the static scratch holds %zu",
+                g.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc) return rc;
+  return brs_retrieval_step(m, q, n_q_heads, n_q, qrep, k, n_sink, window, scale, scores, idx, vals, out, lse, ws,
+                            kStaticScratchBytes, stream);
+}
+
+size_t brs_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 int brs_window_mass(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const float* lse,
                     int64_t window, float scale, float* mass, void* stream) {

@@ -246,6 +246,27 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
                        float* scores, int32_t* idx, float* vals, float* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* brs_retrieval_step for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: the same step with the same results, its workspace taken from a
+ * library-held device array of brs_static_scratch_bytes() bytes (16 MiB) per
+ * GPU instead of a caller buffer.  Arguments, outputs and errors as
+ * brs_retrieval_step without workspace / workspace_bytes; additionally
+ * BRS_E_UNSUPPORTED when the step needs more workspace than the array holds
+ * (brs_attention_workspace_bytes tells), and BRS_E_HIP if the array's address
+ * cannot be obtained.  The array belongs to the device current at the call
+ * (its address is looked up once per device); the stream must be on that
+ * device.  It allocates nothing (no hipMalloc, hipFree or allocating library
+ * call).  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (on different streams, or from several threads without ordering)
+ * race on it.  Nothing in it needs to start at zero. */
+int brs_retrieval_step_static(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
+                              const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
+                              float* scores, int32_t* idx, float* vals, float* out, float* lse, void* stream);
+
+/* Bytes of the per-GPU array brs_retrieval_step_static works in. */
+size_t brs_static_scratch_bytes(void);
+
 /* Attention mass of the local window (InfLLM "method": the attention scores
  * each token receives decide which tokens represent its memory unit).  After
  * an attention call with queries q (same n_q_heads, n_q, scale) that wrote
