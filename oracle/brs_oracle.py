@@ -21,10 +21,10 @@ softmax attention over the local context plus the selected blocks.
   embedding r^m = r^q).
 * O2 eligibility (``eligible_range``): InfLLM "method" -- the memory holds
   what lies outside the local window.
-* O3 scores (``scores_dot_max``, ``scores_cosine``): Landmark "proposed
-  method" (similarity between the query and the landmark key), InfLLM
-  "method" (block-level relevance), MemLong section 2.3.2 (cosine similarity
-  between r^q and the stored embeddings).
+* O3 scores (``scores_dot_max``, ``scores_group_max``, ``scores_cosine``):
+  Landmark "proposed method" (similarity between the query and the landmark
+  key), InfLLM "method" (block-level relevance), MemLong section 2.3.2
+  (cosine similarity between r^q and the stored embeddings).
 * O4 selection (``select_topk``): MemLong section 2.3.2 (TopK of the cosine
   scores, done with an exact index, section 2.4.2).
 * O5 attended set (``attended_mask``): InfLLM "method" (local tokens plus a
@@ -46,7 +46,9 @@ notes): attention sinks are the first S tokens; the window is the last W
 tokens of memory; a partial tail block is never a candidate; a block wholly
 inside sinks or window is not a candidate; ties go to the lower block index
 and NaN ranks last; scores are exact-product float64 sums rounded once to
-float32; softmax scale is 1/sqrt(d) and scores carry no scale; query head h
+float32 (a cosine is the exact value rounded once); when the query heads of a
+kv head share one selection, a block's score is the maximum over those heads
+(as over a block's several representatives); softmax scale is 1/sqrt(d) and scores carry no scale; query head h
 reads kv head h // G; several representatives combine by max; the selection
 is per query head for dot scores and per sequence for cosine scores; local
 and retrieved tokens share one softmax with no gate; query j of n sits at
@@ -204,6 +206,18 @@ def _f32_nearest_signed_root(dot: int, prod: int) -> float:
         else:
             break
     return -float(best) if dot < 0 else float(best)
+
+
+def scores_group_max(Qg: np.ndarray, reps: np.ndarray) -> np.ndarray:
+    """One score per block for a whole group of query heads sharing a kv head:
+    s_b = float32( max over the group's heads h and the block's reps r of
+    q_h . rep_{b,r} ), exact products summed in float64; Qg [G][d], reps
+    [nb][R][d].  A group that shares one selection ranks a block by its best
+    match with any of its heads, the same way several representatives of a
+    block combine (by max).  NaN in any head's dot makes the score NaN.
+    """
+    dots = np.einsum("grd,hd->grh", reps, Qg)  # [nb][R][G], float64
+    return dots.reshape(dots.shape[0], -1).max(axis=1).astype(np.float32)
 
 
 def scores_cosine(rq: np.ndarray, E: np.ndarray) -> np.ndarray:
@@ -429,13 +443,17 @@ def build_reps(K_bg: np.ndarray, mode: str, B: int, R: int, dtype: str, given=No
 
 
 def step(q, K, V, reps, *, block: int, k: int, sinks: int, window: int, mode: str,
-         rq=None, scale=None, heads=None):
+         rq=None, scale=None, heads=None, select: str = "head"):
     """One pass of the path (O3 -> O6) with representatives already built.
 
     q [β][Hq][n][d], K/V [β][Hkv][N][d], reps [β][Hr][nb][R][Dr] (all float64),
     rq [β][Dr] for cosine scoring.  ``heads`` limits the work to a list of
-    (β, h) pairs.  Returns dicts keyed by (β, h) -- for cosine scoring the
-    score/selection key is (β, 0) -- of scores, idx, vals and out.
+    (β, h) pairs.  ``select`` is "head" (one selection per query head) or
+    "group" (one per kv head, shared by its query heads, from
+    ``scores_group_max`` of their last queries); cosine scoring always makes
+    one selection per sequence.  Returns dicts of scores, idx, vals and out:
+    out keyed by (β, h); scores/idx/vals keyed by (β, h), (β, g) for group
+    selection, or (β, 0) for cosine scoring.
     """
     Bt, Hq, n, d = q.shape
     Hkv, N = K.shape[1], K.shape[2]
@@ -451,6 +469,14 @@ def step(q, K, V, reps, *, block: int, k: int, sinks: int, window: int, mode: st
             if key not in res["idx"]:
                 s = np.full(nb_all, np.nan, dtype=np.float32)
                 s[lo:hi] = scores_cosine(rq[b], reps[b, 0, lo:hi, 0, :])
+                res["scores"][key] = s
+                res["idx"][key], res["vals"][key] = select_topk(s, lo, hi, k)
+        elif select == "group":
+            key = (b, g)
+            if key not in res["idx"]:
+                G = Hq // Hkv
+                s = np.full(nb_all, np.nan, dtype=np.float32)
+                s[lo:hi] = scores_group_max(q[b, g * G:(g + 1) * G, -1], reps[b, g, lo:hi])
                 res["scores"][key] = s
                 res["idx"][key], res["vals"][key] = select_topk(s, lo, hi, k)
         else:

@@ -169,6 +169,52 @@ def check_dot_exact_mips():
     assert np.array_equal(O.scores_dot_max(q, np.repeat(r, 4, axis=1)), O.scores_dot_max(q, r))
 
 
+def check_group_max():
+    """Group scores (one selection per kv head): brute force over every
+    (head, representative) pair on small integer vectors, whose dots are
+    exact in float32; a group of one head is the per-head score; the head
+    order and a repeated head change nothing; a block planted for one head
+    of the group wins the group's selection."""
+    rng = np.random.default_rng(18)
+    for trial in range(20):
+        G, nb, R, d = int(rng.integers(1, 5)), int(rng.integers(1, 7)), int(rng.integers(1, 4)), 6
+        Qg = rng.integers(-4, 5, size=(G, d)).astype(np.float64)
+        reps = rng.integers(-4, 5, size=(nb, R, d)).astype(np.float64)
+        want = [max(sum(int(Qg[h, i]) * int(reps[b, r, i]) for i in range(d)) for h in range(G) for r in range(R))
+                for b in range(nb)]
+        assert O.scores_group_max(Qg, reps).tolist() == [float(v) for v in want], trial
+        perm = rng.permutation(G)
+        assert np.array_equal(O.scores_group_max(Qg[perm], reps), O.scores_group_max(Qg, reps))
+        assert np.array_equal(O.scores_group_max(np.concatenate([Qg, Qg[:1]]), reps), O.scores_group_max(Qg, reps))
+    q = bf16_values(rng, (1, 64))
+    reps = bf16_values(rng, (30, 2, 64))
+    assert np.array_equal(O.scores_group_max(q, reps), O.scores_dot_max(q[0], reps))
+    # planted: block 17 carries 0.8 q of head 2 of 4
+    Qg = bf16_values(rng, (4, 64))
+    reps = bf16_values(rng, (40, 1, 64))
+    reps[17, 0] = 0.8 * Qg[2] + 0.1 * reps[17, 0]
+    idx, _ = O.select_topk(O.scores_group_max(Qg, reps), 0, 40, 1)
+    assert idx.tolist() == [17]
+    # one step with group selection: every head of a kv head attends the same blocks
+    Hq, Hkv, N, B, dd = 4, 2, 160, 16, 8
+    qs = rng.standard_normal((1, Hq, 1, dd))
+    K = rng.standard_normal((1, Hkv, N, dd))
+    V = rng.standard_normal((1, Hkv, N, dd))
+    rp = np.stack([np.stack([O.reps_mean(K[0, g], B, "f32") for g in range(Hkv)])])
+    res = O.step(qs, K, V, rp, block=B, k=3, sinks=0, window=16, mode="mean", select="group")
+    for g in range(Hkv):
+        sg = O.scores_group_max(qs[0, 2 * g:2 * g + 2, -1], rp[0, g, 0:9])
+        assert np.array_equal(res["scores"][(0, g)][0:9], sg)
+        for h in (2 * g, 2 * g + 1):
+            T = O.attended_mask(N, B, 0, 16, res["idx"][(0, g)])
+            assert np.array_equal(res["out"][(0, h)], O.attention(qs[0, h], K[0, g], V[0, g], T, 1 / math.sqrt(dd)))
+    one = O.step(qs[:, :2], K[:, :2], V[:, :2], rp[:, :2], block=B, k=3, sinks=0, window=16, mode="mean")
+    same = O.step(qs[:, :2], K[:, :2], V[:, :2], rp[:, :2], block=B, k=3, sinks=0, window=16, mode="mean",
+                  select="group")
+    for h in range(2):
+        assert np.array_equal(one["idx"][(0, h)], same["idx"][(0, h)])
+
+
 def check_cosine():
     from scipy.spatial.distance import cosine as scipy_cosine_distance
 
@@ -648,7 +694,7 @@ def check_prune_equal_hits_and_tail():
 
 CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_eligible_workloads,
           check_mean_exact, check_topnorm_bruteforce, check_dot_exact_mips, check_cosine,
-          check_cosine_exact_rounding,
+          check_cosine_exact_rounding, check_group_max,
           check_topk_bruteforce, check_topk_ties_and_nan, check_attention_full_causal,
           check_attention_set_by_zero_query, check_attention_skips_entries_outside_complete_blocks,
           check_attention_properties, check_gqa_is_replicated_mha,
@@ -770,6 +816,15 @@ def _mut_cos_f64_root_of_product(rq, E):
     ok = den != 0
     s[ok] = dot[ok] / den[ok]
     return s.astype(np.float32)
+
+
+def _mut_group_mean(Qg, reps):
+    dots = np.einsum("grd,hd->grh", reps, Qg)
+    return dots.max(axis=1).mean(axis=1).astype(np.float32)
+
+
+def _mut_group_first_head(Qg, reps):
+    return O.scores_dot_max(Qg[0], reps)
 
 
 def _mut_topk_tie_high(scores, lo, hi, k):
@@ -967,6 +1022,8 @@ MUTANTS = [
     ("reps_topnorm", _mut_topnorm_l1),
     ("scores_dot_max", _mut_dot_f32_accum),
     ("scores_dot_max", _mut_dot_mean_reps),
+    ("scores_group_max", _mut_group_mean),
+    ("scores_group_max", _mut_group_first_head),
     ("scores_cosine", _mut_cos_no_qnorm),
     ("scores_cosine", _mut_cos_f64_norm_product),
     ("scores_cosine", _mut_cos_f64_root_of_product),
