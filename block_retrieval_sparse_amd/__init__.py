@@ -14,7 +14,7 @@ import torch
 from . import _lib
 from ._lib import BrsError, REP_MODES, check, lib
 
-__all__ = ["KVMemory", "select_topk", "BrsError", "lib", "version"]
+__all__ = ["KVMemory", "BlockCache", "select_topk", "BrsError", "lib", "version"]
 
 
 def version() -> int:
@@ -43,19 +43,28 @@ class KVMemory:
 
     K and V are ``[batch][n_kv_heads][capacity][row_stride]``; reps are
     ``[batch][rep_heads][capacity // block][reps_per_block][rep_dim]``.
+    With ``host=True`` K and V live in pinned host memory (the device reads
+    and writes them directly; attention then goes through a
+    :class:`BlockCache`), the representatives in device memory.
     """
 
     def __init__(self, batch: int, n_kv_heads: int, head_dim: int, capacity: int, block_size: int,
                  dtype: torch.dtype = torch.bfloat16, rep_mode: str = "mean", reps_per_block: int = 1,
                  rep_dim: int | None = None, rep_dtype: torch.dtype | None = None,
-                 row_stride: int | None = None, device="cuda"):
+                 row_stride: int | None = None, device="cuda", host: bool = False):
         embed = rep_mode == "embed"
         rep_dim = rep_dim if rep_dim is not None else head_dim
         rep_dtype = rep_dtype if rep_dtype is not None else dtype
         row_stride = row_stride or head_dim
         rep_heads = 1 if embed else n_kv_heads
-        self.k = torch.zeros((batch, n_kv_heads, capacity, row_stride), dtype=dtype, device=device)
-        self.v = torch.zeros_like(self.k)
+        if host:
+            self.k = torch.zeros((batch, n_kv_heads, capacity, row_stride), dtype=dtype, pin_memory=True)
+            self.v = torch.zeros((batch, n_kv_heads, capacity, row_stride), dtype=dtype, pin_memory=True)
+        else:
+            self.k = torch.zeros((batch, n_kv_heads, capacity, row_stride), dtype=dtype, device=device)
+            self.v = torch.zeros_like(self.k)
+        self.host = host
+        self.device = torch.device(device)
         self.reps = torch.zeros((batch, rep_heads, capacity // block_size, reps_per_block, rep_dim),
                                 dtype=rep_dtype, device=device)
         self.desc = _lib.brs_memory(
@@ -149,11 +158,11 @@ class KVMemory:
     def new_mass(self) -> torch.Tensor:
         """A zeroed attention-mass buffer ``[batch][n_kv_heads][capacity]`` fp32."""
         return torch.zeros((self.batch, self.n_kv_heads, self.k.shape[2]), dtype=torch.float32,
-                           device=self.k.device)
+                           device=self.device)
 
     def new_hits(self) -> torch.Tensor:
         """A zeroed retrieval-count buffer ``[batch][capacity // block]`` int32."""
-        return torch.zeros((self.batch, self.blocks_stride), dtype=torch.int32, device=self.k.device)
+        return torch.zeros((self.batch, self.blocks_stride), dtype=torch.int32, device=self.device)
 
     def count_hits(self, idx: torch.Tensor, hits: torch.Tensor, stream=None) -> torch.Tensor:
         """Add one to ``hits`` for every valid entry of the selection ``idx`` ``[batch][heads][k]``."""
@@ -167,14 +176,14 @@ class KVMemory:
         d = self.desc
         return KVMemory(d.batch, d.n_kv_heads, d.head_dim, d.capacity, d.block_size, dtype=self.dtype,
                         rep_mode=self.rep_mode, reps_per_block=d.reps_per_block, rep_dim=d.rep_dim,
-                        rep_dtype=self.reps.dtype, row_stride=d.row_stride, device=self.k.device)
+                        rep_dtype=self.reps.dtype, row_stride=d.row_stride, device=self.device, host=self.host)
 
     def prune_into(self, hits: torch.Tensor, dst: "KVMemory", dst_hits: torch.Tensor | None = None,
                    plan: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         """Copy what survives pruning into ``dst`` (see brs_mem_prune); returns the plan (new block
         index per old complete block, -1 if evicted)."""
         if plan is None:
-            plan = torch.empty(self.blocks_stride, dtype=torch.int32, device=self.k.device)
+            plan = torch.empty(self.blocks_stride, dtype=torch.int32, device=self.device)
         check(lib.brs_mem_prune(self.desc, hits.data_ptr(), dst.desc, _ptr(dst_hits), plan.data_ptr(),
                                 _stream(stream)))
         return plan
@@ -182,6 +191,45 @@ class KVMemory:
     def reps_from_mass(self, mass: torch.Tensor, b0: int, b1: int, stream=None) -> None:
         """Build the representatives of blocks [b0, b1) from the accumulated mass (attnscore memories)."""
         check(lib.brs_reps_from_mass(self.desc, mass.data_ptr(), b0, b1, _stream(stream)))
+
+
+class BlockCache:
+    """A device cache of an offloaded memory's blocks: ``n_pages`` pages of
+    ``block_size`` K/V rows per (batch, kv head) and the tables that map
+    blocks to pages (see brs_cache_fetch)."""
+
+    def __init__(self, mem: KVMemory, n_pages: int, stream=None):
+        d = mem.desc
+        dev = mem.device
+        self.mem, self.n_pages = mem, n_pages
+        self.k = torch.zeros((d.batch, d.n_kv_heads, n_pages * d.block_size, d.row_stride), dtype=mem.dtype,
+                             device=dev)
+        self.v = torch.zeros_like(self.k)
+        bg = d.batch * d.n_kv_heads
+        self.page_of_block = torch.empty((bg, d.capacity // d.block_size + 1), dtype=torch.int32, device=dev)
+        self.page_block = torch.empty((bg, n_pages), dtype=torch.int32, device=dev)
+        self.page_rows = torch.empty((bg, n_pages), dtype=torch.int32, device=dev)
+        self.page_used = torch.empty((bg, n_pages), dtype=torch.int32, device=dev)
+        self.fetched = torch.zeros((d.batch, d.n_kv_heads), dtype=torch.int32, device=dev)
+        self.desc = _lib.brs_page_cache(k=self.k.data_ptr(), v=self.v.data_ptr(),
+                                        page_of_block=self.page_of_block.data_ptr(),
+                                        page_block=self.page_block.data_ptr(), page_rows=self.page_rows.data_ptr(),
+                                        page_used=self.page_used.data_ptr(), n_pages=n_pages, reserved=0)
+        self.steps = 0
+        self.reset(stream)
+
+    def reset(self, stream=None) -> None:
+        check(lib.brs_cache_reset(self.mem.desc, self.desc, _stream(stream)))
+
+    def fetch(self, idx: torch.Tensor | None, n_sink: int, window: int, stream=None) -> None:
+        """Make resident every block an attention call with this selection reads."""
+        self.steps += 1
+        if idx is None:
+            ih, k, ptr = 1, 0, None
+        else:
+            ih, k, ptr = idx.shape[1], idx.shape[2], idx.data_ptr()
+        check(lib.brs_cache_fetch(self.mem.desc, self.desc, ptr, ih, k, n_sink, window, self.steps,
+                                  self.fetched.data_ptr(), _stream(stream)))
 
 
 def select_topk(scores: torch.Tensor, lo: int, hi: int, k: int, want_vals: bool = True, stream=None):

@@ -22,10 +22,11 @@ ERRORS = {0: "BRS_OK", -1: "BRS_E_INVAL", -2: "BRS_E_CAPACITY", -3: "BRS_E_UNSUP
 
 # every symbol include/brs.h and include/brs_measure.h declare
 EXPORTS = ["brs_version", "brs_last_error", "brs_memory_check", "brs_mem_append", "brs_eligible_range",
-           "brs_score_blocks", "brs_select_topk", "brs_attention_workspace_bytes",
+           "brs_score_blocks", "brs_score_blocks_group", "brs_select_topk", "brs_attention_workspace_bytes",
            "brs_retrieval_attention", "brs_retrieval_step", "brs_window_mass", "brs_reps_from_mass",
            "brs_count_hits", "brs_mem_prune", "brs_profile_next_attention", "brs_measure_read",
-           "brs_retrieval_step_static", "brs_static_scratch_bytes"]
+           "brs_retrieval_step_static", "brs_static_scratch_bytes", "brs_cache_reset", "brs_cache_fetch",
+           "brs_retrieval_attention_cached"]
 
 
 class brs_memory(ctypes.Structure):
@@ -35,6 +36,13 @@ class brs_memory(ctypes.Structure):
         ("rep_dim", c_int32), ("rep_heads", c_int32), ("rep_mode", c_int32), ("rep_dtype", c_int32),
         ("reserved", c_int32), ("capacity", c_int64), ("length", c_int64),
         ("k", c_void_p), ("v", c_void_p), ("reps", c_void_p),
+    ]
+
+
+class brs_page_cache(ctypes.Structure):
+    _fields_ = [
+        ("k", c_void_p), ("v", c_void_p), ("page_of_block", c_void_p), ("page_block", c_void_p),
+        ("page_rows", c_void_p), ("page_used", c_void_p), ("n_pages", c_int32), ("reserved", c_int32),
     ]
 
 
@@ -56,6 +64,7 @@ def _load():
         "brs_mem_append": (c_int, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
         "brs_eligible_range": (c_int, [P, c_int64, c_int64, POINTER(c_int64), POINTER(c_int64)]),
         "brs_score_blocks": (c_int, [P, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_void_p]),
+        "brs_score_blocks_group": (c_int, [P, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_void_p]),
         "brs_select_topk": (c_int, [c_void_p, c_int32, c_int32, c_int64, c_int64, c_int64, c_int32,
                                     c_void_p, c_void_p, c_void_p]),
         "brs_attention_workspace_bytes": (c_int, [P, c_int32, c_int32, c_int32, c_int32, c_int64, c_int64,
@@ -63,8 +72,8 @@ def _load():
         "brs_retrieval_attention": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32,
                                             c_int64, c_int64, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                             c_void_p]),
-        "brs_retrieval_step": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int64, c_int64, c_float,
-                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+        "brs_retrieval_step": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int64, c_int64,
+                                       c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
         "brs_window_mass": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int64, c_float, c_void_p,
                                     c_void_p]),
@@ -73,9 +82,16 @@ def _load():
         "brs_mem_prune": (c_int, [P, c_void_p, P, c_void_p, c_void_p, c_void_p]),
         "brs_profile_next_attention": (c_int, [c_void_p, c_void_p]),
         "brs_measure_read": (c_int, [c_void_p, c_int64, c_void_p, c_int64, ctypes.c_uint32, c_void_p, c_void_p]),
-        "brs_retrieval_step_static": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int64, c_int64,
-                                              c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "brs_retrieval_step_static": (c_int, [P, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int64,
+                                              c_int64, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p]),
         "brs_static_scratch_bytes": (c_size_t, []),
+        "brs_cache_reset": (c_int, [P, POINTER(brs_page_cache), c_void_p]),
+        "brs_cache_fetch": (c_int, [P, POINTER(brs_page_cache), c_void_p, c_int32, c_int32, c_int64, c_int64, c_int32,
+                                    c_void_p, c_void_p]),
+        "brs_retrieval_attention_cached": (c_int, [P, POINTER(brs_page_cache), c_void_p, c_int32, c_int32, c_void_p,
+                                                   c_int32, c_int32, c_int64, c_int64, c_float, c_void_p, c_void_p,
+                                                   c_void_p, c_size_t, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libbrs.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "memory.hip", "score.hip", "topk.hip", "attn_decode.hip", "attn_prefill.hip",
-           "mass.hip", "prune.hip", "measure.hip"]
+           "mass.hip", "prune.hip", "measure.hip", "offload.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
@@ -63,6 +63,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every kernel and function of the library must be defined in it: a host
+    # stub the compiler silently failed to emit shows up as an undefined brs::
+    # symbol, which would only fail when the library is loaded
+    r = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [line.strip() for line in r.stdout.splitlines() if "brs::" in line]
+    if missing:
+        raise RuntimeError("libbrs.so leaves library symbols undefined:\n" + "\n".join(missing[:20]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -191,8 +191,27 @@ int brs_score_blocks(const brs_memory* m, const void* qrep, int32_t n_score_head
   if (n_score_heads / m->n_kv_heads > 32) return fail(BRS_E_UNSUPPORTED, "more than 32 query heads per kv head");
   if (!aligned(qrep, brs::elem_bytes(m->dtype))) return fail(BRS_E_INVAL, "q misaligned");
   if (hi == lo) return ok();
-  hipError_t e = brs::launch_score_dot(*m, qrep, n_score_heads, lo, hi, scores, s);
+  hipError_t e = brs::launch_score_dot(*m, qrep, n_score_heads, lo, hi, scores, false, s);
   return e == hipSuccess ? ok() : hip_fail(e, "score_dot");
+}
+
+int brs_score_blocks_group(const brs_memory* m, const void* q, int32_t n_q_heads, int64_t lo, int64_t hi,
+                           float* scores, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  if (m->rep_mode == BRS_REP_EMBED) return fail(BRS_E_INVAL, "group scores need dot scoring (rep_mode != EMBED)");
+  const int64_t nb = m->length / m->block_size;
+  if (lo < 0 || hi < lo || hi > nb)
+    return fail(BRS_E_INVAL, "need 0 <= lo <= hi <= %lld (complete blocks)", (long long)nb);
+  if (!q || !scores) return fail(BRS_E_INVAL, "q/scores must be non-NULL");
+  if (!aligned(scores, 4)) return fail(BRS_E_INVAL, "scores misaligned");
+  if (n_q_heads < 1 || n_q_heads % m->n_kv_heads != 0)
+    return fail(BRS_E_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q_heads / m->n_kv_heads > 32) return fail(BRS_E_UNSUPPORTED, "more than 32 query heads per kv head");
+  if (!aligned(q, brs::elem_bytes(m->dtype))) return fail(BRS_E_INVAL, "q misaligned");
+  if (hi == lo) return ok();
+  hipError_t e = brs::launch_score_dot(*m, q, n_q_heads, lo, hi, scores, true, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "score_dot (group)");
 }
 
 int brs_select_topk(const float* scores, int32_t batch, int32_t n_heads, int64_t blocks_stride,
@@ -216,7 +235,8 @@ static int attn_setup(const brs_memory* m, int32_t n_q_heads, int32_t n_q, int32
   if (n_q_heads < 1 || n_q_heads % m->n_kv_heads != 0)
     return fail(BRS_E_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
   if (n_q < 1 || n_q > m->length) return fail(BRS_E_INVAL, "need 1 <= n_q <= length");
-  if (idx_heads != 1 && idx_heads != n_q_heads) return fail(BRS_E_INVAL, "idx_heads must be 1 or n_q_heads");
+  if (idx_heads != 1 && idx_heads != m->n_kv_heads && idx_heads != n_q_heads)
+    return fail(BRS_E_INVAL, "idx_heads must be 1, n_kv_heads or n_q_heads");
   if (k < 0) return fail(BRS_E_INVAL, "k < 0");
   if (n_sink < 0 || window < 0) return fail(BRS_E_INVAL, "n_sink and window must be >= 0");
   if (!isfinite(scale)) return fail(BRS_E_INVAL, "scale must be finite");
@@ -306,14 +326,31 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
   return run_attention(g, m, q, idx, out, lse, workspace, (hipStream_t)stream);
 }
 
+// the selection lists of a step: 1 for cosine scores; n_q_heads or
+// n_kv_heads (group scores) for dot scores
+static int step_select_heads(const brs_memory* m, int32_t n_q_heads, int32_t select_heads) {
+  if (m->rep_mode == BRS_REP_EMBED) {
+    if (select_heads != 1) return fail(BRS_E_INVAL, "cosine scoring makes one selection per sequence: select_heads = 1");
+    return BRS_OK;
+  }
+  if (select_heads != n_q_heads && select_heads != m->n_kv_heads)
+    return fail(BRS_E_INVAL, "select_heads must be n_q_heads or n_kv_heads for dot scoring");
+  return BRS_OK;
+}
+
 int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q, const void* qrep,
-                       int32_t k, int64_t n_sink, int64_t window, float scale, float* scores, int32_t* idx,
-                       float* vals, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                       int32_t select_heads, int32_t k, int64_t n_sink, int64_t window, float scale, float* scores,
+                       int32_t* idx, float* vals, float* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream) {
   int rc = check_memory(m);
   if (rc) return rc;
   const bool cosine = m->rep_mode == BRS_REP_EMBED;
-  const int32_t hs = cosine ? 1 : n_q_heads;
+  if (n_q_heads < 1 || n_q_heads % m->n_kv_heads != 0)
+    return fail(BRS_E_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  rc = step_select_heads(m, n_q_heads, select_heads);
+  if (rc) return rc;
+  const int32_t hs = select_heads;
+  const bool grouped = !cosine && hs != n_q_heads;
   int64_t lo = 0, hi = 0;
   rc = brs_eligible_range(m, n_sink, window, &lo, &hi);
   if (rc) return rc;
@@ -347,7 +384,7 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
         e0 = nullptr;
       }
       e = cosine ? brs::launch_score_cosine(*m, qrep, lo, hi, scores, s)
-                 : brs::launch_score_dot(*m, qrep, hs, lo, hi, scores, s);
+                 : brs::launch_score_dot(*m, qrep, n_q_heads, lo, hi, scores, grouped, s);
       brs::set_score_stop_event(nullptr);
       if (e != hipSuccess) return hip_fail(e, "score_blocks");
     }
@@ -367,13 +404,17 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
 }
 
 int brs_retrieval_step_static(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
-                              const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
-                              float* scores, int32_t* idx, float* vals, float* out, float* lse, void* stream) {
+                              const void* qrep, int32_t select_heads, int32_t k, int64_t n_sink, int64_t window,
+                              float scale, float* scores, int32_t* idx, float* vals, float* out, float* lse,
+                              void* stream) {
   int rc = check_memory(m);
   if (rc) return rc;
-  const int32_t hs = m->rep_mode == BRS_REP_EMBED ? 1 : n_q_heads;
+  if (n_q_heads < 1 || n_q_heads % m->n_kv_heads != 0)
+    return fail(BRS_E_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  rc = step_select_heads(m, n_q_heads, select_heads);
+  if (rc) return rc;
   brs::AttnGeom g;
-  rc = attn_setup(m, n_q_heads, n_q, hs, k, n_sink, window, scale, g);
+  rc = attn_setup(m, n_q_heads, n_q, select_heads, k, n_sink, window, scale, g);
   if (rc) return rc;
   if (g.total > kStaticScratchBytes)
     return fail(BRS_E_UNSUPPORTED, "this step needs %zu bytes of workspace; the static scratch holds %zu",
@@ -381,8 +422,8 @@ int brs_retrieval_step_static(const brs_memory* m, const void* q, int32_t n_q_he
   void* ws = nullptr;
   rc = static_scratch(&ws);
   if (rc) return rc;
-  return brs_retrieval_step(m, q, n_q_heads, n_q, qrep, k, n_sink, window, scale, scores, idx, vals, out, lse, ws,
-                            kStaticScratchBytes, stream);
+  return brs_retrieval_step(m, q, n_q_heads, n_q, qrep, select_heads, k, n_sink, window, scale, scores, idx, vals,
+                            out, lse, ws, kStaticScratchBytes, stream);
 }
 
 size_t brs_static_scratch_bytes(void) { return kStaticScratchBytes; }
@@ -465,6 +506,84 @@ int brs_mem_prune(const brs_memory* src, const int32_t* hits, brs_memory* dst, i
                                    (int)tail, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prune");
   dst->length = kept * B + tail;
+  return ok();
+}
+
+static int check_cache(const brs_memory* m, const brs_page_cache* c) {
+  if (!c) return fail(BRS_E_INVAL, "cache descriptor is NULL");
+  if (c->reserved != 0) return fail(BRS_E_INVAL, "cache reserved field must be 0");
+  if (c->n_pages < 1 || c->n_pages > brs::cache_max_pages())
+    return fail(BRS_E_UNSUPPORTED, "n_pages must be in [1, %d]", brs::cache_max_pages());
+  if (!c->k || !c->v || !c->page_of_block || !c->page_block || !c->page_rows || !c->page_used)
+    return fail(BRS_E_INVAL, "cache pointers must be non-NULL");
+  if (!aligned(c->k, 16) || !aligned(c->v, 16)) return fail(BRS_E_INVAL, "cache k/v must be 16-byte aligned");
+  if (!aligned(c->page_of_block, 4) || !aligned(c->page_block, 4) || !aligned(c->page_rows, 4) ||
+      !aligned(c->page_used, 4))
+    return fail(BRS_E_INVAL, "cache tables must be 4-byte aligned");
+  if ((m->row_stride * brs::elem_bytes(m->dtype)) % 16 != 0)
+    return fail(BRS_E_UNSUPPORTED, "a cached memory needs row_stride * element size to be a multiple of 16 bytes");
+  if (m->capacity / m->block_size + 1 > brs::cache_max_blocks())
+    return fail(BRS_E_UNSUPPORTED, "a cached memory holds at most %lld blocks", (long long)brs::cache_max_blocks() - 1);
+  return BRS_OK;
+}
+
+int brs_cache_reset(const brs_memory* m, const brs_page_cache* c, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  rc = check_cache(m, c);
+  if (rc) return rc;
+  hipError_t e = brs::launch_cache_reset(*m, *c, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "cache_reset");
+}
+
+int brs_cache_fetch(const brs_memory* m, const brs_page_cache* c, const int32_t* idx, int32_t idx_heads, int32_t k,
+                    int64_t n_sink, int64_t window, int32_t step, int32_t* fetched, void* stream) {
+  int rc = check_memory(m);
+  if (rc) return rc;
+  rc = check_cache(m, c);
+  if (rc) return rc;
+  if (k < 0 || n_sink < 0 || window < 0) return fail(BRS_E_INVAL, "k, n_sink and window must be >= 0");
+  if (k > 0 && (!idx || !aligned(idx, 4))) return fail(BRS_E_INVAL, "idx must be non-NULL and 4-byte aligned");
+  if (idx_heads < 1 || (idx_heads != 1 && idx_heads % m->n_kv_heads != 0))
+    return fail(BRS_E_INVAL, "idx_heads must be 1 or a multiple of n_kv_heads");
+  if (fetched && !aligned(fetched, 4)) return fail(BRS_E_INVAL, "fetched misaligned");
+  const int64_t N = m->length, B = m->block_size;
+  const int64_t S = n_sink < N ? n_sink : N;
+  const int64_t ws0 = N - window;
+  const int64_t ws = ws0 > S ? ws0 : S;
+  const int64_t nbt = (N + B - 1) / B;
+  const int64_t lists = idx_heads >= m->n_kv_heads ? idx_heads / m->n_kv_heads : 1;
+  const int64_t need = (S + B - 1) / B + (ws < N ? nbt - ws / B : 0) + lists * k;
+  if (need > c->n_pages)
+    return fail(BRS_E_CAPACITY, "a step may need %lld blocks per kv head; the cache has %d pages", (long long)need,
+                c->n_pages);
+  hipError_t e = brs::launch_cache_fetch(*m, *c, k > 0 ? idx : nullptr, idx_heads, k, S, ws, step, fetched,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "cache_fetch");
+}
+
+int brs_retrieval_attention_cached(const brs_memory* m, const brs_page_cache* c, const void* q, int32_t n_q_heads,
+                                   int32_t n_q, const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
+                                   int64_t window, float scale, float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  brs::AttnGeom g;
+  int rc = attn_setup(m, n_q_heads, n_q, idx_heads, k, n_sink, window, scale, g);
+  if (rc) return rc;
+  rc = check_cache(m, c);
+  if (rc) return rc;
+  rc = check_attention_buffers(g, q, idx, k, out, lse, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (n_q != 1 || !g.slot) return fail(BRS_E_UNSUPPORTED, "a cached memory supports decode on the slot kernels");
+  g.pages = c->page_of_block;
+  g.pages_stride = (int)(m->capacity / m->block_size + 1);
+  g.head_stride = (int64_t)c->n_pages * m->block_size * m->row_stride;
+  hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = brs::launch_attn_split(g, c->k, c->v, q, idx, workspace, out, s, e0, e1);
+  if (e != hipSuccess) return hip_fail(e, "attn_split (cached)");
+  e = brs::launch_attn_merge(g, workspace, out, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "attn_merge");
   return ok();
 }
 

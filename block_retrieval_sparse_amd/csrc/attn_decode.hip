@@ -109,22 +109,16 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(PlanArgs a) {
   }
   int n_items = (S > 0) + (Wn > 0), n_tokens = S + Wn;
 
-  const int E = a.idx_heads == 1 ? a.k : a.G * a.k;
+  const int nl = sel_lists(a.idx_heads, a.hkv);
+  const int E = nl * a.k;
   for (int base = 0; base < a.nb; base += kMarkBlocks) {
     const int top = min(a.nb, base + kMarkBlocks);
     for (int i = tid; i < top - base; i += nt) marks[i] = 0u;
     __syncthreads();
     for (int e = tid; e < E; e += nt) {
-      int blk;
-      uint32_t bit;
-      if (a.idx_heads == 1) {
-        blk = a.idx[(int64_t)b * a.k + e];
-        bit = full;
-      } else {
-        const int j = e / a.k;
-        blk = a.idx[((int64_t)b * a.hq + g * a.G + j) * a.k + (e - j * a.k)];
-        bit = 1u << j;
-      }
+      const int j = e / a.k;
+      const int blk = a.idx[sel_row(a.idx_heads, a.hkv, b, g, j) * a.k + (e - j * a.k)];
+      const uint32_t bit = nl == a.G ? 1u << j : full;
       if (blk >= base && blk < top) {
         const int lo_t = max(blk * a.B, S);
         const int hi_t = min((blk + 1) * a.B, a.win_start);
@@ -220,6 +214,11 @@ struct SplitArgs {
   int32_t* idx_out;
   float* vals_out;
   int n_units;                   // one-dimensional grid of units
+  // K/V read through a page table (a device cache of blocks; k and v then
+  // point to the page pool): page of block x of slice bg at pages[bg *
+  // pages_stride + x]
+  const int32_t* pages;
+  int pages_stride;
 };
 
 template <typename T>
@@ -295,15 +294,14 @@ __device__ int chunk_plan(const SplitArgs& a, int b, int g, int c, int rg, int4*
                           int* t_end) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
   const int W = (a.nb + 31) >> 5;
-  const int hb = a.idx_heads == 1 ? 1 : a.G;  // bitmaps: one per head, or one shared
+  const int hb = sel_lists(a.idx_heads, a.hkv);  // bitmaps: one per head, or one shared
   const int S = a.sink_end, ws = a.win_start, B = a.B;
   for (int i = tid; i < hb * W; i += nt) pl.bits[i] = 0u;
   __syncthreads();
   const int E = hb * a.kk;
   for (int e = tid; e < E; e += nt) {
     const int j = e / a.kk;
-    const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + j;
-    const int blk = a.idx[row * a.kk + (e - j * a.kk)];
+    const int blk = a.idx[sel_row(a.idx_heads, a.hkv, b, g, j) * a.kk + (e - j * a.kk)];
     if (blk >= 0 && blk < a.nb && max(blk * B, S) < min((blk + 1) * B, ws))
       atomicOr(&pl.bits[j * W + (blk >> 5)], 1u << (blk & 31));
   }
@@ -1047,8 +1045,9 @@ struct StepLds {
   int flag[kSelWaves];
 };
 
-template <int D, int KPTW, int REGS = kSlotRegs>  // KPTW > 0: select in the kernel, KPTW scores per
-                                                  // lane; REGS selection entries per lane
+template <int D, int KPTW, int REGS = kSlotRegs, bool PAGED = false>  // KPTW > 0: select in the kernel, KPTW
+                                                                     // scores per lane; REGS selection entries
+                                                                     // per lane; PAGED: K/V through a page table
 __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<D, REGS>& sm, StepLds* st) {
   constexpr bool STEP = KPTW > 0;
   constexpr int KC = D / 32;  // 32-wide k chunks of the head dim
@@ -1067,11 +1066,11 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   // Selection waves issue their score loads first: issued behind the query
   // loads (or behind other waves' tile loads in the same code), they would
   // wait for those before starting.
-  const int R = a.idx_heads == 1 ? 1 : a.G;  // score rows of this kv slice
+  const int R = sel_lists(a.idx_heads, a.hkv);  // selection rows of this kv slice
   uint32_t raw[STEP ? KPTW : 1];
   if constexpr (STEP) {
     if (wave < R) {
-      const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + wave;
+      const int64_t row = sel_row(a.idx_heads, a.hkv, b, g, wave);
       topk_load_raw<KPTW>(a.scores + row * a.score_stride, a.sel_lo, a.sel_hi, 64, raw);
     }
   }
@@ -1118,21 +1117,23 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
     for (int r = 0; r < REGS; ++r) {
       const int e = lane + 64 * r, ec = min(e, E - 1);
       const int j = ec / K;
-      const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + j;
-      const int v = a.idx[row * K + (ec - j * K)];
+      const int v = a.idx[sel_row(a.idx_heads, a.hkv, b, g, j) * K + (ec - j * K)];
       ent[r] = e < E ? v : -2;
     }
   }
 
-  // the slot last resolved (wave-uniform): its block and head mask (0: skipped)
-  int c_slot = -1, c_blk = 0;
+  // the slot last resolved (wave-uniform): its block, head mask (0: skipped)
+  // and, through a page table, the first physical row of its block
+  int c_slot = -1, c_blk = 0, c_row = 0;
   uint32_t c_mk = 0u;
+  const int32_t* ptab = PAGED ? a.pages + (int64_t)bg * a.pages_stride : nullptr;
   auto resolve = [&](int s) {
     c_slot = s;
     c_mk = 0u;
     c_blk = __builtin_amdgcn_readfirstlane(sm.ents[s]);
     const int X = c_blk;
     if (X < 0 || X >= a.nb || max(X * a.B, a.sink_end) >= min(X * a.B + a.B, a.win_start)) return;
+    if constexpr (PAGED) c_row = __builtin_amdgcn_readfirstlane(ptab[X]) * a.B;
     // entries naming the same block: the first one attends it for all their heads
     int first = 1 << 30, tot = 0;
 #pragma unroll
@@ -1144,7 +1145,7 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
       }
     }
     if (first < s) return;
-    if (a.idx_heads == 1) {
+    if (R != a.G) {  // one list shared by every head of the slice
       c_mk = full;
     } else if (tot == 1) {
       c_mk = 1u << (s / K);
@@ -1163,8 +1164,9 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   };
   // the wave's tile i (wave-uniform): first row, valid row range, head mask;
   // slots = false leaves slot tiles empty (before the selections are known)
-  auto tile_info = [&](int i, int& pos0, int& vlo, int& vhi, uint32_t& mk, bool slots) {
+  auto tile_info = [&](int i, int& pos0, int& vlo, int& vhi, uint32_t& mk, int& row0, bool slots) {
     pos0 = 0;
+    row0 = -1;
     vlo = 0;
     vhi = 0;
     mk = 0u;
@@ -1190,6 +1192,7 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
       vlo = max(X * a.B, a.sink_end);
       vhi = min(X * a.B + a.B, a.win_start);
       pos0 = X * a.B + off;
+      row0 = PAGED ? c_row + off : pos0;
       mk = c_mk;
     }
   };
@@ -1208,17 +1211,23 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
 
   struct Tile {
     uint4 k[2][KC], v[2][KC];
-    int pos0, vlo, vhi;  // first row, valid rows [vlo, vhi)
+    int pos0, vlo, vhi;  // first position, valid positions [vlo, vhi)
+    int row0;            // physical row of pos0 (a slot tile), or -1 (sinks/window through the page table)
     uint32_t mk;         // query heads that attend the tile
   };
   // loads are issued whatever the tile: invalid tokens read zeros
   auto load = [&](Tile& tl, int i, bool slots) {
-    tile_info(i, tl.pos0, tl.vlo, tl.vhi, tl.mk, slots);
+    tile_info(i, tl.pos0, tl.vlo, tl.vhi, tl.mk, tl.row0, slots);
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx) {
       const int pos = tl.pos0 + 16 * sidx + n;
       const bool val = (tl.mk != 0u) & (pos >= tl.vlo) & (pos < tl.vhi);
-      const int off = val ? pos * rs2 + 16 * g4 : kSlotOOR;
+      int row = pos;
+      if constexpr (PAGED) {
+        const int blk = val ? pos / a.B : 0;
+        row = tl.row0 >= 0 ? tl.row0 + 16 * sidx + n : ptab[blk] * a.B + (pos - blk * a.B);
+      }
+      const int off = val ? row * rs2 + 16 * g4 : kSlotOOR;
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk)
         tl.k[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
@@ -1315,7 +1324,7 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   if constexpr (STEP) {
     // wave w selects score row w of the kv slice (loaded at the start)
     if (wave < R) {
-      const int64_t row = a.idx_heads == 1 ? (int64_t)b : (int64_t)b * a.hq + g * a.G + wave;
+      const int64_t row = sel_row(a.idx_heads, a.hkv, b, g, wave);
       const bool out = c == 0 && rg == 0;  // one workgroup per kv slice writes the selection
       int32_t* gi = out ? a.idx_out + row * K : nullptr;
       float* gv = out && a.vals_out ? a.vals_out + row * K : nullptr;
@@ -1388,13 +1397,14 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
 // the slices' unequal work (measured 0.4-0.9 us faster per step than one
 // slice per XCD).
 
-// Attention over the slot layout with the selections read from idx.
-template <int D, int REGS>
+// Attention over the slot layout with the selections read from idx (PAGED:
+// K/V through the page table of a block cache).
+template <int D, int REGS, bool PAGED>
 __global__ __launch_bounds__(64 * kSlotWaves) void attn_split_slot_kernel(SplitArgs a) {
   __shared__ SlotLds<D, REGS> sm;
   const int unit = blockIdx.x;
   if (unit >= a.n_units) return;
-  slot_unit<D, 0, REGS>(a, unit, sm, nullptr);
+  slot_unit<D, 0, REGS, PAGED>(a, unit, sm, nullptr);
 }
 
 // The whole decode step after scoring: the selection of every score row of
@@ -1551,7 +1561,7 @@ bool fast_supported(const AttnGeom& g) {
 
 bool attn_geometry(AttnGeom& g) {
   if (g.d > 512) return false;
-  const int64_t E = g.idx_heads == 1 ? (int64_t)g.k : (int64_t)g.group * g.k;
+  const int64_t E = (int64_t)sel_lists(g.idx_heads, g.hkv) * g.k;
   const int64_t uniq = E < g.nb ? E : g.nb;
   const int rows = g.group * g.n_q;
   g.fast = fast_supported(g);
@@ -1617,7 +1627,7 @@ bool attn_geometry(AttnGeom& g) {
   g.ml_off = g.chunks_off + up((size_t)bg * g.max_chunks * sizeof(int4));
   {
     const int64_t W = ((int64_t)g.nb + 31) / 32;
-    const int64_t hb = g.idx_heads == 1 ? 1 : g.group;
+    const int64_t hb = sel_lists(g.idx_heads, g.hkv);
     g.local_plan = !g.prefill && !g.slot && hb * W <= kPlanWords;
   }
   const size_t parts = g.prefill ? 0 : rows_total * g.max_chunks;
@@ -1660,7 +1670,7 @@ void slot_args(const AttnGeom& g, SplitArgs& a) {
   a.slot_bs = g.slot_bs;
   a.len_a = g.len_a;
   a.len_b = g.len_b;
-  a.n_ent = g.idx_heads == 1 ? g.k : g.group * g.k;
+  a.n_ent = sel_lists(g.idx_heads, g.hkv) * g.k;
   a.slice_bytes = (int)(g.head_stride * 2);
 }
 
@@ -1704,13 +1714,15 @@ SplitArgs split_args(const AttnGeom& g, const void* k, const void* v, const void
   a.out = out;
   slot_args(g, a);
   a.n_units = g.max_chunks * g.batch * g.hkv * g.row_groups;
+  a.pages = g.pages;
+  a.pages_stride = g.pages_stride;
   return a;
 }
 unsigned slot_grid(const SplitArgs& a) { return (unsigned)a.n_units; }
 }  // namespace
 
 bool step_supported(const AttnGeom& g, int64_t lo, int64_t hi, int k) {
-  const int R = g.idx_heads == 1 ? 1 : g.group;
+  const int R = sel_lists(g.idx_heads, g.hkv);
   return g.slot && g.slot_regs == kSlotRegs && R <= kSelWaves && k >= 1 && k <= kStepK && hi - lo <= 64 * 32 &&
          (g.d == 64 || g.d == 128);
 }
@@ -1758,18 +1770,22 @@ hipError_t launch_attn_split(const AttnGeom& g, const void* k, const void* v, co
   const dim3 grid((unsigned)g.max_chunks, (unsigned)(g.batch * g.hkv), (unsigned)g.row_groups);
   if (g.slot) {
     const dim3 grid1(slot_grid(a)), block(64 * kSlotWaves);
-#define BRS_LAUNCH_SLOT(DD, RG)                                                                          \
-  if (g.d == DD && g.slot_regs == RG) {                                                                  \
+#define BRS_LAUNCH_SLOT(DD, RG, PG)                                                                      \
+  if (g.d == DD && g.slot_regs == RG && (g.pages != nullptr) == PG) {                                    \
     if (ev0)                                                                                             \
-      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, RG>), grid1, block, 0, s, ev0, ev1, 0, a);       \
+      hipExtLaunchKernelGGL((attn_split_slot_kernel<DD, RG, PG>), grid1, block, 0, s, ev0, ev1, 0, a);   \
     else                                                                                                 \
-      hipLaunchKernelGGL((attn_split_slot_kernel<DD, RG>), grid1, block, 0, s, a);                       \
+      hipLaunchKernelGGL((attn_split_slot_kernel<DD, RG, PG>), grid1, block, 0, s, a);                   \
     return hipGetLastError();                                                                            \
   }
-    BRS_LAUNCH_SLOT(64, kSlotRegs)
-    BRS_LAUNCH_SLOT(128, kSlotRegs)
-    BRS_LAUNCH_SLOT(64, kSlotRegsMax)
-    BRS_LAUNCH_SLOT(128, kSlotRegsMax)
+    BRS_LAUNCH_SLOT(64, kSlotRegs, false)
+    BRS_LAUNCH_SLOT(128, kSlotRegs, false)
+    BRS_LAUNCH_SLOT(64, kSlotRegsMax, false)
+    BRS_LAUNCH_SLOT(128, kSlotRegsMax, false)
+    BRS_LAUNCH_SLOT(64, kSlotRegs, true)
+    BRS_LAUNCH_SLOT(128, kSlotRegs, true)
+    BRS_LAUNCH_SLOT(64, kSlotRegsMax, true)
+    BRS_LAUNCH_SLOT(128, kSlotRegsMax, true)
 #undef BRS_LAUNCH_SLOT
     return hipErrorInvalidValue;
   }

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   // overlap (the memory counter waits in issue order).
   int blk;
   {
-    const int row = a.idx_heads == 1 ? b : b * a.hq + h;
+    // this head's list: its own, its kv head's, or its sequence's
+    const int row = (int)sel_row(a.idx_heads, a.hkv, b, g, sel_lists(a.idx_heads, a.hkv) == a.G ? h - g * a.G : 0);
     const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.idx + (int64_t)row * a.kk), (short)0, a.kk * 4, kBufferFlags);
     blk = (int)__builtin_amdgcn_raw_buffer_load_b32(irs, tid < a.kk ? tid * 4 : kOutOfRange, 0, 0);

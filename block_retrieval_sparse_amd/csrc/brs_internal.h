@@ -75,6 +75,21 @@ __device__ __forceinline__ float xsum16_32(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// selection lists of a kv slice
+//
+// idx holds batch * idx_heads rows: idx_heads = 1 (one list per sequence,
+// shared by every head), n_kv_heads (one per kv head, shared by its query
+// heads) or n_q_heads (one per query head).  A kv slice (b, g) reads
+// sel_lists rows; list j is row sel_row(.., j).  With one list per query
+// head, list j belongs to query head j of the group; otherwise every head of
+// the slice attends it.
+
+__host__ __device__ inline int sel_lists(int idx_heads, int hkv) { return idx_heads >= hkv ? idx_heads / hkv : 1; }
+__host__ __device__ inline int64_t sel_row(int idx_heads, int hkv, int b, int g, int j) {
+  return (int64_t)b * idx_heads + (idx_heads >= hkv ? (int64_t)g * (idx_heads / hkv) : 0) + j;
+}
+
+// ---------------------------------------------------------------------------
 // attention plan
 //
 // For every (batch, kv head) the plan kernel writes the attended token set as
@@ -114,6 +129,10 @@ struct AttnGeom {
   int max_chunks;         // split workgroups per (batch, kv head, row group)
   int row_groups;         // ceil(group * n_q / kRowsMax)
   int rows_per_group;
+  // a block cache: k / v are the page pool, block x of slice bg at page
+  // pages[bg * pages_stride + x] (nullptr: the memory itself)
+  const int32_t* pages;
+  int pages_stride;
   // workspace offsets (bytes)
   size_t hdr_off, items_off, first_off, chunks_off, ml_off, o_off, total;
 };
@@ -159,10 +178,18 @@ hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const v
                             hipStream_t s);
 // the next score launch on this thread records e when its kernel completes
 void set_score_stop_event(hipEvent_t e);
+// grouped: one score per kv head, the maximum over its query heads
 hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi,
-                            float* scores, hipStream_t s);
+                            float* scores, bool grouped, hipStream_t s);
 hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, int64_t hi,
                                float* scores, hipStream_t s);
+// block cache of an offloaded memory
+int cache_max_pages();
+int64_t cache_max_blocks();
+hipError_t launch_cache_reset(const brs_memory& m, const brs_page_cache& c, hipStream_t s);
+hipError_t launch_cache_fetch(const brs_memory& m, const brs_page_cache& c, const int32_t* idx, int idx_heads,
+                              int k, int64_t sink_end, int64_t win_start, int step, int32_t* fetched,
+                              hipStream_t s);
 hipError_t launch_select_topk(const float* scores, int batch, int heads, int64_t stride, int64_t lo,
                               int64_t hi, int k, int32_t* idx, float* vals, hipStream_t s);
 

@@ -11,7 +11,9 @@
 // once and dotted with all G query heads of the group (grouped-query sharing:
 // the representative bytes are read once per kv head, not once per query
 // head).  L lanes share one row (16-byte loads, coalesced); each lane holds
-// its slice of the G queries in float64 registers.
+// its slice of the G queries in float64 registers.  With `grouped` set the
+// kernels write one score per kv head instead of one per query head: the
+// maximum over the group's heads (for a selection the group shares).
 #include <hip/hip_ext.h>
 
 #include "brs_internal.h"
@@ -154,7 +156,8 @@ __device__ __forceinline__ double elem_f64<uint16_t>(const uint16_t* p, int64_t 
 template <typename T, int EPL, int G>
 __global__ __launch_bounds__(256) void score_dot_kernel(const T* __restrict__ q, const T* __restrict__ reps,
                                                         float* __restrict__ scores, int d, int R, int hkv,
-                                                        int64_t capB, int64_t lo, int64_t hi, int bps) {
+                                                        int64_t capB, int64_t lo, int64_t hi, int bps,
+                                                        int grouped) {
   constexpr int UPL = EPL / Vec<T>::n;  // 16-byte units per lane
   const int L = d / EPL;
   const int lane = threadIdx.x & 63;
@@ -211,9 +214,16 @@ __global__ __launch_bounds__(256) void score_dot_kernel(const T* __restrict__ q,
       for (int j = 0; j < G; ++j) best[j] = nan_max(best[j], acc[j]);
     }
     if (valid) {
+      if (grouped) {
+        double gb = best[0];
 #pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)best[j];
+        for (int j = 1; j < G; ++j) gb = nan_max(gb, best[j]);
+        if (sub == 0) scores[(int64_t)bg * capB + blk] = (float)gb;
+      } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)best[j];
+      }
     }
   }
 }
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(256) void score_dot_kernel(const T* __restrict__ q,
 template <typename T, int EPL, int G, int L, int RPS>
 __global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict__ q, const T* __restrict__ reps,
                                                              float* __restrict__ scores, int d, int R, int hkv,
-                                                             int64_t capB, int64_t lo, int64_t hi) {
+                                                             int64_t capB, int64_t lo, int64_t hi, int grouped) {
   constexpr int UPL = EPL / Vec<T>::n;
   constexpr int SPW = 64 / L;
   const int lane = threadIdx.x & 63;
@@ -278,9 +288,16 @@ __global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict
     for (int j = 0; j < G; ++j) acc[j] = group_max_f64<L>(group_sum_f64<L>(acc[j]), L * R);
     if (row < row_hi && (row % R) == 0) {
       const int64_t blk = row / R;
+      if (grouped) {
+        double gb = acc[0];
 #pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)acc[j];
+        for (int j = 1; j < G; ++j) gb = nan_max(gb, acc[j]);
+        if (sub == 0) scores[(int64_t)bg * capB + blk] = (float)gb;
+      } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)acc[j];
+      }
     }
   }
 }
@@ -290,7 +307,8 @@ __global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict
 template <typename T>
 __global__ __launch_bounds__(256) void score_dot_generic_kernel(const T* __restrict__ q, const T* __restrict__ reps,
                                                                 float* __restrict__ scores, int d, int R, int hkv,
-                                                                int G, int64_t capB, int64_t lo, int64_t hi) {
+                                                                int G, int64_t capB, int64_t lo, int64_t hi,
+                                                                int grouped) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = lo + (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (blk >= hi) return;
@@ -298,6 +316,7 @@ __global__ __launch_bounds__(256) void score_dot_generic_kernel(const T* __restr
   const int b = bg / hkv, g = bg - b * hkv;
   const int hq = hkv * G;
   const T* rrow = reps + ((int64_t)bg * capB + blk) * R * d;
+  double gb = -INFINITY;
   for (int j = 0; j < G; ++j) {
     const T* qrow = q + ((int64_t)b * hq + g * G + j) * d;
     double best = -INFINITY;
@@ -307,8 +326,10 @@ __global__ __launch_bounds__(256) void score_dot_generic_kernel(const T* __restr
       for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off);
       best = nan_max(best, a);
     }
-    if (lane == 0) scores[((int64_t)b * hq + g * G + j) * capB + blk] = (float)best;
+    gb = j == 0 ? best : nan_max(gb, best);
+    if (lane == 0 && !grouped) scores[((int64_t)b * hq + g * G + j) * capB + blk] = (float)best;
   }
+  if (lane == 0 && grouped) scores[(int64_t)bg * capB + blk] = (float)gb;
 }
 
 // Cosine (one score head per sequence): s = q.e / (sqrt(q.q) sqrt(e.e)),
@@ -391,7 +412,8 @@ __global__ __launch_bounds__(256) void score_cosine_rows_kernel(const T* __restr
 }
 
 template <typename T, int EPL, int G>
-hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
+hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, int grouped,
+                   hipStream_t s) {
   const int L = m.head_dim / EPL;
   const int slots = 4 * (64 / L);
   const int64_t nblk = hi - lo;
@@ -402,12 +424,13 @@ hipError_t run_dot(const brs_memory& m, const void* q, int64_t lo, int64_t hi, f
   const int64_t gx = (nblk + (int64_t)slots * bps - 1) / ((int64_t)slots * bps);
   BRS_SCORE_LAUNCH((score_dot_kernel<T, EPL, G>), dim3((unsigned)gx, (unsigned)bg), dim3(256), s,
                      (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads,
-                     m.capacity / m.block_size, lo, hi, bps);
+                     m.capacity / m.block_size, lo, hi, bps, grouped);
   return hipGetLastError();
 }
 
 template <typename T, int EPL, int G, int L>
-hipError_t run_rows(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
+hipError_t run_rows(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, int grouped,
+                    hipStream_t s) {
   constexpr int slots = 4 * (64 / L);
   const int64_t rows = (hi - lo) * m.reps_per_block;
   const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
@@ -418,38 +441,39 @@ hipError_t run_rows(const brs_memory& m, const void* q, int64_t lo, int64_t hi, 
     const int64_t gx = (rows + slots * 4 - 1) / (slots * 4);
     BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 4>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
-                       hi);
+                       hi, grouped);
   } else if (want >= 2) {
     const int64_t gx = (rows + slots * 2 - 1) / (slots * 2);
     BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 2>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
-                       hi);
+                       hi, grouped);
   } else {
     const int64_t gx = (rows + slots - 1) / slots;
     BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 1>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
-                       hi);
+                       hi, grouped);
   }
   return hipGetLastError();
 }
 
 template <typename T, int EPL, int G>
-hipError_t run_dot_any(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, hipStream_t s) {
+hipError_t run_dot_any(const brs_memory& m, const void* q, int64_t lo, int64_t hi, float* scores, int grouped,
+                       hipStream_t s) {
   // the row kernel needs R to divide the slots of a wave (64 / L of them)
   const int L = m.head_dim / EPL;
   const int R = m.reps_per_block;
   const bool rows_ok = (R & (R - 1)) == 0 && R <= 64 / L;
   if (rows_ok) {
-    if (L == 4) return run_rows<T, EPL, G, 4>(m, q, lo, hi, scores, s);
-    if (L == 8) return run_rows<T, EPL, G, 8>(m, q, lo, hi, scores, s);
-    if (L == 16) return run_rows<T, EPL, G, 16>(m, q, lo, hi, scores, s);
+    if (L == 4) return run_rows<T, EPL, G, 4>(m, q, lo, hi, scores, grouped, s);
+    if (L == 8) return run_rows<T, EPL, G, 8>(m, q, lo, hi, scores, grouped, s);
+    if (L == 16) return run_rows<T, EPL, G, 16>(m, q, lo, hi, scores, grouped, s);
   }
-  return run_dot<T, EPL, G>(m, q, lo, hi, scores, s);
+  return run_dot<T, EPL, G>(m, q, lo, hi, scores, grouped, s);
 }
 
 template <typename T>
 hipError_t dispatch_dot(const brs_memory& m, const void* q, int G, int64_t lo, int64_t hi, float* scores,
-                        hipStream_t s) {
+                        int grouped, hipStream_t s) {
   constexpr int E16 = 16 / sizeof(T);  // elements per 16 bytes
   const int d = m.head_dim;
   auto fits = [&](int epl) {
@@ -460,27 +484,28 @@ hipError_t dispatch_dot(const brs_memory& m, const void* q, int G, int64_t lo, i
   auto qal = ((uintptr_t)q % 16) == 0;
   if (qal && (d * (int)sizeof(T)) % 16 == 0) {
     if (G <= 4 && fits(2 * E16)) {
-      if (G == 1) return run_dot_any<T, 2 * E16, 1>(m, q, lo, hi, scores, s);
-      if (G == 2) return run_dot_any<T, 2 * E16, 2>(m, q, lo, hi, scores, s);
-      if (G == 4) return run_dot_any<T, 2 * E16, 4>(m, q, lo, hi, scores, s);
+      if (G == 1) return run_dot_any<T, 2 * E16, 1>(m, q, lo, hi, scores, grouped, s);
+      if (G == 2) return run_dot_any<T, 2 * E16, 2>(m, q, lo, hi, scores, grouped, s);
+      if (G == 4) return run_dot_any<T, 2 * E16, 4>(m, q, lo, hi, scores, grouped, s);
     }
-    if (G == 8 && fits(E16)) return run_dot_any<T, E16, 8>(m, q, lo, hi, scores, s);
+    if (G == 8 && fits(E16)) return run_dot_any<T, E16, 8>(m, q, lo, hi, scores, grouped, s);
   }
   const int64_t bg = (int64_t)m.batch * m.n_kv_heads;
   const int64_t gx = (hi - lo + 3) / 4;
   BRS_SCORE_LAUNCH(score_dot_generic_kernel<T>, dim3((unsigned)gx, (unsigned)bg), dim3(256), s, (const T*)q,
                      (const T*)m.reps, scores, d, m.reps_per_block, m.n_kv_heads, G, m.capacity / m.block_size,
-                     lo, hi);
+                     lo, hi, grouped);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_score_dot(const brs_memory& m, const void* q, int hq, int64_t lo, int64_t hi, float* scores,
-                            hipStream_t s) {
+                            bool grouped, hipStream_t s) {
   const int G = hq / m.n_kv_heads;
-  if (m.dtype == BRS_F32) return dispatch_dot<float>(m, q, G, lo, hi, scores, s);
-  return dispatch_dot<uint16_t>(m, q, G, lo, hi, scores, s);
+  const int gr = grouped ? 1 : 0;
+  if (m.dtype == BRS_F32) return dispatch_dot<float>(m, q, G, lo, hi, scores, gr, s);
+  return dispatch_dot<uint16_t>(m, q, G, lo, hi, scores, gr, s);
 }
 
 hipError_t launch_score_cosine(const brs_memory& m, const void* rq, int64_t lo, int64_t hi, float* scores,

@@ -10,19 +10,26 @@ import math
 
 import torch
 
-from . import KVMemory, _lib, _ptr, _stream, check, lib
+from . import BlockCache, KVMemory, _lib, _ptr, _stream, check, lib
 
 
 class RetrievalStep:
+    """``select``: "head" (one selection per query head) or "group" (one per kv
+    head, shared by its query heads; dot scoring only).  Cosine scoring always
+    makes one selection per sequence."""
+
     def __init__(self, mem: KVMemory, n_q_heads: int, n_q: int, k: int, n_sink: int, window: int,
-                 scale: float | None = None, want_lse: bool = False):
+                 scale: float | None = None, want_lse: bool = False, select: str = "head"):
         self.mem = mem
         self.n_q_heads, self.n_q, self.k = n_q_heads, n_q, k
         self.n_sink, self.window = n_sink, window
         self.scale = 1.0 / math.sqrt(mem.head_dim) if scale is None else scale
-        dev = mem.k.device
+        dev = mem.device
         self.cosine = mem.rep_mode == "embed"
-        self.score_heads = 1 if self.cosine else n_q_heads
+        if select not in ("head", "group"):
+            raise ValueError("select must be 'head' or 'group'")
+        self.grouped = select == "group" and not self.cosine
+        self.score_heads = 1 if self.cosine else (mem.n_kv_heads if self.grouped else n_q_heads)
         self.scores = torch.full((mem.batch, self.score_heads, mem.blocks_stride), float("nan"),
                                  dtype=torch.float32, device=dev)
         self.idx = torch.full((mem.batch, self.score_heads, k), -1, dtype=torch.int32, device=dev)
@@ -35,9 +42,12 @@ class RetrievalStep:
         self.lo, self.hi = mem.eligible_range(n_sink, window)
 
     def score(self, qrep: torch.Tensor, stream=None) -> None:
-        hs = self.score_heads
-        check(lib.brs_score_blocks(self.mem.desc, qrep.data_ptr(), hs, self.lo, self.hi, self.scores.data_ptr(),
-                                   _stream(stream)))
+        if self.grouped:
+            check(lib.brs_score_blocks_group(self.mem.desc, qrep.data_ptr(), self.n_q_heads, self.lo, self.hi,
+                                             self.scores.data_ptr(), _stream(stream)))
+            return
+        check(lib.brs_score_blocks(self.mem.desc, qrep.data_ptr(), self.score_heads, self.lo, self.hi,
+                                   self.scores.data_ptr(), _stream(stream)))
 
     def select(self, stream=None) -> None:
         if self.k == 0:
@@ -67,8 +77,9 @@ class RetrievalStep:
                 raise ValueError("pass a contiguous qrep")
         if profile_events is not None:
             check(lib.brs_profile_next_attention(profile_events[0], profile_events[1]))
-        check(lib.brs_retrieval_step(self.mem.desc, q.data_ptr(), self.n_q_heads, self.n_q, qrep.data_ptr(), self.k,
-                                     self.n_sink, self.window, self.scale, self.scores.data_ptr(),
+        check(lib.brs_retrieval_step(self.mem.desc, q.data_ptr(), self.n_q_heads, self.n_q, qrep.data_ptr(),
+                                     self.score_heads, self.k, self.n_sink, self.window, self.scale,
+                                     self.scores.data_ptr(),
                                      self.idx.data_ptr(), self.vals.data_ptr(), self.out.data_ptr(),
                                      _ptr(self.lse), self.workspace.data_ptr(), self.workspace.numel(),
                                      _stream(stream)))
@@ -82,6 +93,40 @@ class RetrievalStep:
                 raise ValueError("pass a contiguous qrep")
         self.score(qrep, stream)
         self.select(stream)
+        return self.attend(q, stream, profile_events)
+
+
+class CachedStep(RetrievalStep):
+    """One decode step over an offloaded memory (K/V in host memory, see
+    ``KVMemory(host=True)``): scores and selection as RetrievalStep, then
+    brs_cache_fetch stages the blocks the step reads into the cache, then the
+    attention reads them there (brs_retrieval_attention_cached).  Outputs are
+    those of the same step on a resident memory, bit for bit."""
+
+    def __init__(self, mem: KVMemory, cache: BlockCache, n_q_heads: int, k: int, n_sink: int, window: int,
+                 scale: float | None = None, select: str = "head"):
+        super().__init__(mem, n_q_heads, 1, k, n_sink, window, scale=scale, select=select)
+        self.cache = cache
+
+    def fetch(self, stream=None) -> None:
+        self.cache.fetch(self.idx if self.k else None, self.n_sink, self.window, stream)
+
+    def attend(self, q: torch.Tensor, stream=None, profile_events=None) -> torch.Tensor:
+        if profile_events is not None:
+            check(lib.brs_profile_next_attention(profile_events[0], profile_events[1]))
+        check(lib.brs_retrieval_attention_cached(self.mem.desc, self.cache.desc, q.data_ptr(), self.n_q_heads, 1,
+                                                 self.idx.data_ptr() if self.k else None, self.score_heads, self.k,
+                                                 self.n_sink, self.window, self.scale, self.out.data_ptr(),
+                                                 _ptr(self.lse), self.workspace.data_ptr(), self.workspace.numel(),
+                                                 _stream(stream)))
+        return self.out
+
+    def run(self, q: torch.Tensor, qrep: torch.Tensor | None = None, stream=None, profile_events=None):
+        if qrep is None:
+            qrep = q[:, :, -1, :].contiguous()
+        self.score(qrep, stream)
+        self.select(stream)
+        self.fetch(stream)
         return self.attend(q, stream, profile_events)
 
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BRS_VERSION 2
+#define BRS_VERSION 3
 
 /* Storage types. */
 typedef enum { BRS_F32 = 0, BRS_BF16 = 1 } brs_dtype;
@@ -174,6 +174,23 @@ int brs_eligible_range(const brs_memory* m, int64_t n_sink, int64_t window, int6
 int brs_score_blocks(const brs_memory* m, const void* qrep, int32_t n_score_heads, int64_t lo,
                      int64_t hi, float* scores, void* stream);
 
+/* Scores for a selection shared by the query heads of each kv head (dot
+ * scoring only; grouped-query attention): the score of block b for kv head g
+ * is the maximum over the group's query heads h and the block's R
+ * representatives of q_h . rep -- the block's best match with any head of
+ * the group, combined by max as a block's representatives are (InfLLM
+ * "method": block-level relevance; Landmark Attention "proposed method").
+ * Exact products summed in float64, rounded once to float32; NaN in any dot
+ * makes the score NaN.
+ *   q      : [batch][n_q_heads][head_dim] dtype, as brs_score_blocks.
+ *   scores : [batch][n_kv_heads][capacity / block_size] float32; columns
+ *            [lo, hi) are written.
+ * brs_select_topk with n_heads = n_kv_heads then gives one selection per kv
+ * head (idx_heads = n_kv_heads in brs_retrieval_attention).  Errors as
+ * brs_score_blocks; BRS_E_INVAL for EMBED memories. */
+int brs_score_blocks_group(const brs_memory* m, const void* q, int32_t n_q_heads, int64_t lo, int64_t hi,
+                           float* scores, void* stream);
+
 /* Exact top-k per row of scores (MemLong 2.3.2: TopK of the scores, computed
  * exactly, 2.4.2).
  *   scores : [batch][n_heads][blocks_stride] float32, columns [lo, hi) read.
@@ -203,7 +220,8 @@ int brs_attention_workspace_bytes(const brs_memory* m, int32_t n_q_heads, int32_
  *          N - n_q + j (N = m->length: the queries' own tokens are already
  *          appended).
  *   idx  : [batch][idx_heads][k] int32 block indices; idx_heads = n_q_heads
- *          (one list per query head) or 1 (one list for all heads of a
+ *          (one list per query head), n_kv_heads (one list per kv head,
+ *          shared by its query heads) or 1 (one list for all heads of a
  *          sequence).  Entries < 0 or >= N / block_size are skipped;
  *          duplicates count once.
  *   For query j of head h the attended set is the SET
@@ -229,21 +247,23 @@ int brs_retrieval_attention(const brs_memory* m, const void* q, int32_t n_q_head
 
 /* One whole step (score_blocks, select_topk, retrieval_attention) in one
  * call, with the candidate range of brs_eligible_range(n_sink, window):
- * identical results to the three calls made in turn, and the same
- * selection semantics (per query head for dot scores, per sequence for
- * cosine).
- *   q, out, lse : as brs_retrieval_attention (idx_heads = n_q_heads for
- *               dot scores, 1 for cosine);
+ * identical results to the calls made in turn.
+ *   select_heads : the selection lists per sequence.  Dot scores: n_q_heads
+ *               (brs_score_blocks, one selection per query head) or
+ *               n_kv_heads (brs_score_blocks_group, one selection per kv
+ *               head shared by its query heads).  Cosine scores: 1 (one per
+ *               sequence).
+ *   q, out, lse : as brs_retrieval_attention (idx_heads = select_heads);
  *   qrep      : as brs_score_blocks (unused when k = 0);
- *   scores    : [batch][n_score_heads][capacity / block_size] float32;
- *   idx, vals : [batch][n_score_heads][k] as brs_select_topk (vals may be
+ *   scores    : [batch][select_heads][capacity / block_size] float32;
+ *   idx, vals : [batch][select_heads][k] as brs_select_topk (vals may be
  *               NULL; scores and idx may be NULL when k = 0);
  *   workspace : brs_attention_workspace_bytes(m, n_q_heads, n_q,
- *               n_score_heads, k, n_sink, window) bytes.
+ *               select_heads, k, n_sink, window) bytes.
  * Errors as the separate calls; nothing is enqueued on error. */
 int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
-                       const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
-                       float* scores, int32_t* idx, float* vals, float* out, float* lse,
+                       const void* qrep, int32_t select_heads, int32_t k, int64_t n_sink, int64_t window,
+                       float scale, float* scores, int32_t* idx, float* vals, float* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* brs_retrieval_step for callers that cannot allocate device memory -- code
@@ -261,8 +281,9 @@ int brs_retrieval_step(const brs_memory* m, const void* q, int32_t n_q_heads, in
  * on one GPU (on different streams, or from several threads without ordering)
  * race on it.  Nothing in it needs to start at zero. */
 int brs_retrieval_step_static(const brs_memory* m, const void* q, int32_t n_q_heads, int32_t n_q,
-                              const void* qrep, int32_t k, int64_t n_sink, int64_t window, float scale,
-                              float* scores, int32_t* idx, float* vals, float* out, float* lse, void* stream);
+                              const void* qrep, int32_t select_heads, int32_t k, int64_t n_sink, int64_t window,
+                              float scale, float* scores, int32_t* idx, float* vals, float* out, float* lse,
+                              void* stream);
 
 /* Bytes of the per-GPU array brs_retrieval_step_static works in. */
 size_t brs_static_scratch_bytes(void);
@@ -331,6 +352,61 @@ int brs_count_hits(const brs_memory* m, const int32_t* idx, int32_t idx_heads, i
  * (host side) on success.  BRS_E_UNSUPPORTED above 16384 middle blocks. */
 int brs_mem_prune(const brs_memory* src, const int32_t* hits, brs_memory* dst, int32_t* dst_hits, int32_t* plan,
                   void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Offload to host memory with a device cache of blocks (InfLLM "method": all
+ * memory units are kept in CPU memory and the GPU keeps a cache of the units
+ * used most, loading the units a step needs that it does not hold;
+ * RetrievalAttention "proposed method": the KV cache is split between GPU and
+ * CPU memory).
+ *
+ * The memory's k and v are then HOST memory: pinned and mapped (hipHostMalloc,
+ * e.g. a torch tensor made with pin_memory=True), read and written by the
+ * device through the same address.  brs_mem_append fills it as usual; the
+ * representatives stay in device memory, so scoring and selection are
+ * unchanged.  A caller-owned page pool in device memory caches blocks: */
+typedef struct brs_page_cache {
+  void* k;                 /* device [batch][n_kv_heads][n_pages * block_size][row_stride] dtype */
+  void* v;                 /* device, as k                                                        */
+  int32_t* page_of_block;  /* device [batch][n_kv_heads][capacity / block_size + 1]: page or -1   */
+  int32_t* page_block;     /* device [batch][n_kv_heads][n_pages]: block held, -1 if free         */
+  int32_t* page_rows;      /* device [batch][n_kv_heads][n_pages]: rows of that block copied      */
+  int32_t* page_used;      /* device [batch][n_kv_heads][n_pages]: last step that needed the page */
+  int32_t n_pages;         /* pages per (batch, kv head), 1 .. 2048                               */
+  int32_t reserved;        /* must be 0                                                           */
+} brs_page_cache;
+
+/* Empties the cache (every table to "nothing cached").  Enqueued on stream.
+ * Requires a valid memory descriptor for the geometry; row_stride * element
+ * size a multiple of 16 bytes; capacity / block_size < 262144. */
+int brs_cache_reset(const brs_memory* m, const brs_page_cache* c, void* stream);
+
+/* Makes resident every block that brs_retrieval_attention_cached with the
+ * same idx, idx_heads, k, n_sink and window will read, for every (batch, kv
+ * head): the blocks holding sink or window tokens and the selected blocks
+ * holding tokens outside both.  A needed block already cached keeps its page
+ * (the rows a growing tail block gained since are copied); the others are
+ * copied from host memory into pages that are free, else that were needed
+ * least recently (lowest page_used, then lowest page index), among those this
+ * step does not need.  page_used of every needed page becomes `step` (any
+ * increasing counter).  fetched (device [batch][n_kv_heads] int32, or NULL)
+ * gets += the blocks copied.  idx as brs_retrieval_attention (idx_heads = 1,
+ * n_kv_heads or the query heads).  BRS_E_CAPACITY when n_pages is below the
+ * blocks a step may need: ceil(S'/B) + the window's blocks + (lists of a kv
+ * head) * k, with S' the sinks kept.  Enqueued on stream. */
+int brs_cache_fetch(const brs_memory* m, const brs_page_cache* c, const int32_t* idx, int32_t idx_heads, int32_t k,
+                    int64_t n_sink, int64_t window, int32_t step, int32_t* fetched, void* stream);
+
+/* brs_retrieval_attention for an offloaded memory: K/V are read from the
+ * cache's pages through page_of_block (after brs_cache_fetch with the same
+ * selection), with results identical bit for bit to brs_retrieval_attention
+ * over the same data resident in device memory.  Decode only (n_q = 1) on
+ * the slot kernels (bfloat16, head_dim 64 or 128); other shapes return
+ * BRS_E_UNSUPPORTED.  Workspace as brs_attention_workspace_bytes. */
+int brs_retrieval_attention_cached(const brs_memory* m, const brs_page_cache* c, const void* q, int32_t n_q_heads,
+                                   int32_t n_q, const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
+                                   int64_t window, float scale, float* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Measurement hook: the next brs_retrieval_attention, brs_retrieval_step or
  * brs_window_mass call on this thread records `start_event` and `stop_event`

@@ -87,9 +87,11 @@ def check_idx(gidx: np.ndarray, oidx: np.ndarray, oscores: np.ndarray, k: int, w
                 f"{what}: slot {j}: gpu {gidx[j]} oracle {oidx[j]} outside the 1e-6 tie band")
 
 
-def check_step(w: Workload, mem, x: dict, step, pairs=None, query_rows=None, check_scores=True) -> dict:
+def check_step(w: Workload, mem, x: dict, step, pairs=None, query_rows=None, check_scores=True,
+               select: str = "head") -> dict:
     """Compare scores, selection and attention of an executed RetrievalStep with
-    the oracle on the (batch, query head) ``pairs`` (default: all)."""
+    the oracle on the (batch, query head) ``pairs`` (default: all).  With
+    ``select="group"`` the selection is one per kv head (group scores)."""
     torch.cuda.synchronize()
     N = mem.length
     lo, hi = O.eligible_range(N, w.block, w.sinks, w.window)
@@ -106,12 +108,14 @@ def check_step(w: Workload, mem, x: dict, step, pairs=None, query_rows=None, che
     done_sel = set()
     for (b, h) in pairs:
         g = O.kv_head_of(h, w.n_q_heads, w.n_kv_heads)
-        sh = 0 if w.rep_mode == "embed" else h
+        sh = 0 if w.rep_mode == "embed" else (g if select == "group" else h)
         key = (b, sh)
         if key not in done_sel:
             done_sel.add(key)
             if w.rep_mode == "embed":
                 s = O.scores_cosine(rq[b], reps[(b, 0)][lo:hi, 0, :])
+            elif select == "group":
+                s = O.scores_group_max(q[b, g * G:(g + 1) * G, -1], reps[(b, g)][lo:hi])
             else:
                 s = O.scores_dot_max(q[b, h, -1], reps[(b, g)][lo:hi])
             full = np.full(gscores.shape[2], np.nan, dtype=np.float32)

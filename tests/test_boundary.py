@@ -36,7 +36,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version(L):
-    assert L.lib.brs_version() == 2
+    assert L.lib.brs_version() == 3
 
 
 def desc(L, **kw):
@@ -135,17 +135,19 @@ def test_retrieval_step_rejects_before_device_work(L):
     n = ctypes.c_size_t()
     assert L.lib.brs_attention_workspace_bytes(m, 8, 1, 8, 32, 128, 1024, ctypes.byref(n)) == 0
     ws = n.value
-    args = dict(q=0x1000, hq=8, nq=1, qrep=0x4000, k=32, S=128, Wn=1024, sc=0.1, scores=0x40000, idx=0x2000,
+    args = dict(q=0x1000, hq=8, nq=1, qrep=0x4000, sh=8, k=32, S=128, Wn=1024, sc=0.1, scores=0x40000, idx=0x2000,
                 vals=0x6000, out=0x3000, lse=None)
 
     def call(ws_ptr=0x100000, ws_bytes=ws, mem=m, **kw):
         a = dict(args)
         a.update(kw)
-        return L.lib.brs_retrieval_step(mem, a["q"], a["hq"], a["nq"], a["qrep"], a["k"], a["S"], a["Wn"],
+        return L.lib.brs_retrieval_step(mem, a["q"], a["hq"], a["nq"], a["qrep"], a["sh"], a["k"], a["S"], a["Wn"],
                                         a["sc"], a["scores"], a["idx"], a["vals"], a["out"], a["lse"], ws_ptr,
                                         ws_bytes, None)
 
     assert call(hq=7) == -1                       # not a multiple of the kv heads
+    assert call(sh=4) == -1                       # neither the query heads nor the kv heads (2)
+    assert call(sh=1) == -1                       # one list per sequence is for cosine scores
     assert call(nq=5000) == -1
     assert call(k=0, S=0, Wn=0) == -5             # nothing to attend
     assert call(k=4096) == -3                     # beyond the selection limit
@@ -201,3 +203,27 @@ def test_count_hits_and_prune_reject_before_device_work(L):
     assert pr(m, 0x1000, desc(L, block_size=32, k=0x90000, v=0xa0000, reps=0xb0000), None, 0x3000, None) == -1
     assert pr(m, 0x1000, desc(L), None, 0x3000, None) == -1  # same buffers
     assert pr(m, 0x1000, None, None, 0x3000, None) == -1
+
+
+def test_cache_calls_reject_before_device_work(L):
+    m = desc(L, length=4096, capacity=8192)
+    c = L.brs_page_cache(k=0x50000, v=0x60000, page_of_block=0x70000, page_block=0x71000, page_rows=0x72000,
+                         page_used=0x73000, n_pages=20, reserved=0)
+    # 4 query heads' lists over 2 kv heads: ceil(128 / 64) + 1024 / 64 + 2 lists * k = 2 + 16 + 2 * 2 = 22 > 20
+    assert L.lib.brs_cache_fetch(m, c, 0x80000, 4, 2, 128, 1024, 1, None, None) == -2
+    assert b"pages" in L.lib.brs_last_error()
+    c.n_pages = 0
+    assert L.lib.brs_cache_fetch(m, c, 0x80000, 2, 2, 128, 1024, 1, None, None) == -3
+    c.n_pages = 64
+    c.reserved = 1
+    assert L.lib.brs_cache_reset(m, c, None) == -1
+    c.reserved = 0
+    c.k = 0x50008
+    assert L.lib.brs_cache_reset(m, c, None) == -1     # misaligned pool
+    c.k = 0x50000
+    assert L.lib.brs_cache_fetch(m, c, 0x80000, 3, 2, 128, 1024, 1, None, None) == -1  # lists must tile the kv heads
+    # a chunk of queries is not served by the cached path
+    n = ctypes.c_size_t()
+    assert L.lib.brs_attention_workspace_bytes(m, 2, 64, 2, 2, 128, 1024, ctypes.byref(n)) == 0
+    assert L.lib.brs_retrieval_attention_cached(m, c, 0x1000, 2, 64, 0x80000, 2, 2, 128, 1024, 0.1, 0x3000, None,
+                                                0x100000, n.value, None) == -3

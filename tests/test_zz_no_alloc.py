@@ -31,8 +31,8 @@ def test_static_step_rejects_oversized_workspace_on_host():
     need = ctypes.c_size_t()
     rc = L.lib.brs_attention_workspace_bytes(d, big.n_q_heads, 1, big.n_q_heads, big.k, 0, 0, need)
     assert rc == 0 and need.value > L.lib.brs_static_scratch_bytes()
-    rc = L.lib.brs_retrieval_step_static(d, 0x40000, big.n_q_heads, 1, 0x40000, big.k, 0, 0, 0.1, 0x50000, 0x60000,
-                                         None, 0x70000, None, None)
+    rc = L.lib.brs_retrieval_step_static(d, 0x40000, big.n_q_heads, 1, 0x40000, big.n_q_heads, big.k, 0, 0, 0.1,
+                                         0x50000, 0x60000, None, 0x70000, None, None)
     assert rc == -3 and b"static scratch" in L.lib.brs_last_error()
 
 
@@ -52,8 +52,8 @@ def _run(brs, L, w, static: bool):
         st.out.fill_(float("nan"))
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream().cuda_stream
-        L.check(L.lib.brs_retrieval_step_static(mem.desc, x["q"].data_ptr(), w.n_q_heads, 1, qrep.data_ptr(), w.k,
-                                                w.sinks, w.window, st.scale, st.scores.data_ptr(),
+        L.check(L.lib.brs_retrieval_step_static(mem.desc, x["q"].data_ptr(), w.n_q_heads, 1, qrep.data_ptr(),
+                                                w.n_q_heads, w.k, w.sinks, w.window, st.scale, st.scores.data_ptr(),
                                                 st.idx.data_ptr(), st.vals.data_ptr(), st.out.data_ptr(), None,
                                                 stream))
     else:
