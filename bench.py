@@ -627,6 +627,81 @@ def extra_passes(w, args, layers, hip) -> dict:
     return out
 
 
+def offload_pass(w, args, hip, stream) -> dict:
+    """InfLLM-style offload at the workload's shape: K/V in pinned host memory,
+    a device cache of blocks sized to what one step may need, decode steps
+    whose query drifts (q_t = 0.9 q_(t-1) + 0.44 e_t, so consecutive steps
+    share most of their selection).  Reports the blocks and bytes copied over
+    the host link per step, the fetch kernel's time and link rate (events
+    around its launch after a synchronize), and the whole step's time."""
+    import torch
+
+    import block_retrieval_sparse_amd as brs
+    from block_retrieval_sparse_amd.pipeline import CachedStep
+    from synth import inputs as I
+
+    dev = "cuda:0"
+    x = I.make_all(w, dev)
+    mem = brs.KVMemory(w.batch, w.n_kv_heads, w.head_dim, w.n_tokens, w.block, dtype=I.torch_dtype(w),
+                       rep_mode=w.rep_mode, reps_per_block=w.reps_per_block, row_stride=w.stride, device=dev,
+                       host=True)
+    mem.append(x["k"], x["v"])
+    torch.cuda.synchronize()
+    nbt = -(-w.n_tokens // w.block)
+    S = min(w.sinks, w.n_tokens)
+    ws = max(w.n_tokens - w.window, S)
+    n_pages = -(-S // w.block) + (nbt - ws // w.block if ws < w.n_tokens else 0) + w.group * w.k
+    cache = brs.BlockCache(mem, n_pages)
+    st = CachedStep(mem, cache, w.n_q_heads, w.k, w.sinks, w.window)
+    g = torch.Generator(device=dev).manual_seed(w.seed + 99)
+    q = x["q"].float()
+    n_t = max(args.steps, 10)
+    fetch_ms, step_ms, blocks = [], [], []
+    for t in range(n_t):
+        if t > 0:
+            q = 0.9 * q + math.sqrt(1 - 0.81) * torch.randn(q.shape, generator=g, device=dev)
+        qb = q.to(I.torch_dtype(w))
+        qrep = qb[:, :, -1, :].contiguous()
+        torch.cuda.synchronize()
+        before = int(cache.fetched.sum())
+        e = [hip.create() for _ in range(4)]
+        hip.record(e[0], stream)
+        st.score(qrep)
+        st.select()
+        torch.cuda.synchronize()
+        hip.record(e[1], stream)
+        st.fetch()
+        hip.record(e[2], stream)
+        st.attend(qb)
+        hip.record(e[3], stream)
+        torch.cuda.synchronize()
+        fetch_ms.append(hip.elapsed_ms(e[1], e[2]))
+        step_ms.append(hip.elapsed_ms(e[0], e[1]) + hip.elapsed_ms(e[1], e[3]))
+        for ev in e:
+            hip.destroy(ev)
+        blocks.append(int(cache.fetched.sum()) - before)
+    row_bytes = w.stride * w.elem_bytes
+    blk_bytes = 2 * w.block * row_bytes  # K and V of one block
+    warm = blocks[1:]
+    res = {
+        "workload": w.name, "pages_per_kv_head": n_pages, "steps": n_t,
+        "cold_step": {"blocks_copied": blocks[0], "bytes": blocks[0] * blk_bytes, "fetch_us": fetch_ms[0] * 1e3,
+                      "link_GB/s": blocks[0] * blk_bytes / (fetch_ms[0] * 1e-3) / 1e9},
+        "steady": {"blocks_copied_per_step": sum(warm) / len(warm),
+                   "bytes_per_step": sum(warm) / len(warm) * blk_bytes,
+                   "fetch_us_median": pct(fetch_ms[1:], 0.5) * 1e3,
+                   "link_GB/s": (sum(warm) * blk_bytes) / (sum(fetch_ms[1:]) * 1e-3) / 1e9,
+                   "step_us_median": pct(step_ms[1:], 0.5) * 1e3},
+        "note": "K/V in pinned host memory, a device page cache of the blocks one step may need; query drifts "
+                "0.9 per step; step = score + select + fetch + attention (events with a synchronize after the "
+                "selection, so the fetch is timed alone)",
+    }
+    del st, cache, mem, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def run(args):
     import torch
 
@@ -665,6 +740,8 @@ def run(args):
         line["roofline"]["frac_of_gather_read"] = line["roofline"]["achieved"] / refs["gather_GB/s"]
         line["roofline"]["frac_of_contiguous_read"] = line["roofline"]["achieved"] / refs["contiguous_GB/s"]
     if args.workload == HEADLINE and not args.only:
+        log("offload pass (host memory + device block cache) ...")
+        line["offload"] = offload_pass(main, args, hip, stream)
         for key, name in EXTRA:
             sub = run_workload(WORKLOADS[name], args, hip, stream, cyc, headline=False)
             if sub.get("roofline", {}).get("bound") == "hbm":
