@@ -24,6 +24,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kNeedWords = 8192;  // blocks per (batch, kv head): 262144
 constexpr int kMaxPages = 2048;   // pages per (batch, kv head)
+constexpr int kBatch = 8;         // 16-byte units of K and of V a thread reads before it writes
 
 struct FetchArgs {
   const char* host_k;
@@ -176,23 +177,38 @@ __global__ __launch_bounds__(kThreads) void cache_fetch_kernel(FetchArgs a) {
   const int n_jobs = s_n[1];
   if (tid == 0 && a.fetched) a.fetched[bg] += n_jobs;
 
-  // the copies: 16-byte units of every job's rows, K then V
+  // The copies: 16-byte units of every job's rows, K and V.  Each thread
+  // issues the loads of kBatch units of K and of V before any store, so
+  // that 2 kBatch host reads per thread are in flight across the link (a
+  // load-store pair at a time would leave the link idle for most of each
+  // round trip).
   const int units_row = a.row_bytes / 16;
-  const char* hk = a.host_k + (int64_t)bg * a.slice_bytes_mem;
-  const char* hv = a.host_v + (int64_t)bg * a.slice_bytes_mem;
-  char* pk = a.pool_k + (int64_t)bg * a.slice_bytes_pool;
-  char* pv = a.pool_v + (int64_t)bg * a.slice_bytes_pool;
+  const char* __restrict__ hk = a.host_k + (int64_t)bg * a.slice_bytes_mem;
+  const char* __restrict__ hv = a.host_v + (int64_t)bg * a.slice_bytes_mem;
+  char* __restrict__ pk = a.pool_k + (int64_t)bg * a.slice_bytes_pool;
+  char* __restrict__ pv = a.pool_v + (int64_t)bg * a.slice_bytes_pool;
   for (int j = 0; j < n_jobs; ++j) {
     const int4 jb = jobs[j];
     const int n_units = (jb.w - jb.z) * units_row;
     const int64_t src0 = ((int64_t)jb.x * B + jb.z) * a.row_bytes;
     const int64_t dst0 = ((int64_t)jb.y * B + jb.z) * a.row_bytes;
-    for (int u = tid; u < n_units; u += kThreads) {
-      const int64_t o = (int64_t)u * 16;
-      const uint4 kv = *reinterpret_cast<const uint4*>(hk + src0 + o);
-      const uint4 vv = *reinterpret_cast<const uint4*>(hv + src0 + o);
-      *reinterpret_cast<uint4*>(pk + dst0 + o) = kv;
-      *reinterpret_cast<uint4*>(pv + dst0 + o) = vv;
+    for (int u0 = tid; u0 < n_units; u0 += kBatch * kThreads) {
+      uint4 kv[kBatch], vv[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        // past the job's end a lane re-reads unit u0 (no branch around the loads)
+        const int u = u0 + i * kThreads < n_units ? u0 + i * kThreads : u0;
+        kv[i] = *reinterpret_cast<const uint4*>(hk + src0 + (int64_t)u * 16);
+        vv[i] = *reinterpret_cast<const uint4*>(hv + src0 + (int64_t)u * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int u = u0 + i * kThreads;
+        if (u < n_units) {
+          *reinterpret_cast<uint4*>(pk + dst0 + (int64_t)u * 16) = kv[i];
+          *reinterpret_cast<uint4*>(pv + dst0 + (int64_t)u * 16) = vv[i];
+        }
+      }
     }
   }
 }

@@ -17,8 +17,12 @@
  * --------------------------------
  * - All pointers to tensors are DEVICE pointers (HIP device memory) unless a
  *   parameter says "host".  The caller allocates and owns all of them; the
- *   library never allocates, frees or retains device memory, and never
- *   creates streams.
+ *   library never allocates or frees device memory and never creates
+ *   streams.  It keeps no state between calls, with two exceptions:
+ *   brs_retrieval_step_static's workspace, a fixed device array the library
+ *   holds on every GPU it runs on until the process ends, and the events
+ *   armed by brs_profile_next_attention (per thread, until the next
+ *   attention call takes them).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *   device work is enqueued on it; results are ready once the caller has
  *   synchronised that stream.

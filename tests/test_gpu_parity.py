@@ -57,6 +57,12 @@ SMALL = {
     "prefill_many_segments": W["infllm_gqa_decode_128k"].scaled(n_q_heads=4, n_kv_heads=2, n_tokens=300 * 16 + 7,
                                                                  block=16, window=64, sinks=8, k=250, n_q=64,
                                                                  planted_per_head=0),
+    # a query chunk with more selected blocks than the prefill kernel's
+    # segment table holds (k + 2 > 256): the split path with row groups of
+    # 16 query rows takes it
+    "prefill_k_past_segment_table": W["infllm_gqa_decode_128k"].scaled(
+        n_q_heads=4, n_kv_heads=2, n_tokens=400 * 16 + 7, block=16, window=64, sinks=8, k=300, n_q=64,
+        planted_per_head=0),
 }
 
 
