@@ -93,6 +93,115 @@ __device__ void rank_and_copy(const double* key, int* chosen, const T* base, T* 
   }
 }
 
+// Row-parallel forms of MEAN and TOPNORM, for rows whose head dims are whole
+// 16-byte units (U per row, U <= L): L lanes share a row, lane `sub` holding
+// unit `sub`, 256 / L rows per pass, `passes` passes (at most kRowPasses);
+// every load of the block is issued before any is used.  Same arithmetic
+// as the per-column / per-row forms: float64 sums, one rounding.
+constexpr int kRowPasses = 16;
+
+template <typename T>
+struct Unit;  // the elements of a 16-byte unit as float64
+template <>
+struct Unit<uint16_t> {
+  static constexpr int n = 8;
+  __device__ static double at(const uint4& u, int e) {
+    const int k = e >> 1;  // the 32-bit word; element 2k in its low half, 2k + 1 in its high half
+    const uint32_t w = k == 0 ? u.x : (k == 1 ? u.y : (k == 2 ? u.z : u.w));
+    return (double)((e & 1) ? bf16_hi(w) : bf16_lo(w));
+  }
+};
+template <>
+struct Unit<float> {
+  static constexpr int n = 4;
+  __device__ static double at(const uint4& u, int e) {
+    return (double)__uint_as_float(e == 0 ? u.x : (e == 1 ? u.y : (e == 2 ? u.z : u.w)));
+  }
+};
+
+template <typename T, int L>
+__device__ __forceinline__ void load_block_rows(const T* base, int B, int rs, int U, int passes, uint4 (&raw)[kRowPasses]) {
+  constexpr int RPP = 256 / L;
+  const int sub = threadIdx.x % L, rw = threadIdx.x / L;
+  const int uu = sub < U ? sub : 0;
+#pragma unroll
+  for (int p = 0; p < kRowPasses; ++p) {
+    if (p < passes) {
+      const int t = p * RPP + rw;
+      const int tt = t < B ? t : 0;  // rows past the block re-read row 0 (no branch around the loads)
+      raw[p] = *reinterpret_cast<const uint4*>(base + (int64_t)tt * rs + uu * Unit<T>::n);
+    }
+  }
+}
+
+template <typename T, int L>
+__global__ __launch_bounds__(256) void rep_mean_rows_kernel(const T* __restrict__ K, T* __restrict__ reps,
+                                                            int64_t b0, int B, int d, int rs, int64_t cap,
+                                                            int64_t capB, int passes) {
+  constexpr int RPP = 256 / L, VN = Unit<T>::n;
+  __shared__ double part[RPP][L * VN];
+  const int64_t blk = b0 + blockIdx.x;
+  const int64_t bg = blockIdx.y;
+  const T* base = K + (bg * cap + blk * B) * (int64_t)rs;
+  const int U = d / VN;
+  const int sub = threadIdx.x % L, rw = threadIdx.x / L;
+  uint4 raw[kRowPasses];
+  load_block_rows<T, L>(base, B, rs, U, passes, raw);
+  double acc[VN];
+#pragma unroll
+  for (int e = 0; e < VN; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int p = 0; p < kRowPasses; ++p)
+    if (p < passes && p * RPP + rw < B) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] += Unit<T>::at(raw[p], e);
+    }
+#pragma unroll
+  for (int e = 0; e < VN; ++e) part[rw][sub * VN + e] = acc[e];
+  __syncthreads();
+  T* dst = reps + (bg * capB + blk) * (int64_t)d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    double s = 0.0;
+    for (int r = 0; r < RPP; ++r) s += part[r][c];
+    store_rounded(dst + c, s / (double)B);
+  }
+}
+
+template <typename T, int L>
+__global__ __launch_bounds__(256) void rep_topnorm_rows_kernel(const T* __restrict__ K, T* __restrict__ reps,
+                                                               int64_t b0, int B, int R, int d, int rs, int64_t cap,
+                                                               int64_t capB, int passes) {
+  constexpr int RPP = 256 / L, VN = Unit<T>::n;
+  __shared__ double n2[kRowPasses * RPP];
+  __shared__ int chosen[64];
+  const int64_t blk = b0 + blockIdx.x;
+  const int64_t bg = blockIdx.y;
+  const T* base = K + (bg * cap + blk * B) * (int64_t)rs;
+  const int U = d / VN;
+  const int sub = threadIdx.x % L, rw = threadIdx.x / L;
+  if (threadIdx.x < R) chosen[threadIdx.x] = threadIdx.x;
+  uint4 raw[kRowPasses];
+  load_block_rows<T, L>(base, B, rs, U, passes, raw);
+#pragma unroll
+  for (int p = 0; p < kRowPasses; ++p) {
+    if (p < passes) {
+      double s = 0.0;
+      if (sub < U) {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+          const double x = Unit<T>::at(raw[p], e);
+          s = fma(x, x, s);
+        }
+      }
+      for (int off = 1; off < L; off <<= 1) s += __shfl_xor(s, off);
+      const int t = p * RPP + rw;
+      if (sub == 0 && t < B) n2[t] = s;
+    }
+  }
+  __syncthreads();
+  rank_and_copy(n2, chosen, base, reps + (bg * capB + blk) * (int64_t)R * d, B, R, d, rs);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rep_topnorm_kernel(const T* __restrict__ K, T* __restrict__ reps,
                                                           int64_t b0, int B, int R, int d, int rs, int64_t cap,
@@ -216,10 +325,46 @@ hipError_t launch_rep_build(const brs_memory& m, int64_t b0, int64_t b1, const v
                          b0 * per_block);
     return hipGetLastError();
   }
+  // the row-parallel forms when a row's head dims are whole 16-byte units
+  // (at most 32 per row) and the block fits in kRowPasses passes
+  const int es = elem_bytes(m.dtype);
+  const int U = (m.head_dim * es) % 16 == 0 ? m.head_dim * es / 16 : 0;
+  const int L = U <= 0 ? 0 : (U <= 4 ? 4 : (U <= 8 ? 8 : (U <= 16 ? 16 : (U <= 32 ? 32 : 0))));
+  const int passes = L ? (m.block_size + 256 / L - 1) / (256 / L) : 0;
+  const bool rows = L > 0 && passes <= kRowPasses && (m.row_stride * es) % 16 == 0 &&
+                    ((uintptr_t)m.k % 16) == 0;
   // the grid's y dimension covers (batch, kv head); x covers the new blocks
   for (int64_t done = 0; done < nblk; done += 65535) {
     const int64_t n = nblk - done < 65535 ? nblk - done : 65535;
     const dim3 grid((unsigned)n, (unsigned)heads);
+    if (rows && (m.rep_mode == BRS_REP_MEAN || m.rep_mode == BRS_REP_TOPNORM)) {
+      const bool mean = m.rep_mode == BRS_REP_MEAN;
+#define BRS_ROWS_LAUNCH(T, LL)                                                                                   \
+  if (L == LL) {                                                                                                 \
+    if (mean)                                                                                                    \
+      hipLaunchKernelGGL((rep_mean_rows_kernel<T, LL>), grid, dim3(256), 0, s, (const T*)m.k, (T*)m.reps,       \
+                         b0 + done, m.block_size, m.head_dim, m.row_stride, m.capacity, capB, passes);          \
+    else                                                                                                         \
+      hipLaunchKernelGGL((rep_topnorm_rows_kernel<T, LL>), grid, dim3(256), 0, s, (const T*)m.k, (T*)m.reps,    \
+                         b0 + done, m.block_size, m.reps_per_block, m.head_dim, m.row_stride, m.capacity, capB, \
+                         passes);                                                                                \
+  }
+      if (m.dtype == BRS_F32) {
+        BRS_ROWS_LAUNCH(float, 4)
+        BRS_ROWS_LAUNCH(float, 8)
+        BRS_ROWS_LAUNCH(float, 16)
+        BRS_ROWS_LAUNCH(float, 32)
+      } else {
+        BRS_ROWS_LAUNCH(uint16_t, 4)
+        BRS_ROWS_LAUNCH(uint16_t, 8)
+        BRS_ROWS_LAUNCH(uint16_t, 16)
+        BRS_ROWS_LAUNCH(uint16_t, 32)
+      }
+#undef BRS_ROWS_LAUNCH
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      continue;
+    }
     if (m.rep_mode == BRS_REP_MEAN) {
       if (m.dtype == BRS_F32)
         hipLaunchKernelGGL(rep_mean_kernel<float>, grid, dim3(128), 0, s, (const float*)m.k, (float*)m.reps,
