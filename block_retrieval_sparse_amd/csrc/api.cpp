@@ -573,13 +573,20 @@ int brs_retrieval_attention_cached(const brs_memory* m, const brs_page_cache* c,
   if (rc) return rc;
   rc = check_attention_buffers(g, q, idx, k, out, lse, workspace, workspace_bytes);
   if (rc) return rc;
-  if (n_q != 1 || !g.slot) return fail(BRS_E_UNSUPPORTED, "a cached memory supports decode on the slot kernels");
   g.pages = c->page_of_block;
   g.pages_stride = (int)(m->capacity / m->block_size + 1);
   g.head_stride = (int64_t)c->n_pages * m->block_size * m->row_stride;
+  // the chunked-prefill kernel, or the slot kernels, both read K/V through the page table
+  const bool prefill = g.prefill && brs::prefill_supported(g);
+  if (!prefill && !g.slot)
+    return fail(BRS_E_UNSUPPORTED, "a cached memory supports the slot-layout and chunked-prefill kernels only");
   hipEvent_t e0 = g_prof_start, e1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   hipStream_t s = (hipStream_t)stream;
+  if (prefill) {
+    hipError_t e = brs::launch_attn_prefill(g, c->k, c->v, q, idx, out, lse, s, e0, e1);
+    return e == hipSuccess ? ok() : hip_fail(e, "attn_prefill (cached)");
+  }
   hipError_t e = brs::launch_attn_split(g, c->k, c->v, q, idx, workspace, out, s, e0, e1);
   if (e != hipSuccess) return hip_fail(e, "attn_split (cached)");
   e = brs::launch_attn_merge(g, workspace, out, lse, s);

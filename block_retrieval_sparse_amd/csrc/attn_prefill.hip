@@ -68,6 +68,11 @@ struct PrefillArgs {
   int win_start;
   float qscale;
   int n_tiles, n_units, per_xcd;
+  // K/V read through a page table (a device cache of blocks; k and v then
+  // point to the page pool): page of block x of slice bg at pages[bg *
+  // pages_stride + x]; null: the memory itself
+  const int32_t* pages;
+  int pages_stride;
 };
 
 __device__ __forceinline__ bf16x8_p as_bf16x8_p(const uint4& u) { return __builtin_bit_cast(bf16x8_p, u); }
@@ -212,8 +217,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
   const int n_tok = sh_tot[0];
   const int n_stages = (n_tok + kStage - 1) / kStage;
 
-  // token table: stream offset tau -> (position, byte offset), kNoPos past the end
+  // token table: stream offset tau -> (position, byte offset of its K/V
+  // row: position order in the memory, or through the page table), kNoPos
+  // past the end
   const int row_bytes = a.row_stride * 2;
+  const int32_t* ptab = a.pages ? a.pages + (int64_t)bg * a.pages_stride : nullptr;
   // (count a multiple of 512: each thread fills a run of count / 512
   // consecutive entries, with one search for the run's first segment)
   auto fill = [&](int tau0, int count) {
@@ -230,7 +238,12 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
       if (tau < n_tok) {
         while (tau >= c.w + c.y) c = s_items[++lo];  // segments are contiguous in the stream
         const int pos = c.x + (tau - c.w);
-        e = make_int2(pos, pos * row_bytes);
+        int row = pos;
+        if (ptab) {
+          const int x = pos / a.B;
+          row = ptab[x] * a.B + (pos - x * a.B);
+        }
+        e = make_int2(pos, row * row_bytes);
       }
       s_tab[tau & (kTabTokens - 1)] = e;
     }
@@ -537,6 +550,8 @@ hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, 
   a.per_xcd = (a.n_units + kXcds - 1) / kXcds;
   a.slice_bytes = (int)(g.head_stride * 2);
   a.win_start = g.win_start;
+  a.pages = g.pages;
+  a.pages_stride = g.pages_stride;
   const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(512);
   const bool ones = 8 * a.nvec < 16 * a.nj;  // a spare padded column exists
 #define BRS_PREFILL_LAUNCH(DP, NJ, ONES)                                                      \

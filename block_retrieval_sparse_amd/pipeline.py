@@ -97,15 +97,16 @@ class RetrievalStep:
 
 
 class CachedStep(RetrievalStep):
-    """One decode step over an offloaded memory (K/V in host memory, see
-    ``KVMemory(host=True)``): scores and selection as RetrievalStep, then
-    brs_cache_fetch stages the blocks the step reads into the cache, then the
-    attention reads them there (brs_retrieval_attention_cached).  Outputs are
-    those of the same step on a resident memory, bit for bit."""
+    """One step (decode, or a chunk of n_q queries) over an offloaded memory
+    (K/V in host memory, see ``KVMemory(host=True)``): scores and selection
+    as RetrievalStep, then brs_cache_fetch stages the blocks the step reads
+    into the cache, then the attention reads them there
+    (brs_retrieval_attention_cached).  Outputs are those of the same step on
+    a resident memory, bit for bit."""
 
     def __init__(self, mem: KVMemory, cache: BlockCache, n_q_heads: int, k: int, n_sink: int, window: int,
-                 scale: float | None = None, select: str = "head"):
-        super().__init__(mem, n_q_heads, 1, k, n_sink, window, scale=scale, select=select)
+                 scale: float | None = None, select: str = "head", n_q: int = 1):
+        super().__init__(mem, n_q_heads, n_q, k, n_sink, window, scale=scale, select=select)
         self.cache = cache
 
     def fetch(self, stream=None) -> None:
@@ -114,7 +115,7 @@ class CachedStep(RetrievalStep):
     def attend(self, q: torch.Tensor, stream=None, profile_events=None) -> torch.Tensor:
         if profile_events is not None:
             check(lib.brs_profile_next_attention(profile_events[0], profile_events[1]))
-        check(lib.brs_retrieval_attention_cached(self.mem.desc, self.cache.desc, q.data_ptr(), self.n_q_heads, 1,
+        check(lib.brs_retrieval_attention_cached(self.mem.desc, self.cache.desc, q.data_ptr(), self.n_q_heads, self.n_q,
                                                  self.idx.data_ptr() if self.k else None, self.score_heads, self.k,
                                                  self.n_sink, self.window, self.scale, self.out.data_ptr(),
                                                  _ptr(self.lse), self.workspace.data_ptr(), self.workspace.numel(),

@@ -404,9 +404,12 @@ int brs_cache_fetch(const brs_memory* m, const brs_page_cache* c, const int32_t*
 /* brs_retrieval_attention for an offloaded memory: K/V are read from the
  * cache's pages through page_of_block (after brs_cache_fetch with the same
  * selection), with results identical bit for bit to brs_retrieval_attention
- * over the same data resident in device memory.  Decode only (n_q = 1) on
- * the slot kernels (bfloat16, head_dim 64 or 128); other shapes return
- * BRS_E_UNSUPPORTED.  Workspace as brs_attention_workspace_bytes. */
+ * over the same data resident in device memory.  Served by the kernels that
+ * read K/V row by row: the slot-layout decode kernels (bfloat16, head_dim 64
+ * or 128, any n_q whose rows they take) and the chunked-prefill kernel
+ * (bfloat16, n_q >= 64, head_dim <= 128, k + 2 <= 256; InfLLM "method":
+ * memory units stay offloaded during chunked prefill as well); other shapes
+ * return BRS_E_UNSUPPORTED.  Workspace as brs_attention_workspace_bytes. */
 int brs_retrieval_attention_cached(const brs_memory* m, const brs_page_cache* c, const void* q, int32_t n_q_heads,
                                    int32_t n_q, const int32_t* idx, int32_t idx_heads, int32_t k, int64_t n_sink,
                                    int64_t window, float scale, float* out, float* lse, void* workspace,

@@ -117,3 +117,45 @@ def test_offload_1m_token_memory_step():
     idx = a.idx.cpu().numpy()
     want = sum(len(np.unique(idx[0, g * w.group:(g + 1) * w.group])) for g in range(w.n_kv_heads))
     assert int(cache.fetched.sum()) == want
+
+
+CHUNK_CASES = {
+    # chunked prefill on the matrix-core kernel, dot scores, one list per query head
+    "prefill_dot": W["infllm_gqa_decode_128k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=6000 + 11, block=64,
+                                                      window=200, sinks=16, k=5, n_q=100, planted_per_head=0),
+    # MemLong chunked prefill: cosine scores, one list per sequence, head dim 100 in rows of 104
+    "prefill_cosine": W["memlong_chunk_prefill_80k"].scaled(n_q_heads=4, n_kv_heads=4, n_tokens=8 * 512 + 512),
+    # several queries on the slot kernels
+    "decode_multi_q": W["infllm_gqa_decode_128k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=6000, window=300, k=5,
+                                                         n_q=3, planted_per_head=0),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNK_CASES))
+def test_offload_chunk_matches_resident(name):
+    """A step of n_q > 1 queries (InfLLM "method": the memory units stay in
+    host memory during chunked prefill too) over the cache equals the step
+    on the resident memory, bit for bit: the prefill kernel reads its token
+    rows through the page table as the slot kernels do."""
+    import block_retrieval_sparse_amd as brs
+    from block_retrieval_sparse_amd.pipeline import CachedStep, RetrievalStep
+
+    w = CHUNK_CASES[name]
+    res, x = C.load(w)
+    rep_dtype = torch.bfloat16 if w.rep_mode == "embed" else I.torch_dtype(w)
+    off = brs.KVMemory(w.batch, w.n_kv_heads, w.head_dim, w.n_tokens, w.block, dtype=I.torch_dtype(w),
+                       rep_mode=w.rep_mode, reps_per_block=w.reps_per_block, rep_dim=w.rep_dim, rep_dtype=rep_dtype,
+                       row_stride=w.stride, device="cuda", host=True)
+    given = x.get("given_reps", x.get("embeds"))
+    off.append(x["k"], x["v"], given[:, :, :w.n_tokens // w.block] if given is not None else None)
+    qrep = x["rq"] if w.rep_mode == "embed" else x["q"][:, :, -1, :].contiguous()
+    a = RetrievalStep(res, w.n_q_heads, w.n_q, w.k, w.sinks, w.window)
+    a.run_separate(x["q"], qrep)
+    lists = 1 if w.rep_mode == "embed" else w.group
+    cache = brs.BlockCache(off, pages_needed(w, w.n_tokens, lists))
+    b = CachedStep(off, cache, w.n_q_heads, w.k, w.sinks, w.window, n_q=w.n_q)
+    b.run(x["q"], qrep)
+    torch.cuda.synchronize()
+    assert torch.equal(a.idx, b.idx)
+    assert torch.equal(a.out, b.out), float((a.out - b.out).abs().max())
+    assert int(cache.fetched.sum()) > 0
