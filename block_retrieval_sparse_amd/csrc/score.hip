@@ -231,14 +231,11 @@ __global__ __launch_bounds__(256) void score_dot_kernel(const T* __restrict__ q,
 // Row-granular variant, used when R divides the slots of a wave: each slot
 // (L lanes) takes one representative row, RPS rows in flight per slot, and a
 // block's R rows sit in R adjacent slots, so the max over representatives is
-// a shuffle.  Rows of one (batch, kv head) are contiguous in memory.  A
-// workgroup takes `batches` consecutive batches of slots * RPS rows (the
-// queries are converted once for all of them).
+// a shuffle.  Rows of one (batch, kv head) are contiguous in memory.
 template <typename T, int EPL, int G, int L, int RPS>
 __global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict__ q, const T* __restrict__ reps,
                                                              float* __restrict__ scores, int d, int R, int hkv,
-                                                             int64_t capB, int64_t lo, int64_t hi, int grouped,
-                                                             int batches) {
+                                                             int64_t capB, int64_t lo, int64_t hi, int grouped) {
   constexpr int UPL = EPL / Vec<T>::n;
   constexpr int SPW = 64 / L;
   const int lane = threadIdx.x & 63;
@@ -260,57 +257,48 @@ __global__ __launch_bounds__(256) void score_dot_rows_kernel(const T* __restrict
     }
   }
   const int64_t row_lo = lo * R, row_hi = hi * R;
+  const int64_t row0 = row_lo + (int64_t)blockIdx.x * slots * RPS;
   const T* rbase = reps + (int64_t)bg * capB * R * d + sub * EPL;
   float* sbase = scores + ((int64_t)b * hq + g * G) * capB;
+
   uint4 raw[RPS][UPL];
-  auto load = [&](uint4(&dst)[RPS][UPL], int bt) {
-    const int64_t row0 = row_lo + ((int64_t)blockIdx.x * batches + bt) * slots * RPS;
 #pragma unroll
-    for (int i = 0; i < RPS; ++i) {
-      const int64_t row = row0 + (int64_t)i * slots + slot;
+  for (int i = 0; i < RPS; ++i) {
+    const int64_t row = row0 + (int64_t)i * slots + slot;
 #pragma unroll
-      for (int u = 0; u < UPL; ++u)
-        dst[i][u] = row < row_hi ? *reinterpret_cast<const uint4*>(rbase + row * d + u * Vec<T>::n)
-                                 : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < UPL; ++u)
+      raw[i][u] = row < row_hi ? *reinterpret_cast<const uint4*>(rbase + row * d + u * Vec<T>::n)
+                               : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    const int64_t row = row0 + (int64_t)i * slots + slot;
+    double x[EPL];
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) Vec<T>::to_f64(raw[i][u], &x[u * Vec<T>::n]);
+    double acc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      double a = 0.0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = fma(qd[j][e], x[e], a);
+      acc[j] = a;
     }
-  };
-  auto score = [&](const uint4(&src)[RPS][UPL], int bt) {
-    const int64_t row0 = row_lo + ((int64_t)blockIdx.x * batches + bt) * slots * RPS;
 #pragma unroll
-    for (int i = 0; i < RPS; ++i) {
-      const int64_t row = row0 + (int64_t)i * slots + slot;
-      double x[EPL];
+    for (int j = 0; j < G; ++j) acc[j] = group_max_f64<L>(group_sum_f64<L>(acc[j]), L * R);
+    if (row < row_hi && (row % R) == 0) {
+      const int64_t blk = row / R;
+      if (grouped) {
+        double gb = acc[0];
 #pragma unroll
-      for (int u = 0; u < UPL; ++u) Vec<T>::to_f64(src[i][u], &x[u * Vec<T>::n]);
-      double acc[G];
+        for (int j = 1; j < G; ++j) gb = nan_max(gb, acc[j]);
+        if (sub == 0) scores[(int64_t)bg * capB + blk] = (float)gb;
+      } else {
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        double a = 0.0;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) a = fma(qd[j][e], x[e], a);
-        acc[j] = a;
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] = group_max_f64<L>(group_sum_f64<L>(acc[j]), L * R);
-      if (row < row_hi && (row % R) == 0) {
-        const int64_t blk = row / R;
-        if (grouped) {
-          double gb = acc[0];
-#pragma unroll
-          for (int j = 1; j < G; ++j) gb = nan_max(gb, acc[j]);
-          if (sub == 0) scores[(int64_t)bg * capB + blk] = (float)gb;
-        } else {
-#pragma unroll
-          for (int j = 0; j < G; ++j)
-            if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)acc[j];
-        }
+        for (int j = 0; j < G; ++j)
+          if (sub == (j % L)) sbase[(int64_t)j * capB + blk] = (float)acc[j];
       }
     }
-  };
-  for (int bt = 0; bt < batches; ++bt) {
-    if (row_lo + ((int64_t)blockIdx.x * batches + bt) * slots * RPS >= row_hi) break;
-    load(raw, bt);
-    score(raw, bt);
   }
 }
 
@@ -450,23 +438,20 @@ hipError_t run_rows(const brs_memory& m, const void* q, int64_t lo, int64_t hi, 
   const dim3 block(256);
   const int64_t capB = m.capacity / m.block_size;
   if (want >= 4) {
-    // large inputs: several row batches per workgroup, about 2048 workgroups per 512 Ki rows
-    const int batches = want >= 32 ? 8 : (want >= 16 ? 4 : (want >= 8 ? 2 : 1));
-    const int64_t per = (int64_t)slots * 4 * batches;
-    const int64_t gx = (rows + per - 1) / per;
+    const int64_t gx = (rows + slots * 4 - 1) / (slots * 4);
     BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 4>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
-                       hi, grouped, batches);
+                       hi, grouped);
   } else if (want >= 2) {
     const int64_t gx = (rows + slots * 2 - 1) / (slots * 2);
     BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 2>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
-                       hi, grouped, 1);
+                       hi, grouped);
   } else {
     const int64_t gx = (rows + slots - 1) / slots;
     BRS_SCORE_LAUNCH((score_dot_rows_kernel<T, EPL, G, L, 1>), dim3((unsigned)gx, (unsigned)bg), block, s,
                        (const T*)q, (const T*)m.reps, scores, m.head_dim, m.reps_per_block, m.n_kv_heads, capB, lo,
-                       hi, grouped, 1);
+                       hi, grouped);
   }
   return hipGetLastError();
 }
