@@ -131,8 +131,9 @@ CHUNK_CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CHUNK_CASES))
-def test_offload_chunk_matches_resident(name):
+@pytest.mark.parametrize("name,select", [(n, "head") for n in CHUNK_CASES] + [("prefill_dot", "group"),
+                                                                             ("decode_multi_q", "group")])
+def test_offload_chunk_matches_resident(name, select):
     """A step of n_q > 1 queries (InfLLM "method": the memory units stay in
     host memory during chunked prefill too) over the cache equals the step
     on the resident memory, bit for bit: the prefill kernel reads its token
@@ -149,11 +150,11 @@ def test_offload_chunk_matches_resident(name):
     given = x.get("given_reps", x.get("embeds"))
     off.append(x["k"], x["v"], given[:, :, :w.n_tokens // w.block] if given is not None else None)
     qrep = x["rq"] if w.rep_mode == "embed" else x["q"][:, :, -1, :].contiguous()
-    a = RetrievalStep(res, w.n_q_heads, w.n_q, w.k, w.sinks, w.window)
+    a = RetrievalStep(res, w.n_q_heads, w.n_q, w.k, w.sinks, w.window, select=select)
     a.run_separate(x["q"], qrep)
-    lists = 1 if w.rep_mode == "embed" else w.group
+    lists = 1 if (w.rep_mode == "embed" or select == "group") else w.group
     cache = brs.BlockCache(off, pages_needed(w, w.n_tokens, lists))
-    b = CachedStep(off, cache, w.n_q_heads, w.k, w.sinks, w.window, n_q=w.n_q)
+    b = CachedStep(off, cache, w.n_q_heads, w.k, w.sinks, w.window, select=select, n_q=w.n_q)
     b.run(x["q"], qrep)
     torch.cuda.synchronize()
     assert torch.equal(a.idx, b.idx)
