@@ -222,8 +222,12 @@ def test_cache_calls_reject_before_device_work(L):
     assert L.lib.brs_cache_reset(m, c, None) == -1     # misaligned pool
     c.k = 0x50000
     assert L.lib.brs_cache_fetch(m, c, 0x80000, 3, 2, 128, 1024, 1, None, None) == -1  # lists must tile the kv heads
-    # a chunk of queries is not served by the cached path
+    # a float32 memory is served by neither the slot-layout nor the prefill kernels, the two that read
+    # K/V through a page table
+    mf = desc(L, dtype=L.BRS_F32, rep_dtype=L.BRS_F32, length=4096, capacity=8192)
     n = ctypes.c_size_t()
-    assert L.lib.brs_attention_workspace_bytes(m, 2, 64, 2, 2, 128, 1024, ctypes.byref(n)) == 0
-    assert L.lib.brs_retrieval_attention_cached(m, c, 0x1000, 2, 64, 0x80000, 2, 2, 128, 1024, 0.1, 0x3000, None,
-                                                0x100000, n.value, None) == -3
+    for n_q in (1, 64):
+        assert L.lib.brs_attention_workspace_bytes(mf, 2, n_q, 2, 2, 128, 1024, ctypes.byref(n)) == 0
+        assert L.lib.brs_retrieval_attention_cached(mf, c, 0x1000, 2, n_q, 0x80000, 2, 2, 128, 1024, 0.1, 0x3000,
+                                                    None, 0x100000, n.value, None) == -3
+        assert b"slot-layout and chunked-prefill" in L.lib.brs_last_error()
