@@ -14,8 +14,9 @@
 //     positions <= its last query (the causal limit), and flattens them into
 //     a token stream with a position table in LDS;
 //   - each 64-token stage of K and V is staged once in LDS for all 8 waves,
-//     in three buffers fed by a ring of loads four stages ahead, so global
-//     loads are in flight while earlier stages are multiplied;
+//     in two buffers each (K is stored two stages ahead of the softmax, V
+//     one), fed by a ring of loads four stages ahead, so global loads are in
+//     flight while earlier stages are multiplied;
 //   - S^T = K Q^T and O += P V on v_mfma_f32_16x16x32_bf16 with the layouts
 //     of the decode kernel (V read back transposed with ds_read_b64_tr_b16,
 //     P split into bf16 high and low parts so weights keep ~16 bits);
@@ -26,7 +27,6 @@
 // then fetched from HBM once into that XCD's L2 and shared by its tiles.
 #include <hip/hip_ext.h>
 #include <math.h>
-#include <stdlib.h>
 
 #include "brs_internal.h"
 
@@ -35,14 +35,14 @@ namespace {
 
 constexpr int kPrefItems = 256;  // segments of one (batch, kv head) held in LDS
 constexpr int kPrefQ = 64;       // queries per workgroup
-constexpr int kStage = 64;       // tokens per stage (two 32-token halves)
 constexpr float kLazyP = 8.0f;
 constexpr float kFarNegP = -1e30f;
 constexpr int kXcds = 8;
-constexpr int kAhead = 4;         // stages of K/V loads in flight per thread (register ring)
-constexpr int kBufs = 3;          // stage buffers in LDS
-constexpr int kTabTokens = 4096;  // token table ring (64 stages)
-constexpr int kRefill = 32;       // stages refilled at a time (half the ring)
+constexpr int kParts = 2;      // token parts: waves per query group
+constexpr int kThreads = 256 * kParts;
+constexpr int kStage = 32 * kParts;  // tokens per stage
+constexpr int kAhead = 4;      // stages of K/V loads in flight per thread (register ring)
+constexpr int kRefill = 32;    // token-table stages refilled at a time (half the ring)
 constexpr int kNoPos = 0x7fffffff;
 constexpr int kOutOfRange = 0x7ffff000;  // buffer offset past any slice: loads return zeros
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data, no swizzle)
@@ -85,27 +85,44 @@ __device__ __forceinline__ int dpp_mov_i(int v) {
 }
 
 
+// PAGED: K/V rows are read through the page table of a block cache.
 // DP: head dim rounded up to a multiple of 32 (the k chunk of the S^T MFMA).
 // NJ: 16-column output tiles in use, ceil(d / 16) (compile-time, so the
 // P V loop has no branches).
 // ONES: V carries a column of ones in a spare padded column (head dims with
 // d mod 16 in 1..8), so the P V products also yield the softmax row sums.
-template <int DP, int NJ, bool ONES>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
+template <bool PAGED, int DP, int NJ, bool ONES>
+__global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
+  constexpr int NT = kThreads;
+  constexpr int HT = NT / 2;  // threads that move K (the others move V)
+  constexpr int STG = kStage;
+  constexpr int KH = kParts;
+  constexpr int AH = kAhead;
   constexpr int KC = DP / 32;
   static_assert(NJ >= 1 && NJ <= DP / 16, "output tiles");
-  constexpr int KP = DP + 16;  // LDS row pitch in halves (keeps transposed reads conflict-free)
-  constexpr int VPT = (kStage * (DP / 8) + 255) / 256;  // 16-byte vectors per thread and stage
-  constexpr int BUF = kStage * KP;                      // halves per stage buffer
-  // stage buffers: K in [0, 3 BUF), V in [3 BUF, 6 BUF)
-  __shared__ __align__(16) uint16_t s_kv[2 * kBufs * BUF];
-  __shared__ int2 s_tab[kTabTokens];  // (position, K/V row byte offset) of stream tokens, a ring
-  __shared__ uint4 s_junk[256];
+  // LDS row pitch in halves, for K and V: V rows are read transposed, 8 rows
+  // by 4 lanes of 8 bytes, and a pitch of an odd multiple of 8 dwords spreads
+  // the 8 rows over all banks; the unit at column DP of a K row is never read
+  // (lanes without a vector store there)
+  constexpr int PK = DP + 16;
+  constexpr int PV = DP + 16;
+  constexpr int VOFF = 2 * STG * PK;  // V buffers after the two K buffers
+  constexpr int VPT = (STG * (DP / 8) + HT - 1) / HT;  // 16-byte vectors per thread and stage
+  constexpr int RF = kRefill;
+  static_assert(RF >= AH + 3, "a refilled stage is first read after the barrier that follows the refill");
+  constexpr int TABST = 2 * RF;     // stages in the token table ring
+  constexpr int TAB = TABST * STG;  // token table ring entries
+  constexpr int OC = 16 * NJ;                         // output columns in the merge
+  // stage buffers: K in [0, VOFF), V in [VOFF, VOFF + 2 STG PV); after the
+  // loop they hold the partial outputs of the merge
+  __shared__ __align__(16) uint16_t s_kv[VOFF + 2 * STG * PV];
+  static_assert((KH - 1) * 64 * OC * 4 <= (int)sizeof(s_kv), "merge area");
+  __shared__ int2 s_tab[TAB];  // (position, K/V row byte offset) of stream tokens, a ring
   __shared__ int4 s_items[kPrefItems];
   __shared__ int s_blk[kPrefItems];
   __shared__ int wave_tot[16];
   __shared__ int sh_tot[4];
-  __shared__ float s_ml[4][16][2];
+  __shared__ float s_ml[KH - 1][4][16][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -199,84 +216,98 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     const int len = tid < n_items ? s_items[tid].y : 0;
     const int inc = block_inclusive_scan(len, wave_tot);
     if (tid < n_items) s_items[tid].w = inc - len;
-    if (tid == 511) sh_tot[0] = inc;
+    if (tid == NT - 1) sh_tot[0] = inc;
   }
-  // pad columns of K and V (columns 8 nvec .. DP - 1, which the products
-  // read): zero, except V's column of ones.  Rows and pads are whole
-  // 16-byte units.
+  // pad columns that the products read (K: 8 nvec .. DP - 1, V: 8 nvec ..
+  // 16 NJ - 1): zero, except V's column of ones.  Whole 16-byte units.
   {
-    const int npad = DP / 8 - a.nvec;
-    for (int e = tid; e < 2 * kBufs * kStage * npad; e += 512) {
-      const int i = e / npad, c = e - i * npad;
-      const bool ones = ONES && i >= kBufs * kStage && c == 0;
-      *reinterpret_cast<uint4*>(s_kv + i * KP + 8 * (a.nvec + c)) = make_uint4(ones ? 0x3f80u : 0u, 0u, 0u, 0u);
+    const int kpad = DP / 8 - a.nvec, vpad = 2 * NJ - a.nvec;
+    for (int e = tid; e < 2 * STG * kpad; e += NT) {
+      const int i = e / kpad, c = e - i * kpad;
+      *reinterpret_cast<uint4*>(s_kv + i * PK + 8 * (a.nvec + c)) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int e = tid; e < 2 * STG * vpad; e += NT) {
+      const int i = e / vpad, c = e - i * vpad;
+      const bool ones = ONES && c == 0;
+      *reinterpret_cast<uint4*>(s_kv + VOFF + i * PV + 8 * (a.nvec + c)) =
+          make_uint4(ones ? 0x3f80u : 0u, 0u, 0u, 0u);
     }
   }
   __syncthreads();
   const int ns = n_items;
   const int n_tok = sh_tot[0];
-  const int n_stages = (n_tok + kStage - 1) / kStage;
+  const int n_stages = (n_tok + STG - 1) / STG;
 
   // token table: stream offset tau -> (position, byte offset of its K/V
   // row: position order in the memory, or through the page table), kNoPos
-  // past the end
+  // past the end; entry tau sits at tau mod TAB
   const int row_bytes = a.row_stride * 2;
-  const int32_t* ptab = a.pages ? a.pages + (int64_t)bg * a.pages_stride : nullptr;
-  // (count a multiple of 512: each thread fills a run of count / 512
-  // consecutive entries, with one search for the run's first segment)
+  const int32_t* ptab = PAGED ? a.pages + (int64_t)bg * a.pages_stride : nullptr;
+  // each thread fills a run of consecutive entries, with one search for the
+  // run's first segment
   auto fill = [&](int tau0, int count) {
-    const int per = count / 512, t0 = tau0 + tid * per;
-    int lo = 0, hi = ns - 1;  // last item with w <= t0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_items[mid].w <= t0) lo = mid; else hi = mid - 1;
-    }
-    int4 c = s_items[lo];
-    for (int j = 0; j < per; ++j) {
-      const int tau = t0 + j;
-      int2 e = make_int2(kNoPos, kOutOfRange);
-      if (tau < n_tok) {
-        while (tau >= c.w + c.y) c = s_items[++lo];  // segments are contiguous in the stream
-        const int pos = c.x + (tau - c.w);
-        int row = pos;
-        if (ptab) {
-          const int x = pos / a.B;
-          row = ptab[x] * a.B + (pos - x * a.B);
-        }
-        e = make_int2(pos, row * row_bytes);
+    const int per = (count + NT - 1) / NT;
+    const int first = tid * per;
+    if (first < count) {
+      const int t0 = tau0 + first;
+      int lo = 0, hi = ns - 1;  // last item with w <= t0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_items[mid].w <= t0) lo = mid; else hi = mid - 1;
       }
-      s_tab[tau & (kTabTokens - 1)] = e;
+      int4 c = s_items[lo];
+      const int cnt = min(per, count - first);
+      for (int j = 0; j < cnt; ++j) {
+        const int tau = t0 + j;
+        int2 e = make_int2(kNoPos, kOutOfRange);
+        if (tau < n_tok) {
+          while (tau >= c.w + c.y) c = s_items[++lo];  // segments are contiguous in the stream
+          const int pos = c.x + (tau - c.w);
+          int row = pos;
+          if (PAGED) {
+            const int x = pos / a.B;
+            row = ptab[x] * a.B + (pos - x * a.B);
+          }
+          e = make_int2(pos, row * row_bytes);
+        }
+        s_tab[tau % TAB] = e;
+      }
     }
   };
-  fill(0, kTabTokens);
+  fill(0, TAB);
 
-  // staging: waves 0-3 move K, waves 4-7 move V; thread t of the 256 moves
-  // vectors e = t + 256 j of the stage.  Buffer loads with one 32-bit offset
-  // per vector (rows past the end read zeros); kAhead stages of loads are in
-  // flight in a ring of registers.
-  const int kvec = kStage * a.nvec;
-  const bool stage_v = wave >= 4;
+  // staging: threads [0, HT) move K, [HT, NT) move V; thread t of its half
+  // moves vectors e = t + HT j of the stage.  Buffer loads with one 32-bit
+  // offset per vector (rows past the end read zeros); AH stages of loads
+  // are in flight in a ring of registers.  K is stored two stages ahead of
+  // the one whose softmax runs, V one stage ahead, so two buffers of each
+  // suffice.
+  const int kvec = STG * a.nvec;
+  const bool stage_v = wave >= 2 * KH;  // wave-uniform, so the buffer resource stays scalar
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((stage_v ? a.v : a.k) + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kBufferFlags);
-  const int t256 = tid & 255;
+  const int th = stage_v ? tid - HT : tid;
   // Per vector: its row's table entry within a stage (byte offset), its
-  // column in bytes, and its LDS slot.  A lane without a vector gets column
-  // kOutOfRange: row offset + kOutOfRange stays below 2^32 (a slice is under
-  // kOutOfRange - 4096 bytes) and past the buffer's end, so it reads zeros.
+  // column in bytes, and its LDS slot in buffer 0 (-1: none).  A lane without
+  // a vector gets column kOutOfRange: row offset + kOutOfRange stays below
+  // 2^32 (a slice is under kOutOfRange - 4096 bytes) and past the buffer's
+  // end, so it reads zeros, which it stores into the unread unit of a K row.
   uint32_t stab[VPT], scol[VPT];
   int soff[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int e = t256 + 256 * j;
+    const int e = th + HT * j;
     const int r = e / a.nvec, c = e - r * a.nvec;
-    stab[j] = (uint32_t)(r < kStage ? r : 0) * (uint32_t)sizeof(int2);
+    stab[j] = (uint32_t)(r < STG ? r : 0) * (uint32_t)sizeof(int2);
     scol[j] = e < kvec ? 16u * c : (uint32_t)kOutOfRange;
-    soff[j] = e < kvec ? (stage_v ? kBufs * BUF : 0) + r * KP + 8 * c : -1;
+    soff[j] = e < kvec ? (stage_v ? VOFF + r * PV : r * PK) + 8 * c : -1;
   }
-  uint4 stg[kAhead][VPT];
+  const int junk = (th % STG) * PK + DP;
+  const int bstride = stage_v ? STG * PV : STG * PK;
+  uint4 stg[AH][VPT];
   auto stage_offsets = [&](int(&at)[VPT], int stage) {
-    // a stage's 64 table entries never wrap around the ring
-    const char* tab = reinterpret_cast<const char*>(s_tab) + ((stage * kStage) & (kTabTokens - 1)) * sizeof(int2);
+    // a stage's entries never wrap around the ring
+    const char* tab = reinterpret_cast<const char*>(s_tab) + (stage % TABST) * STG * (int)sizeof(int2);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const uint32_t off = (uint32_t)reinterpret_cast<const int2*>(tab + stab[j])->y;
@@ -288,14 +319,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < VPT; ++j)
       dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at[j], 0, 0));
   };
-  // lanes without a vector store into a junk slot: no branch around the stores
   auto stage_store = [&](const uint4(&src)[VPT], int stage) {
-    const int base = (stage % kBufs) * BUF;
+    const int base = (stage & 1) * bstride;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      uint4* dst = soff[j] >= 0 ? reinterpret_cast<uint4*>(s_kv + base + soff[j]) : &s_junk[t256];
-      *dst = src[j];
-    }
+    for (int j = 0; j < VPT; ++j) *reinterpret_cast<uint4*>(s_kv + (soff[j] >= 0 ? base + soff[j] : junk)) = src[j];
   };
 
   // Rows past the last query compute unused values (rows never mix in
@@ -323,36 +350,42 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
 
   // S^T for this wave's rows of stage s
   auto qk = [&](f32x4_p(&st)[2], int s) {
-    const uint16_t* kbuf = s_kv + (s % kBufs) * BUF;
+    const uint16_t* kbuf = s_kv + (s & 1) * (STG * PK);
+    st[0] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+    st[1] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) {
-      st[sidx] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < KC; ++kk) {
+      const uint4 qv = qb[kk];
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(kbuf + (r0 + 16 * sidx + n) * KP + 32 * kk + 8 * g4);
-        st[sidx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_p(ka), as_bf16x8_p(qb[kk]), st[sidx], 0, 0, 0);
+      for (int sidx = 0; sidx < 2; ++sidx) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(kbuf + (r0 + 16 * sidx + n) * PK + 32 * kk + 8 * g4);
+        st[sidx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_p(ka), as_bf16x8_p(qv), st[sidx], 0, 0, 0);
       }
     }
   };
 
   // softmax of stage s from its S^T, then O += P V
   auto softmax_pv = [&](f32x4_p(&st)[2], int s) {  // st: masked in place
-    const uint16_t* vbuf = s_kv + kBufs * BUF + (s % kBufs) * BUF;
+    const uint16_t* vbuf = s_kv + VOFF + (s & 1) * (STG * PV);
+    // V of tile jj as the B operand of P V: lane (g4, n) holds column
+    // 16 jj + n of this wave's rows 4 g4 .. + 3 and 16 + 4 g4 .. + 3 (the
+    // token order of the S^T accumulator)
+    auto vtile = [&](int jj) {
+      const int col = 16 * jj + 4 * (n & 3);
+      const i16x4_p v0 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)(vbuf + (r0 + 4 * g4 + (n >> 2)) * PV + col));
+      const i16x4_p v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_p*)(vbuf + (r0 + 16 + 4 * g4 + (n >> 2)) * PV + col));
+      return __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // all V tiles are requested before the softmax, whose VALU work hides
+    // their latency
     bf16x8_p vb[NJ];
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      {
-        const int col = 16 * jj + 4 * (n & 3);
-        const i16x4_p v0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)(vbuf + (r0 + 4 * g4 + (n >> 2)) * KP + col));
-        const i16x4_p v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_p*)(vbuf + (r0 + 16 + 4 * g4 + (n >> 2)) * KP + col));
-        vb[jj] = __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
-    const int tbase = s * kStage + r0;
-    // whole: the stream is in position order, so its last token bounds the half
-    const bool whole = s_tab[(tbase + 31) & (kTabTokens - 1)].x <= plim_min;
+    for (int jj = 0; jj < NJ; ++jj) vb[jj] = vtile(jj);
+    const int2* tabs = s_tab + (s % TABST) * STG + r0;
+    // whole: the stream is in position order, so its last token bounds the part
+    const bool whole = tabs[31].x <= plim_min;
     // logits of tokens past a row's causal limit become -inf, so their
     // weights come out as zero
     // (in place, so both branches leave the logits in the same registers)
@@ -361,7 +394,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
       for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int pos = s_tab[(tbase + 16 * sidx + 4 * g4 + i) & (kTabTokens - 1)].x;
+          const int pos = tabs[16 * sidx + 4 * g4 + i].x;
           st[sidx][i] = pos <= plim ? st[sidx][i] : -INFINITY;
         }
     }
@@ -404,51 +437,57 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     const bf16x8_p pa_hi = __builtin_bit_cast(bf16x8_p, make_uint4(ph[0], ph[1], ph[2], ph[3]));
     const bf16x8_p pa_lo = __builtin_bit_cast(bf16x8_p, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
+    for (int jj = 0; jj < NJ; ++jj) {
       o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[jj], o[jj], 0, 0, 0);
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
       o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[jj], o[jj], 0, 0, 0);
+    }
   };
 
-  // Pipeline over stages, three LDS buffers: in iteration s the wave
-  // multiplies S^T of stage s+1 while it finishes the softmax and P V of
-  // stage s; stage s+2 moves from registers to LDS and stage s+2+kAhead is
-  // requested into the registers it frees (stages s+3 .. s+1+kAhead are in
-  // flight).  Loads, stores and barriers run unconditionally (past the end
-  // the loads read zeros) so the memory waits stay one ring slot deep.
+  // Pipeline over stages, two LDS buffers for K and two for V: in iteration
+  // s the wave multiplies S^T of stage s+1 while it finishes the softmax and
+  // P V of stage s; K of stage s+2 and V of stage s+1 move from registers to
+  // LDS, and the loads of K s+2+AH and V s+1+AH go into the registers they
+  // free.
+  // Loads, stores and barriers run unconditionally (past the end the loads
+  // read zeros) so the memory waits stay one ring slot deep.
   if (n_stages > 0) {
-    __syncthreads();  // token table
+    __syncthreads();  // token table, pads
     int at[VPT];
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j) {
-      stage_offsets(at, j);
-      stage_load(stg[j], at);
+    // K stages 0 and 1 (V stage 0) go to LDS, the next AH stages into the ring
+    const int lag = stage_v ? 1 : 2;
+    for (int t = 0; t < lag; ++t) {
+      stage_offsets(at, t);
+      stage_load(stg[0], at);
+      stage_store(stg[0], t);
     }
-    stage_store(stg[0], 0);
-    stage_offsets(at, kAhead);
-    stage_load(stg[0], at);
-    stage_store(stg[1], 1);
-    stage_offsets(at, kAhead + 1);
-    stage_load(stg[1], at);
+    // ring slot of stage t: (t + 2 - lag) mod AH, the same slot for the K and
+    // the V stage that an iteration stores (no branch between the movers)
+#pragma unroll
+    for (int i = 0; i < AH; ++i) {
+      stage_offsets(at, lag + i);
+      stage_load(stg[(i + 2) % AH], at);
+    }
     __syncthreads();
-    // S^T tiles of even stages in st_a, odd ones in st_b (kAhead is even)
-    static_assert(kAhead % 2 == 0, "stage parity");
+    // S^T tiles of even stages in st_a, odd ones in st_b
     f32x4_p st_a[2], st_b[2];
     qk(st_a, 0);
-    for (int s0 = 0; s0 < n_stages; s0 += kAhead) {
+    __syncthreads();  // K buffer 0 takes stage 2 in the first iteration
+    // unrolled over U stages: the S^T pair and the ring slots repeat with it
+    constexpr int U = AH > 2 ? AH : 2;
+    for (int s0 = 0; s0 < n_stages; s0 += U) {
 #pragma unroll
-      for (int j = 0; j < kAhead; ++j) {
+      for (int j = 0; j < U; ++j) {
         const int s = s0 + j;
         f32x4_p(&st_cur)[2] = (j % 2 == 0) ? st_a : st_b;
         f32x4_p(&st_nxt)[2] = (j % 2 == 0) ? st_b : st_a;
-        // refill the token table half a ring ahead (entries of finished stages)
-        if (s % kRefill == 0 && s >= kRefill) fill((s + kRefill) * kStage, kRefill * kStage);
-        stage_offsets(at, s + 2 + kAhead);
+        // refill the table half a ring ahead (entries of finished stages)
+        if (s % RF == 0 && s >= RF) fill((s + RF) * STG, RF * STG);
         if (s + 1 < n_stages) qk(st_nxt, s + 1);
         if (s < n_stages) softmax_pv(st_cur, s);
-        stage_store(stg[(j + 2) % kAhead], s + 2);
-        stage_load(stg[(j + 2) % kAhead], at);
+        // (s0 is a multiple of AH)
+        stage_offsets(at, s + lag + AH);
+        stage_store(stg[(j + 2) % AH], s + lag);
+        stage_load(stg[(j + 2) % AH], at);
         __syncthreads();
       }
     }
@@ -473,39 +512,55 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(PrefillArgs a) {
     lpart = xsum16_32(lpart);
   }
 
-  // merge the two token halves: waves 4-7 hand (max, sum, O) to waves 0-3 through LDS
+  // merge the KH token parts: waves of parts 1.. hand (max, sum, O) to the
+  // waves of part 0 through LDS
   __syncthreads();
-  float* s_o = reinterpret_cast<float*>(s_kv);  // [4][16][DP] floats
-  if (kh == 1) {
+  float* s_o = reinterpret_cast<float*>(s_kv);  // [KH - 1][4][16][OC] floats
+  if (kh > 0) {
     if (lane < 16) {
-      s_ml[qg][lane][0] = mref;
-      s_ml[qg][lane][1] = lpart;
+      s_ml[kh - 1][qg][lane][0] = mref;
+      s_ml[kh - 1][qg][lane][1] = lpart;
     }
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[(qg * 16 + 4 * g4 + i) * DP + 16 * jj + n] = o[jj][i];
+      for (int i = 0; i < 4; ++i) s_o[(((kh - 1) * 4 + qg) * 16 + 4 * g4 + i) * OC + 16 * jj + n] = o[jj][i];
   }
   __syncthreads();
   if (kh == 0) {
-    const float m2 = s_ml[qg][n][0], l2 = s_ml[qg][n][1];
-    const float M = fmaxf(mref, m2);
-    const float f1 = exp2_fast(mref - M), f2 = exp2_fast(m2 - M);
-    const float L = lpart * f1 + l2 * f2;
+    float M = mref;
+#pragma unroll
+    for (int p = 0; p < KH - 1; ++p) M = fmaxf(M, s_ml[p][qg][n][0]);
+    float f[KH];
+    f[0] = exp2_fast(mref - M);
+    float L = lpart * f[0];
+#pragma unroll
+    for (int p = 0; p < KH - 1; ++p) {
+      f[p + 1] = exp2_fast(s_ml[p][qg][n][0] - M);
+      L += s_ml[p][qg][n][1] * f[p + 1];
+    }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     if (a.lse && g4 == 0 && q0 + 16 * qg + n < a.n_q)
       a.lse[(int64_t)bh * a.n_q + q0 + 16 * qg + n] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
-    const float c1 = f1 * inv, c2 = f2 * inv;
+#pragma unroll
+    for (int p = 0; p < KH; ++p) f[p] *= inv;
     float* orow = a.out + ((int64_t)bh * a.n_q + q0 + 16 * qg) * a.d;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g4 + i;
-      const float a1 = __shfl(c1, r), a2 = __shfl(c2, r);
+      float c[KH];
+#pragma unroll
+      for (int p = 0; p < KH; ++p) c[p] = __shfl(f[p], r);
       if (q0 + 16 * qg + r < a.n_q) {
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
           const int col = 16 * jj + n;
-          if (col < a.d) orow[(int64_t)r * a.d + col] = o[jj][i] * a1 + s_o[(qg * 16 + r) * DP + col] * a2;
+          if (col < a.d) {
+            float acc = o[jj][i] * c[0];
+#pragma unroll
+            for (int p = 0; p < KH - 1; ++p) acc += s_o[((p * 4 + qg) * 16 + r) * OC + col] * c[p + 1];
+            orow[(int64_t)r * a.d + col] = acc;
+          }
         }
       }
     }
@@ -552,35 +607,32 @@ hipError_t launch_attn_prefill(const AttnGeom& g, const void* k, const void* v, 
   a.win_start = g.win_start;
   a.pages = g.pages;
   a.pages_stride = g.pages_stride;
-  const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(512);
+  const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(kThreads);
   const bool ones = 8 * a.nvec < 16 * a.nj;  // a spare padded column exists
-#define BRS_PREFILL_LAUNCH(DP, NJ, ONES)                                                      \
-  if (a.nj == NJ && ones == ONES) {                                                          \
+  const bool paged = a.pages != nullptr;
+#define BRS_PREFILL_LAUNCH(PAGED, DP, NJ, ONES)                                                 \
+  if (paged == PAGED && a.nj == NJ && ones == ONES) {                                         \
     if (ev0)                                                                                  \
-      hipExtLaunchKernelGGL((attn_prefill_kernel<DP, NJ, ONES>), grid, block, 0, s, ev0, ev1, 0, a); \
+      hipExtLaunchKernelGGL((attn_prefill_kernel<PAGED, DP, NJ, ONES>), grid, block, 0, s, ev0, ev1, 0, a); \
     else                                                                                      \
-      hipLaunchKernelGGL((attn_prefill_kernel<DP, NJ, ONES>), grid, block, 0, s, a);          \
+      hipLaunchKernelGGL((attn_prefill_kernel<PAGED, DP, NJ, ONES>), grid, block, 0, s, a);   \
     return hipGetLastError();                                                                 \
   }
-  if (g.d <= 64) {
-    BRS_PREFILL_LAUNCH(64, 1, true)
-    BRS_PREFILL_LAUNCH(64, 1, false)
-    BRS_PREFILL_LAUNCH(64, 2, true)
-    BRS_PREFILL_LAUNCH(64, 2, false)
-    BRS_PREFILL_LAUNCH(64, 3, true)
-    BRS_PREFILL_LAUNCH(64, 3, false)
-    BRS_PREFILL_LAUNCH(64, 4, true)
-    BRS_PREFILL_LAUNCH(64, 4, false)
-  } else {
-    BRS_PREFILL_LAUNCH(128, 5, true)
-    BRS_PREFILL_LAUNCH(128, 5, false)
-    BRS_PREFILL_LAUNCH(128, 6, true)
-    BRS_PREFILL_LAUNCH(128, 6, false)
-    BRS_PREFILL_LAUNCH(128, 7, true)
-    BRS_PREFILL_LAUNCH(128, 7, false)
-    BRS_PREFILL_LAUNCH(128, 8, true)
-    BRS_PREFILL_LAUNCH(128, 8, false)
+#define BRS_PREFILL_ALL(P)                                                                    \
+  if (g.d <= 64) {                                                                            \
+    BRS_PREFILL_LAUNCH(P, 64, 1, true) BRS_PREFILL_LAUNCH(P, 64, 1, false)                    \
+    BRS_PREFILL_LAUNCH(P, 64, 2, true) BRS_PREFILL_LAUNCH(P, 64, 2, false)                    \
+    BRS_PREFILL_LAUNCH(P, 64, 3, true) BRS_PREFILL_LAUNCH(P, 64, 3, false)                    \
+    BRS_PREFILL_LAUNCH(P, 64, 4, true) BRS_PREFILL_LAUNCH(P, 64, 4, false)                    \
+  } else {                                                                                    \
+    BRS_PREFILL_LAUNCH(P, 128, 5, true) BRS_PREFILL_LAUNCH(P, 128, 5, false)                  \
+    BRS_PREFILL_LAUNCH(P, 128, 6, true) BRS_PREFILL_LAUNCH(P, 128, 6, false)                  \
+    BRS_PREFILL_LAUNCH(P, 128, 7, true) BRS_PREFILL_LAUNCH(P, 128, 7, false)                  \
+    BRS_PREFILL_LAUNCH(P, 128, 8, true) BRS_PREFILL_LAUNCH(P, 128, 8, false)                  \
   }
+  BRS_PREFILL_ALL(true)
+  BRS_PREFILL_ALL(false)
+#undef BRS_PREFILL_ALL
 #undef BRS_PREFILL_LAUNCH
   return hipErrorInvalidValue;
 }
