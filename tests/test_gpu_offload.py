@@ -125,6 +125,10 @@ CHUNK_CASES = {
                                                       window=200, sinks=16, k=5, n_q=100, planted_per_head=0),
     # MemLong chunked prefill: cosine scores, one list per sequence, head dim 100 in rows of 104
     "prefill_cosine": W["memlong_chunk_prefill_80k"].scaled(n_q_heads=4, n_kv_heads=4, n_tokens=8 * 512 + 512),
+    # head dim 64 (the kernel's 64-column contraction), two sequences, a short window
+    "prefill_d64": W["retrievalattn_gqa_decode_1m_b8"].scaled(
+        batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, rep_dim=64, n_tokens=4000 + 9, block=32, k=7, window=60,
+        sinks=8, n_q=70, planted_per_head=0),
     # several queries on the slot kernels
     "decode_multi_q": W["infllm_gqa_decode_128k"].scaled(n_q_heads=8, n_kv_heads=2, n_tokens=6000, window=300, k=5,
                                                          n_q=3, planted_per_head=0),
@@ -132,6 +136,7 @@ CHUNK_CASES = {
 
 
 @pytest.mark.parametrize("name,select", [(n, "head") for n in CHUNK_CASES] + [("prefill_dot", "group"),
+                                                                             ("prefill_d64", "group"),
                                                                              ("decode_multi_q", "group")])
 def test_offload_chunk_matches_resident(name, select):
     """A step of n_q > 1 queries (InfLLM "method": the memory units stay in
