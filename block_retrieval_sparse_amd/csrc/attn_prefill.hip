@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  fill(0, TAB);
+  fill(0, RF * STG);  // the rest after the first loads are issued
 
   // staging: threads [0, HT) move K, [HT, NT) move V; thread t of its half
   // moves vectors e = t + HT j of the stage.  Buffer loads with one 32-bit
@@ -453,20 +453,36 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
   if (n_stages > 0) {
     __syncthreads();  // token table, pads
     int at[VPT];
-    // K stages 0 and 1 (V stage 0) go to LDS, the next AH stages into the ring
+    // Ring slot of stage t: (t + 2 - lag) mod AH, the same slot for the K and
+    // the V stage that an iteration stores (no branch between the movers in
+    // the loop).  Stages 0 .. AH-1 are requested together; K stages 0 and 1
+    // (V stage 0) then go to LDS, each slot refilled with the stage AH later.
+    static_assert(AH >= 2, "K stages 0 and 1 take two ring slots");
     const int lag = stage_v ? 1 : 2;
-    for (int t = 0; t < lag; ++t) {
-      stage_offsets(at, t);
-      stage_load(stg[0], at);
-      stage_store(stg[0], t);
-    }
-    // ring slot of stage t: (t + 2 - lag) mod AH, the same slot for the K and
-    // the V stage that an iteration stores (no branch between the movers)
+    if (stage_v) {
 #pragma unroll
-    for (int i = 0; i < AH; ++i) {
-      stage_offsets(at, lag + i);
-      stage_load(stg[(i + 2) % AH], at);
+      for (int t = 0; t < AH; ++t) {
+        stage_offsets(at, t);
+        stage_load(stg[(t + 1) % AH], at);
+      }
+      stage_store(stg[1 % AH], 0);
+      stage_offsets(at, AH);
+      stage_load(stg[1 % AH], at);
+    } else {
+#pragma unroll
+      for (int t = 0; t < AH; ++t) {
+        stage_offsets(at, t);
+        stage_load(stg[t], at);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        stage_store(stg[t], t);
+        stage_offsets(at, t + AH);
+        stage_load(stg[t], at);
+      }
     }
+    // the table's second half, behind the loads in flight
+    fill(RF * STG, RF * STG);
     __syncthreads();
     // S^T tiles of even stages in st_a, odd ones in st_b
     f32x4_p st_a[2], st_b[2];
