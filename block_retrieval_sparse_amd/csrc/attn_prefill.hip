@@ -119,9 +119,9 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
   static_assert((KH - 1) * 64 * OC * 4 <= (int)sizeof(s_kv), "merge area");
   __shared__ int2 s_tab[TAB];  // (position, K/V row byte offset) of stream tokens, a ring
   __shared__ int4 s_items[kPrefItems];
-  __shared__ int s_blk[kPrefItems];
-  __shared__ int wave_tot[16];
-  __shared__ int sh_tot[4];
+  __shared__ int s_blk[kPrefItems];   // valid selection entries (-1: none)
+  __shared__ int s_keep[kPrefItems];  // the same without repeats
+  __shared__ int sh_tot[2];           // stream tokens, items
   __shared__ float s_ml[KH - 1][4][16][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -180,43 +180,17 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
     for (int kk = 0; kk < KC; ++kk) qb[kk] = make_uint4(w[kk][0], w[kk][1], w[kk][2], w[kk][3]);
   }
 
+  // Three barriers: the entries, the kept entries, the items.  Every kept
+  // block finds its rank in block order, its stream offset and (thread 0)
+  // the totals by one pass over the kept entries, with no block-wide scan.
   const int S = a.sink_end;
+  const int s_len = min(S, pmax + 1);  // the sinks, clipped to the causal limit
+  auto seg_lo = [&](int x) { return max(x * a.B, S); };
+  auto seg_len = [&](int x) { return max(min(min((x + 1) * a.B, a.win_start), pmax + 1) - seg_lo(x), 0); };
   if (tid < kPrefItems) {
     const bool valid = tid < a.kk && blk >= 0 && blk < a.nb &&
                        max(blk * a.B, S) < min((blk + 1) * a.B, a.win_start);
     s_blk[tid] = valid ? blk : -1;
-  }
-  __syncthreads();
-  bool dup = false;  // an earlier entry holds the same block
-  if (tid < a.kk && s_blk[tid] >= 0)
-    for (int j = 0; j < tid; ++j) dup |= s_blk[j] == s_blk[tid];
-  __syncthreads();
-  if (dup) s_blk[tid] = -1;
-  __syncthreads();
-  const int mine = tid < a.kk ? s_blk[tid] : -1;
-  int rank = 0;  // kept blocks below this one
-  if (mine >= 0)
-    for (int j = 0; j < a.kk; ++j) {
-      const int o = s_blk[j];
-      rank += o >= 0 && o < mine;
-    }
-  const int n_kept = __syncthreads_count(mine >= 0);
-  const int hs = S > 0 ? 1 : 0;
-  const int n_items = hs + n_kept + 1;
-  if (mine >= 0) {
-    const int lo_t = max(mine * a.B, S);
-    const int hi_t = min(min((mine + 1) * a.B, a.win_start), pmax + 1);
-    s_items[hs + rank] = make_int4(lo_t, max(hi_t - lo_t, 0), 0, 0);
-  }
-  if (tid == 0 && hs) s_items[0] = make_int4(0, min(S, pmax + 1), 0, 0);
-  if (tid == 0) s_items[hs + n_kept] = make_int4(a.win_start, max(min(a.N, pmax + 1) - a.win_start, 0), 0, 0);
-  __syncthreads();
-  // stream offsets (segments past pmax have length 0; they come last)
-  {
-    const int len = tid < n_items ? s_items[tid].y : 0;
-    const int inc = block_inclusive_scan(len, wave_tot);
-    if (tid < n_items) s_items[tid].w = inc - len;
-    if (tid == NT - 1) sh_tot[0] = inc;
   }
   // pad columns that the products read (K: 8 nvec .. DP - 1, V: 8 nvec ..
   // 16 NJ - 1): zero, except V's column of ones.  Whole 16-byte units.
@@ -234,7 +208,45 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  const int ns = n_items;
+  // an entry is kept unless an earlier entry holds the same block
+  if (tid < kPrefItems) {
+    const int x = tid < a.kk ? s_blk[tid] : -1;
+    bool dup = false;
+    if (x >= 0)
+      for (int j = 0; j < tid; ++j) dup |= s_blk[j] == x;
+    s_keep[tid] = dup ? -1 : x;
+  }
+  __syncthreads();
+  {
+    const int mine = tid < a.kk ? s_keep[tid] : -1;
+    if (mine >= 0 || tid == 0) {
+      int rank = 0, before = 0, n_kept = 0, kept_tok = 0;  // kept blocks below mine and their tokens; totals
+      for (int j = 0; j < a.kk; ++j) {
+        const int o = s_keep[j];
+        if (o >= 0) {
+          const int len = seg_len(o);
+          ++n_kept;
+          kept_tok += len;
+          if (o < mine) {
+            ++rank;
+            before += len;
+          }
+        }
+      }
+      const int hs = S > 0 ? 1 : 0;
+      // segments past pmax have length 0; they come last among the blocks
+      if (mine >= 0) s_items[hs + rank] = make_int4(seg_lo(mine), seg_len(mine), 0, s_len + before);
+      if (tid == 0) {
+        if (hs) s_items[0] = make_int4(0, s_len, 0, 0);
+        const int win_len = max(min(a.N, pmax + 1) - a.win_start, 0);
+        s_items[hs + n_kept] = make_int4(a.win_start, win_len, 0, s_len + kept_tok);
+        sh_tot[0] = s_len + kept_tok + win_len;
+        sh_tot[1] = hs + n_kept + 1;
+      }
+    }
+  }
+  __syncthreads();
+  const int ns = sh_tot[1];  // items
   const int n_tok = sh_tot[0];
   const int n_stages = (n_tok + STG - 1) / STG;
 
