@@ -116,13 +116,14 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
   // stage buffers: K in [0, VOFF), V in [VOFF, VOFF + 2 STG PV); after the
   // loop they hold the partial outputs of the merge
   __shared__ __align__(16) uint16_t s_kv[VOFF + 2 * STG * PV];
-  static_assert((KH - 1) * 64 * OC * 4 <= (int)sizeof(s_kv), "merge area");
+  static_assert(KH * 64 * OC * 4 <= (int)sizeof(s_kv), "merge area");
   __shared__ int2 s_tab[TAB];  // (position, K/V row byte offset) of stream tokens, a ring
   __shared__ int4 s_items[kPrefItems];
   __shared__ int s_blk[kPrefItems];   // valid selection entries (-1: none)
   __shared__ int s_keep[kPrefItems];  // the same without repeats
   __shared__ int sh_tot[2];           // stream tokens, items
-  __shared__ float s_ml[KH - 1][4][16][2];
+  __shared__ float s_ml[KH][64][2];  // per part and row: (max, sum)
+  __shared__ float s_f[KH][64];      // per part and row: merge factor over the sum
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -540,57 +541,58 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
     lpart = xsum16_32(lpart);
   }
 
-  // merge the KH token parts: waves of parts 1.. hand (max, sum, O) to the
-  // waves of part 0 through LDS
+  // merge the KH token parts: every wave hands (max, sum) of its rows and its
+  // O tile to LDS; one thread per row finds the row's factors; then all
+  // threads combine the parts two columns at a time and write the output
+  // rows in order (consecutive threads, consecutive columns)
   __syncthreads();
-  float* s_o = reinterpret_cast<float*>(s_kv);  // [KH - 1][4][16][OC] floats
-  if (kh > 0) {
-    if (lane < 16) {
-      s_ml[kh - 1][qg][lane][0] = mref;
-      s_ml[kh - 1][qg][lane][1] = lpart;
-    }
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[(((kh - 1) * 4 + qg) * 16 + 4 * g4 + i) * OC + 16 * jj + n] = o[jj][i];
+  float* s_o = reinterpret_cast<float*>(s_kv);  // [KH][64][OC] floats
+  if (lane < 16) {
+    s_ml[kh][16 * qg + lane][0] = mref;
+    s_ml[kh][16 * qg + lane][1] = lpart;
   }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[(kh * 64 + 16 * qg + 4 * g4 + i) * OC + 16 * jj + n] = o[jj][i];
   __syncthreads();
-  if (kh == 0) {
-    float M = mref;
+  const int rows = min(kPrefQ, a.n_q - q0);
+  if (tid < rows) {
+    float M = s_ml[0][tid][0];
 #pragma unroll
-    for (int p = 0; p < KH - 1; ++p) M = fmaxf(M, s_ml[p][qg][n][0]);
-    float f[KH];
-    f[0] = exp2_fast(mref - M);
-    float L = lpart * f[0];
+    for (int p = 1; p < KH; ++p) M = fmaxf(M, s_ml[p][tid][0]);
+    float f[KH], L = 0.f;
 #pragma unroll
-    for (int p = 0; p < KH - 1; ++p) {
-      f[p + 1] = exp2_fast(s_ml[p][qg][n][0] - M);
-      L += s_ml[p][qg][n][1] * f[p + 1];
+    for (int p = 0; p < KH; ++p) {
+      f[p] = exp2_fast(s_ml[p][tid][0] - M);
+      L += s_ml[p][tid][1] * f[p];
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    if (a.lse && g4 == 0 && q0 + 16 * qg + n < a.n_q)
-      a.lse[(int64_t)bh * a.n_q + q0 + 16 * qg + n] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+    if (a.lse) a.lse[(int64_t)bh * a.n_q + q0 + tid] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 #pragma unroll
-    for (int p = 0; p < KH; ++p) f[p] *= inv;
-    float* orow = a.out + ((int64_t)bh * a.n_q + q0 + 16 * qg) * a.d;
+    for (int p = 0; p < KH; ++p) s_f[p][tid] = f[p] * inv;
+  }
+  __syncthreads();
+  // element e = (row r, column pair c2) of the rows x d/2 float2 units (d is even)
+  const int h2 = a.d >> 1;
+  const int dr = NT / h2, dc = NT - dr * h2;
+  int r = tid / h2, c2 = tid - r * h2;
+  float* obase = a.out + ((int64_t)bh * a.n_q + q0) * a.d;
+  for (int e = tid; e < rows * h2; e += NT) {
+    float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      float c[KH];
-#pragma unroll
-      for (int p = 0; p < KH; ++p) c[p] = __shfl(f[p], r);
-      if (q0 + 16 * qg + r < a.n_q) {
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int col = 16 * jj + n;
-          if (col < a.d) {
-            float acc = o[jj][i] * c[0];
-#pragma unroll
-            for (int p = 0; p < KH - 1; ++p) acc += s_o[((p * 4 + qg) * 16 + r) * OC + col] * c[p + 1];
-            orow[(int64_t)r * a.d + col] = acc;
-          }
-        }
-      }
+    for (int p = 0; p < KH; ++p) {
+      const float f = s_f[p][r];
+      const float2 v = *reinterpret_cast<const float2*>(s_o + (p * 64 + r) * OC + 2 * c2);
+      acc.x += v.x * f;
+      acc.y += v.y * f;
+    }
+    *reinterpret_cast<float2*>(obase + (int64_t)r * a.d + 2 * c2) = acc;
+    c2 += dc;
+    r += dr;
+    if (c2 >= h2) {
+      c2 -= h2;
+      ++r;
     }
   }
 }
