@@ -692,6 +692,49 @@ def check_prune_equal_hits_and_tail():
     assert plan2[5] == 0 and plan2[first] == -1 and (plan2[first + 1:] >= 0).all()
 
 
+def check_step_bruteforce():
+    """One whole step on tiny inputs against pure-Python loops: the candidate
+    blocks from their definition (complete, with a token outside the sinks and
+    the window), each block's score as the largest dot with its representatives,
+    its rank as a count of better candidates, and each query's output as a
+    softmax written out over the union of sinks, window and chosen blocks that
+    lies at or before the query's position (InfLLM "method"; Landmark Attention
+    "proposed method")."""
+    rng = np.random.default_rng(41)
+    Hq, Hkv, N, B, R, d, n = 2, 1, 53, 5, 2, 4, 3
+    for S, W, k in ((3, 7, 3), (6, 0, 2), (0, 11, 4), (2, 4, 20)):
+        q = rng.standard_normal((1, Hq, n, d))
+        K = rng.standard_normal((1, Hkv, N, d))
+        V = rng.standard_normal((1, Hkv, N, d))
+        reps = rng.standard_normal((1, Hkv, N // B, R, d))
+        scale = 0.7
+        res = O.step(q, K, V, reps, block=B, k=k, sinks=S, window=W, mode="given", scale=scale)
+        cand = [b for b in range(N // B) if (b + 1) * B <= N
+                and any(S <= t < N - W for t in range(b * B, (b + 1) * B))]
+        for h in range(Hq):
+            score = {}
+            for b in cand:
+                score[b] = np.float32(max(math.fsum(float(q[0, h, -1, i]) * float(reps[0, 0, b, r, i])
+                                                     for i in range(d)) for r in range(R)))
+            rank = {b: sum(1 for c in cand if score[c] > score[b] or (score[c] == score[b] and c < b))
+                    for b in cand}
+            chosen = sorted((b for b in cand if rank[b] < k), key=lambda b: rank[b])
+            idx = res["idx"][(0, h)]
+            assert [int(x) for x in idx if x >= 0] == chosen
+            assert (idx[len(chosen):] == -1).all() and len(idx) == k
+            T = set(range(min(S, N))) | set(range(max(N - W, 0), N))
+            for b in chosen:
+                T |= set(range(b * B, (b + 1) * B))
+            for j in range(n):
+                vis = sorted(t for t in T if t <= N - n + j)
+                z = [scale * math.fsum(float(q[0, h, j, i]) * float(K[0, 0, t, i]) for i in range(d)) for t in vis]
+                e = [math.exp(x) for x in z]
+                den = math.fsum(e)
+                for c in range(d):
+                    want = math.fsum(e[m] * float(V[0, 0, t, c]) for m, t in enumerate(vis)) / den
+                    assert abs(res["out"][(0, h)][j, c] - want) <= 1e-12
+
+
 CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_eligible_workloads,
           check_mean_exact, check_topnorm_bruteforce, check_dot_exact_mips, check_cosine,
           check_cosine_exact_rounding, check_group_max,
@@ -701,7 +744,7 @@ CHECKS = [check_round_f32, check_round_bf16, check_eligible_bruteforce, check_el
           check_planted_recall, check_hand_worked_fixture, check_step_cosine_chunks,
           check_weights_and_lse_library, check_window_mass_zero_query, check_window_mass_conservation_and_range,
           check_reps_attnscore_bruteforce, check_count_hits_bincount, check_prune_characterisation,
-          check_prune_equal_hits_and_tail]
+          check_prune_equal_hits_and_tail, check_step_bruteforce]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -1011,7 +1054,57 @@ def _orig_prune(n_tokens, B, capacity, hits, key=None):
             j += 1
     return new
 
+_orig_step = O.step
+_orig_compact = O.compact
+
+
+def _mut_step_window_short(q, K, V, reps, **kw):
+    return _orig_step(q, K, V, reps, **{**kw, "window": max(kw["window"] - 1, 0)})
+
+
+def _mut_step_no_sinks(q, K, V, reps, **kw):
+    return _orig_step(q, K, V, reps, **{**kw, "sinks": 0})
+
+
+def _mut_step_k_short(q, K, V, reps, **kw):
+    return _orig_step(q, K, V, reps, **{**kw, "k": max(kw["k"] - 1, 1)})
+
+
+def _mut_step_unscaled(q, K, V, reps, **kw):
+    return _orig_step(q, K, V, reps, **{**kw, "scale": 1.0})
+
+
+def _mut_step_group_as_head(q, K, V, reps, **kw):
+    return _orig_step(q, K, V, reps, **{**kw, "select": "head"})
+
+
+def _mut_compact_no_tail(K, plan, B, n_tokens):
+    return _orig_compact(K, plan, B, (n_tokens // B) * B)
+
+
+def _mut_compact_reversed(K, plan, B, n_tokens):
+    nb = n_tokens // B
+    rows = [K[b * B:(b + 1) * B] for b in reversed(range(nb)) if plan[b] >= 0]
+    rows.append(K[nb * B:n_tokens])
+    return np.concatenate(rows, axis=0)
+
+
+def _mut_compact_drops_first_kept(K, plan, B, n_tokens):
+    nb = n_tokens // B
+    rows = [K[b * B:(b + 1) * B] for b in range(nb) if plan[b] > 0]
+    rows.append(K[nb * B:n_tokens])
+    return np.concatenate(rows, axis=0)
+
+
 MUTANTS = [
+    ("step", _mut_step_window_short),
+    ("step", _mut_step_no_sinks),
+    ("step", _mut_step_k_short),
+    ("step", _mut_step_unscaled),
+    ("step", _mut_step_group_as_head),
+    ("compact", _mut_compact_no_tail),
+    ("compact", _mut_compact_reversed),
+    ("compact", _mut_compact_drops_first_kept),
     ("round_to_dtype", _mut_round_trunc),
     ("round_to_dtype", _mut_round_half_up),
     ("eligible_range", _mut_elig_floor),
