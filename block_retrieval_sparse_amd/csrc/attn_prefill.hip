@@ -150,12 +150,22 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
   // selection row is requested before the query rows so that the two loads
   // overlap (the memory counter waits in issue order).
   int blk;
+  // every wave also reads the whole row (contiguous layout), to find the
+  // stream's first segment without waiting for the workgroup
+  int erow[kPrefItems / 64];
   {
     // this head's list: its own, its kv head's, or its sequence's
     const int row = (int)sel_row(a.idx_heads, a.hkv, b, g, sel_lists(a.idx_heads, a.hkv) == a.G ? h - g * a.G : 0);
     const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.idx + (int64_t)row * a.kk), (short)0, a.kk * 4, kBufferFlags);
     blk = (int)__builtin_amdgcn_raw_buffer_load_b32(irs, tid < a.kk ? tid * 4 : kOutOfRange, 0, 0);
+    if constexpr (!PAGED) {
+#pragma unroll
+      for (int j = 0; j < kPrefItems / 64; ++j) {
+        const int e = lane + 64 * j;
+        erow[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(irs, e < a.kk ? e * 4 : kOutOfRange, 0, 0);
+      }
+    }
   }
 
   // query rows of this wave as the B operand of S^T = K Q^T: lane (g4, n)
@@ -181,13 +191,110 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
     for (int kk = 0; kk < KC; ++kk) qb[kk] = make_uint4(w[kk][0], w[kk][1], w[kk][2], w[kk][3]);
   }
 
+  const int S = a.sink_end;
+  const int s_len = min(S, pmax + 1);  // the sinks, clipped to the causal limit
+  const int row_bytes = a.row_stride * 2;
+  auto seg_lo = [&](int x) { return max(x * a.B, S); };
+  auto seg_len = [&](int x) { return max(min(min((x + 1) * a.B, a.win_start), pmax + 1) - seg_lo(x), 0); };
+  // staging: threads [0, HT) move K, [HT, NT) move V; thread t of its half
+  // moves vectors e = t + HT j of the stage.  Buffer loads with one 32-bit
+  // offset per vector (rows past the end read zeros); AH stages of loads
+  // are in flight in a ring of registers.  K is stored two stages ahead of
+  // the one whose softmax runs, V one stage ahead, so two buffers of each
+  // suffice.
+  const int kvec = STG * a.nvec;
+  const bool stage_v = wave >= 2 * KH;  // wave-uniform, so the buffer resource stays scalar
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((stage_v ? a.v : a.k) + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kBufferFlags);
+  const int th = stage_v ? tid - HT : tid;
+  // Per vector: its row's table entry within a stage (byte offset), its
+  // column in bytes, and its LDS slot in buffer 0 (-1: none).  A lane without
+  // a vector gets column kOutOfRange: row offset + kOutOfRange stays below
+  // 2^32 (a slice is under kOutOfRange - 4096 bytes) and past the buffer's
+  // end, so it reads zeros, which it stores into the unread unit of a K row.
+  uint32_t stab[VPT], scol[VPT];
+  int soff[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int e = th + HT * j;
+    const int r = e / a.nvec, c = e - r * a.nvec;
+    stab[j] = (uint32_t)(r < STG ? r : 0) * (uint32_t)sizeof(int2);
+    scol[j] = e < kvec ? 16u * c : (uint32_t)kOutOfRange;
+    soff[j] = e < kvec ? (stage_v ? VOFF + r * PV : r * PK) + 8 * c : -1;
+  }
+  const int junk = (th % STG) * PK + DP;
+  const int bstride = stage_v ? STG * PV : STG * PK;
+  uint4 stg[AH][VPT];
+  auto stage_offsets = [&](int(&at)[VPT], int stage) {
+    // a stage's entries never wrap around the ring
+    const char* tab = reinterpret_cast<const char*>(s_tab) + (stage % TABST) * STG * (int)sizeof(int2);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const uint32_t off = (uint32_t)reinterpret_cast<const int2*>(tab + stab[j])->y;
+      at[j] = (int)(off + scol[j]);
+    }
+  };
+  auto stage_load = [&](uint4(&dst)[VPT], const int(&at)[VPT]) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at[j], 0, 0));
+  };
+  auto stage_store = [&](const uint4(&src)[VPT], int stage) {
+    const int base = (stage & 1) * bstride;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) *reinterpret_cast<uint4*>(s_kv + (soff[j] >= 0 ? base + soff[j] : junk)) = src[j];
+  };
+
+  // The stream's first segment (the sinks, else the lowest valid selected
+  // block, else the window), from the selection row alone.  When it covers
+  // the first AH stages (contiguous layout), their K/V loads are issued now,
+  // so that they are in flight while the segments and the token table are
+  // built; the prologue below then skips them.
+  bool early = false;
+  if constexpr (!PAGED) {
+    int mn = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPrefItems / 64; ++j) {
+      const int x = erow[j];
+      const bool v = lane + 64 * j < a.kk && x >= 0 && x < a.nb && max(x * a.B, S) < min((x + 1) * a.B, a.win_start);
+      mn = v ? min(mn, x) : mn;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
+    int lo0, len0;
+    if (s_len > 0) {
+      lo0 = 0;
+      len0 = s_len;
+    } else if (mn != 0x7fffffff) {
+      lo0 = seg_lo(mn);
+      len0 = seg_len(mn);
+    } else {
+      lo0 = a.win_start;
+      len0 = max(min(a.N, pmax + 1) - a.win_start, 0);
+    }
+    early = __builtin_amdgcn_readfirstlane(len0 >= AH * STG ? 1 : 0) != 0;
+    if (early) {
+      // stage t, vector j: token lo0 + STG t + (its row in the stage)
+      auto direct = [&](int(&at)[VPT], int t) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+          at[j] = (int)((uint32_t)(lo0 + STG * t + (int)(stab[j] / (uint32_t)sizeof(int2))) * (uint32_t)row_bytes +
+                        scol[j]);
+      };
+      // ring slot sl holds stage sl (K) or stage sl - 1 mod AH (V): the role
+      // enters the address only, so no value is selected after its load
+      int at0[VPT];
+#pragma unroll
+      for (int sl = 0; sl < AH; ++sl) {
+        direct(at0, stage_v ? (sl + AH - 1) % AH : sl);
+        stage_load(stg[sl], at0);
+      }
+    }
+  }
+
   // Three barriers: the entries, the kept entries, the items.  Every kept
   // block finds its rank in block order, its stream offset and (thread 0)
   // the totals by one pass over the kept entries, with no block-wide scan.
-  const int S = a.sink_end;
-  const int s_len = min(S, pmax + 1);  // the sinks, clipped to the causal limit
-  auto seg_lo = [&](int x) { return max(x * a.B, S); };
-  auto seg_len = [&](int x) { return max(min(min((x + 1) * a.B, a.win_start), pmax + 1) - seg_lo(x), 0); };
   if (tid < kPrefItems) {
     const bool valid = tid < a.kk && blk >= 0 && blk < a.nb &&
                        max(blk * a.B, S) < min((blk + 1) * a.B, a.win_start);
@@ -254,7 +361,6 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
   // token table: stream offset tau -> (position, byte offset of its K/V
   // row: position order in the memory, or through the page table), kNoPos
   // past the end; entry tau sits at tau mod TAB
-  const int row_bytes = a.row_stride * 2;
   const int32_t* ptab = PAGED ? a.pages + (int64_t)bg * a.pages_stride : nullptr;
   // each thread fills a run of consecutive entries, with one search for the
   // run's first segment
@@ -288,55 +394,6 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
     }
   };
   fill(0, RF * STG);  // the rest after the first loads are issued
-
-  // staging: threads [0, HT) move K, [HT, NT) move V; thread t of its half
-  // moves vectors e = t + HT j of the stage.  Buffer loads with one 32-bit
-  // offset per vector (rows past the end read zeros); AH stages of loads
-  // are in flight in a ring of registers.  K is stored two stages ahead of
-  // the one whose softmax runs, V one stage ahead, so two buffers of each
-  // suffice.
-  const int kvec = STG * a.nvec;
-  const bool stage_v = wave >= 2 * KH;  // wave-uniform, so the buffer resource stays scalar
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((stage_v ? a.v : a.k) + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kBufferFlags);
-  const int th = stage_v ? tid - HT : tid;
-  // Per vector: its row's table entry within a stage (byte offset), its
-  // column in bytes, and its LDS slot in buffer 0 (-1: none).  A lane without
-  // a vector gets column kOutOfRange: row offset + kOutOfRange stays below
-  // 2^32 (a slice is under kOutOfRange - 4096 bytes) and past the buffer's
-  // end, so it reads zeros, which it stores into the unread unit of a K row.
-  uint32_t stab[VPT], scol[VPT];
-  int soff[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int e = th + HT * j;
-    const int r = e / a.nvec, c = e - r * a.nvec;
-    stab[j] = (uint32_t)(r < STG ? r : 0) * (uint32_t)sizeof(int2);
-    scol[j] = e < kvec ? 16u * c : (uint32_t)kOutOfRange;
-    soff[j] = e < kvec ? (stage_v ? VOFF + r * PV : r * PK) + 8 * c : -1;
-  }
-  const int junk = (th % STG) * PK + DP;
-  const int bstride = stage_v ? STG * PV : STG * PK;
-  uint4 stg[AH][VPT];
-  auto stage_offsets = [&](int(&at)[VPT], int stage) {
-    // a stage's entries never wrap around the ring
-    const char* tab = reinterpret_cast<const char*>(s_tab) + (stage % TABST) * STG * (int)sizeof(int2);
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const uint32_t off = (uint32_t)reinterpret_cast<const int2*>(tab + stab[j])->y;
-      at[j] = (int)(off + scol[j]);
-    }
-  };
-  auto stage_load = [&](uint4(&dst)[VPT], const int(&at)[VPT]) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-      dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at[j], 0, 0));
-  };
-  auto stage_store = [&](const uint4(&src)[VPT], int stage) {
-    const int base = (stage & 1) * bstride;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) *reinterpret_cast<uint4*>(s_kv + (soff[j] >= 0 ? base + soff[j] : junk)) = src[j];
-  };
 
   // Rows past the last query compute unused values (rows never mix in
   // either product).
@@ -473,19 +530,23 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(PrefillArgs a) {
     static_assert(AH >= 2, "K stages 0 and 1 take two ring slots");
     const int lag = stage_v ? 1 : 2;
     if (stage_v) {
+      if (!early) {
 #pragma unroll
-      for (int t = 0; t < AH; ++t) {
-        stage_offsets(at, t);
-        stage_load(stg[(t + 1) % AH], at);
+        for (int t = 0; t < AH; ++t) {
+          stage_offsets(at, t);
+          stage_load(stg[(t + 1) % AH], at);
+        }
       }
       stage_store(stg[1 % AH], 0);
       stage_offsets(at, AH);
       stage_load(stg[1 % AH], at);
     } else {
+      if (!early) {
 #pragma unroll
-      for (int t = 0; t < AH; ++t) {
-        stage_offsets(at, t);
-        stage_load(stg[t], at);
+        for (int t = 0; t < AH; ++t) {
+          stage_offsets(at, t);
+          stage_load(stg[t], at);
+        }
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
