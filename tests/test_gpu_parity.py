@@ -57,6 +57,19 @@ SMALL = {
     "prefill_many_segments": W["infllm_gqa_decode_128k"].scaled(n_q_heads=4, n_kv_heads=2, n_tokens=300 * 16 + 7,
                                                                  block=16, window=64, sinks=8, k=250, n_q=64,
                                                                  planted_per_head=0),
+    # the prefill kernel requests its first four 64-token stages before the
+    # segments are built when the first segment covers them: sinks first
+    # (300 sink tokens), a selected 300-token block first (no sinks), the
+    # window first (every token in the window, so no candidate blocks)
+    "prefill_first_segment_sinks": W["infllm_gqa_decode_128k"].scaled(
+        n_q_heads=4, n_kv_heads=2, n_tokens=5000 + 9, block=64, window=128, sinks=300, k=6, n_q=80,
+        planted_per_head=0),
+    "prefill_first_segment_block": W["memlong_chunk_prefill_80k"].scaled(
+        n_q_heads=2, n_kv_heads=2, head_dim=128, row_stride=128, n_tokens=20 * 300 + 77, block=300, window=400,
+        k=4, n_q=96),
+    "prefill_first_segment_window": W["infllm_gqa_decode_128k"].scaled(
+        n_q_heads=4, n_kv_heads=2, n_tokens=3000, block=64, window=3000, sinks=0, k=4, n_q=70,
+        planted_per_head=0),
     # a query chunk with more selected blocks than the prefill kernel's
     # segment table holds (k + 2 > 256): the split path with row groups of
     # 16 query rows takes it
