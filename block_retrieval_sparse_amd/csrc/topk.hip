@@ -39,9 +39,26 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   const int64_t my1 = (my0 + c < hi) ? my0 + c : hi;
 
   uint32_t keys[KPT > 0 ? KPT : 1];
-  if (KPT > 0) {
+  if constexpr (KPT > 0) {
+    // a thread's run as 16-byte loads when the row and the runs are 16-byte
+    // aligned and whole (a wave's loads then touch each cache line in one
+    // instruction instead of one per element)
+    const bool vec = KPT % 4 == 0 && c == KPT && ((uintptr_t)(s + lo) & 15) == 0 && my1 - my0 == KPT;
+    if (vec) {
 #pragma unroll
-    for (int i = 0; i < (KPT > 0 ? KPT : 1); ++i) keys[i] = (my0 + i < my1) ? topk_key(s[my0 + i]) : 0u;
+      for (int i = 0; i < KPT; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(s + my0 + i);
+        keys[i] = topk_key(v.x);
+        keys[i + 1] = topk_key(v.y);
+        keys[i + 2] = topk_key(v.z);
+        keys[i + 3] = topk_key(v.w);
+      }
+    } else if (n > 0) {
+      // unconditional loads (past the run: column lo again, never used), so
+      // they are all in flight together
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) keys[i] = topk_key(s[my0 + i < my1 ? my0 + i : lo]);
+    }
   }
   const int64_t mine = my1 > my0 ? my1 - my0 : 0;
   // f(i, key) for this thread's keys in index order (register keys: the
