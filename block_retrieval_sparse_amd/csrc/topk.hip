@@ -11,29 +11,38 @@
 //     select of the k-th key with a 256-bin histogram in LDS, ties at it to
 //     the lowest indices, rank sort of the winners;
 //   otherwise: the same with 1024 threads, keys in registers or re-read,
-//     one histogram per wave (atomics never contend across waves).
+//     histograms per wave (atomics never contend across waves); once the
+//     keys at or above the digits found so far number at most 2k, they are
+//     gathered and ranked directly instead of running the remaining passes.
 #include "brs_wave_topk.h"
 
 namespace brs {
 namespace {
+
+constexpr int kGather = 2048;  // keys gathered for the final ranking (k <= kGather)
 
 template <int NT, int KPT>  // KPT = 0: keys re-read from global memory each pass
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t stride, int64_t lo,
                                                   int64_t hi, int k, int32_t* __restrict__ idx,
                                                   float* __restrict__ vals) {
   constexpr int NW = NT / 64;
-  __shared__ uint32_t whist[NW][256];  // one histogram per wave (no atomics across waves)
+  // per wave (no atomics across waves), four histograms by lane mod 4 in the
+  // first pass, whose digit (sign and top exponent bits) many keys share;
+  // one in the later passes
+  constexpr int NSUB = 4;
+  __shared__ uint32_t whist[NW][NSUB][256];
   __shared__ uint32_t hist[256];
   __shared__ int wave_tot[16];
   __shared__ uint32_t sh_digit;
-  __shared__ int sh_above;
+  __shared__ int sh_above, sh_neq;
+  __shared__ int srank[kGather];
   __shared__ int sel_count;
-  __shared__ uint64_t sel_key[2048];
+  __shared__ __align__(16) uint64_t sel_key[kGather];
 
   const int64_t row = blockIdx.x;
   const float* s = scores + row * stride;
   const int64_t n = hi - lo;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t c = (n + NT - 1) / NT;  // candidates per thread, contiguous
   const int64_t my0 = lo + tid * c;
   const int64_t my1 = (my0 + c < hi) ? my0 + c : hi;
@@ -74,25 +83,52 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   };
 
   if (tid == 0) sel_count = 0;
-  uint32_t thresh = 0;
+  // Radix select, 8 bits per pass.  After each pass, when the keys at or
+  // above the lowest key with the digits found so far number at most
+  // kGather, they are gathered and ranked directly (the usual case: few keys
+  // share the top digits); otherwise the select runs on to the exact k-th key
+  // and the keys equal to it are taken in index order.
+  uint32_t thresh = 0, lb = 0;
   int take_eq = 0;
+  bool direct = false;
   const bool all = n <= k;
   if (!all) {
     uint32_t prefix = 0, mask = 0;
     int kk = k;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = tid; i < NW * 256; i += NT) whist[i >> 8][i & 255] = 0u;
+      uint32_t* wflat = &whist[0][0][0];
+      if (pass == 0) {
+        for (int i = tid; i < NW * NSUB * 256; i += NT) wflat[i] = 0u;
+      } else {
+        for (int i = tid; i < NW * 256; i += NT) wflat[(i >> 8) * (NSUB * 256) + (i & 255)] = 0u;
+      }
       __syncthreads();
-      const int wv = tid >> 6;
-      for_keys([&](int64_t, uint32_t x) {
-        if ((x & mask) == prefix) atomicAdd(&whist[wv][(x >> shift) & 255u], 1u);
-      });
+      const int wv = tid >> 6, sub = pass == 0 ? (lane & (NSUB - 1)) : 0;
+      if constexpr (KPT > 0) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          const bool match = i < mine && (keys[i] & mask) == prefix;
+          const uint32_t dg = (keys[i] >> shift) & 255u;
+          if (match) atomicAdd(&whist[wv][sub][dg], 1u);
+        }
+      } else {
+        for_keys([&](int64_t, uint32_t x) {
+          if ((x & mask) == prefix) atomicAdd(&whist[wv][sub][(x >> shift) & 255u], 1u);
+        });
+      }
       __syncthreads();
       for (int i = tid; i < 256; i += NT) {
         uint32_t t = 0u;
+        if (pass == 0) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) t += whist[w][i];
+          for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int u = 0; u < NSUB; ++u) t += whist[w][u][i];
+        } else {
+#pragma unroll
+          for (int w = 0; w < NW; ++w) t += whist[w][0][i];
+        }
         hist[i] = t;
       }
       __syncthreads();
@@ -116,6 +152,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
           if (before < kk && before + h[i] >= kk) {
             sh_digit = 255u - (uint32_t)(4 * tid + i);
             sh_above = before;
+            sh_neq = h[i];
           }
           before += h[i];
         }
@@ -124,44 +161,109 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       kk -= sh_above;
       prefix |= sh_digit << shift;
       mask |= 0xffu << shift;
+      const int neq = sh_neq;
       __syncthreads();
+      // keys >= prefix: the k - kk above it and the neq sharing its digits
+      // (ranked by counting: at most 2k of them)
+      if (k - kk + neq <= min(kGather, 2 * k)) {
+        lb = prefix;
+        direct = true;
+        break;
+      }
     }
-    thresh = prefix;
-    take_eq = kk;
+    if (!direct) {
+      thresh = prefix;
+      take_eq = kk;
+    }
   }
 
-  // count my keys equal to the threshold, in index order
-  int eq = 0;
-  if (!all) for_keys([&](int64_t, uint32_t x) { eq += x == thresh; });
-  const int eq_incl = block_inclusive_scan(all ? 0 : eq, wave_tot);
-  int rank_eq = eq_incl - eq;
-  for_keys([&](int64_t i, uint32_t x) {
-    bool take = all || x > thresh;
-    if (!all && x == thresh) {
-      take = rank_eq < take_eq;
+  // gather: every key >= lb (direct), or the k winners with the keys equal
+  // to the threshold taken in index order; one slot reservation per wave
+  int rank_eq = 0;
+  if (!all && !direct) {
+    int eq = 0;
+    for_keys([&](int64_t, uint32_t x) { eq += x == thresh; });
+    rank_eq = block_inclusive_scan(eq, wave_tot) - eq;
+  }
+  for (int i = tid; i < kGather; i += NT) srank[i] = 0;
+  const int cap = direct ? kGather : k;
+  auto taken = [&](uint32_t x) {
+    if (all) return true;
+    if (direct) return x >= lb;
+    bool t = x > thresh;
+    if (x == thresh) {
+      t = rank_eq < take_eq;
       ++rank_eq;
     }
-    if (take) {
-      const int p = atomicAdd(&sel_count, 1);
-      const uint32_t b = (uint32_t)(my0 + i);
-      if (p < k) sel_key[p] = ((uint64_t)x << 32) | (uint64_t)(0xffffffffu - b);
+    return t;
+  };
+  if constexpr (KPT > 0) {
+    uint32_t tk = 0u;  // bit i: key i taken
+    int total = 0;     // the wave's taken keys
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool take = i < mine && taken(keys[i]);
+      tk |= take ? (1u << i) : 0u;
+      total += (int)__popcll(__ballot(take));
     }
-  });
+    if (total > 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sel_count, total);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const bool take = (tk >> i) & 1u;
+        const uint64_t m = __ballot(take);
+        const int p = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint32_t b = (uint32_t)(my0 + i);
+        if (take && p < cap) sel_key[p] = ((uint64_t)keys[i] << 32) | (uint64_t)(0xffffffffu - b);
+        base += (int)__popcll(m);
+      }
+    }
+  } else {
+    for_keys([&](int64_t i, uint32_t x) {
+      if (taken(x)) {
+        const int p = atomicAdd(&sel_count, 1);
+        const uint32_t b = (uint32_t)(my0 + i);
+        if (p < cap) sel_key[p] = ((uint64_t)x << 32) | (uint64_t)(0xffffffffu - b);
+      }
+    });
+  }
   __syncthreads();
-  const int cnt = min(sel_count, k);
+  const int cnt = min(sel_count, cap);
   int32_t* orow = idx + row * k;
   float* vrow = vals ? vals + row * k : nullptr;
-  for (int i = tid; i < cnt; i += NT) {
+  // ranks by counting on (key, ~index); each count is split over P threads
+  // whose partial counts are summed in LDS, so that every thread takes part
+  const int P = cnt > 0 ? max(1, NT / cnt) : 1;
+  for (int u = tid; u < P * cnt; u += NT) {
+    const int i = u % cnt, part = u / cnt;
+    const int j0 = part * cnt / P, j1 = (part + 1) * cnt / P;
     const uint64_t me = sel_key[i];
-    int rank = 0;
-    for (int j = 0; j < cnt; ++j) rank += sel_key[j] > me;
-    const int64_t b = (int64_t)(0xffffffffu - (uint32_t)(me & 0xffffffffu));
+    int c = 0;
+    int j = j0;
+    if ((j & 1) && j < j1) c += sel_key[j++] > me;
+    // two keys per 16-byte read
+#pragma unroll 4
+    for (; j + 1 < j1; j += 2) {
+      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(&sel_key[j]);
+      c += (v.x > me) + (v.y > me);
+    }
+    if (j < j1) c += sel_key[j] > me;
+    atomicAdd(&srank[i], c);
+  }
+  __syncthreads();
+  for (int i = tid; i < cnt; i += NT) {
+    const int rank = srank[i];
     if (rank < k) {
+      const int64_t b = (int64_t)(0xffffffffu - (uint32_t)(sel_key[i] & 0xffffffffu));
       orow[rank] = (int32_t)b;
       if (vrow) vrow[rank] = s[b];
     }
   }
-  for (int i = cnt + tid; i < k; i += NT) {
+  const int filled = min(cnt, k);
+  for (int i = filled + tid; i < k; i += NT) {
     orow[i] = -1;
     if (vrow) vrow[i] = -INFINITY;
   }
