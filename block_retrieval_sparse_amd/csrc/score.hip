@@ -87,8 +87,9 @@ __device__ __forceinline__ void lane_pair(double v, double& p0, double& p1) {
   if constexpr (OFF <= 8) {
     constexpr int ctrl = OFF == 1 ? 0xb1 : OFF == 2 ? 0x4e : OFF == 4 ? 0x141 : 0x140;
     p0 = v;
-    p1 = join((uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, ctrl, 0xf, 0xf, false),
-              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, ctrl, 0xf, 0xf, false));
+    // every lane is written by these permutations: no old value to keep
+    p1 = join((uint32_t)__builtin_amdgcn_mov_dpp((int)lo, ctrl, 0xf, 0xf, true),
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, ctrl, 0xf, 0xf, true));
   } else if constexpr (OFF == 16) {
     // a swap returns {own, partner} or {partner, own} by row; both halves
     // are swapped alike, so element e of the two halves is one value
