@@ -309,7 +309,13 @@ def test_broadcast_selection_dot_mode(name):
                                       # one 1024-thread workgroup per row (radix select), keys in registers
                                       (3000, 100, "normal"), (3000, 64, "nan"), (10000, 512, "ties"),
                                       (16384, 1, "normal"), (4096, 200, "zeros"), (12000, 333, "ties"),
-                                      (8000, 300, "mostly_nan")])
+                                      (8000, 300, "mostly_nan"),
+                                      # the keys at or above the digits found so far ranked directly
+                                      # once at most 2k: after the first pass (normal), after later
+                                      # ones (scores within a narrow band), at the 2048-key gather
+                                      # limit (2k = 2048), never (k = 2048), and with k <= 64
+                                      (16384, 320, "normal"), (16384, 320, "near"), (16384, 1024, "normal"),
+                                      (16384, 2048, "ties"), (5000, 40, "normal"), (16384, 700, "nan")])
 def test_select_topk(n, k, kind):
     import block_retrieval_sparse_amd as brs
 
@@ -318,6 +324,8 @@ def test_select_topk(n, k, kind):
     s = rng.standard_normal((rows, stride)).astype(np.float32)
     if kind == "ties":
         s = np.round(s * 4) / 4
+    if kind == "near":  # one exponent, few distinct leading mantissa bits
+        s = (3.0 + 0.05 * s).astype(np.float32)
     if kind == "nan":
         s[:, rng.integers(0, stride, 40)] = np.nan
     if kind == "mostly_nan":  # fewer numbers than k: the k-th key is NaN's
