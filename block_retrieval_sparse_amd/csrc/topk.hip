@@ -84,8 +84,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 
   if (tid == 0) sel_count = 0;
   // Radix select, 8 bits per pass.  After each pass, when the keys at or
-  // above the lowest key with the digits found so far number at most
-  // kGather, they are gathered and ranked directly (the usual case: few keys
+  // above the lowest key with the digits found so far number at most 2k (and
+  // kGather), they are gathered and ranked directly (the usual case: few keys
   // share the top digits); otherwise the select runs on to the exact k-th key
   // and the keys equal to it are taken in index order.
   uint32_t thresh = 0, lb = 0;
