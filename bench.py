@@ -378,7 +378,7 @@ def read_references(hip, stream, dev, gather_bytes: int, chunk_bytes: int) -> di
     torch.cuda.empty_cache()
     return {"contiguous_GB/s": c_gbs, "contiguous_bytes": n,
             "gather_GB/s": g_gbs, "gather_bytes": n_chunks * chunk_bytes, "gather_chunk_bytes": chunk_bytes,
-            "note": "brs_measure_read, best of 5 launches after one untimed; HIP events around each launch"}
+            "note": "brs_measure_read (one workgroup per chunk, non-temporal 16-byte buffer loads), best of 5 launches after one untimed; HIP events around each launch"}
 
 
 # ---------------------------------------------------------------------------

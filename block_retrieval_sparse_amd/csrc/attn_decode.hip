@@ -1021,6 +1021,7 @@ constexpr int kSelWaves = 4;           // waves 0..R-1 select (R <= 4 score rows
 constexpr int kStepK = 128;            // largest k selected inside the attention kernel
 constexpr int kStepCand = 256;         // candidates the fast selection ranks (else the radix select)
 constexpr int kWaitVm0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr int kVStream = 2;            // cache policy of the whole-row V loads: non-temporal
 
 // A pointer the compiler keeps in scalar registers (a buffer resource built
 // from a vector register would need a loop over its distinct values).
@@ -1198,6 +1199,10 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
   };
 
   const int rs2 = a.row_stride * 2;
+  // whole-row V loads: VRPI tile rows per load instruction, lane (vr, vu)
+  constexpr int VUPR = D / 8, VRPI = 64 / VUPR;
+  static_assert(VRPI * 2 * KC == 32, "a tile's 32 V rows in 2 KC loads per lane");
+  const int vr = lane / VUPR, vu = lane - vr * VUPR;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr((const uint16_t*)a.k + (int64_t)bg * a.head_stride), (short)0, a.slice_bytes, kSlotFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1231,9 +1236,24 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk)
         tl.k[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
+      if constexpr (PAGED) {
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        tl.v[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 64 * kk, 0, 0));
+        for (int kk = 0; kk < KC; ++kk)
+          tl.v[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 64 * kk, 0, 0));
+      }
+    }
+    if constexpr (!PAGED) {
+      // V only goes to LDS, so its loads need not follow the operand layout:
+      // load j of lane l takes 16-byte unit vu of tile row VRPI j + vr, so an
+      // instruction reads whole rows (whole cache lines), with the
+      // non-temporal policy (each row is read once)
+#pragma unroll
+      for (int j = 0; j < 2 * KC; ++j) {
+        const int pos = tl.pos0 + VRPI * j + vr;
+        const bool val = (tl.mk != 0u) & (pos >= tl.vlo) & (pos < tl.vhi);
+        tl.v[j / KC][j % KC] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, val ? pos * rs2 + 16 * vu : kSlotOOR, 0, kVStream));
+      }
     }
   };
 
@@ -1243,8 +1263,12 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        *reinterpret_cast<uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]) = tl.v[sidx][kk];
+      for (int kk = 0; kk < KC; ++kk) {
+        if constexpr (PAGED)
+          *reinterpret_cast<uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]) = tl.v[sidx][kk];
+        else
+          *reinterpret_cast<uint4*>(&s_v[wave][VRPI * (sidx * KC + kk) + vr][8 * vu]) = tl.v[sidx][kk];
+      }
     f32x4_t st2[2];
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx) {

@@ -19,13 +19,16 @@ extern "C" {
  *   offsets : device array of n_chunks byte offsets from base (each a
  *             multiple of 16), one workgroup per chunk -- the access pattern
  *             of retrieved blocks; or NULL with n_chunks = 1 to read
- *             [base, base + chunk_bytes) as one contiguous span with a
- *             grid-stride loop.
+ *             [base, base + chunk_bytes) as one contiguous span, one
+ *             workgroup per 256 KB of it.  Non-temporal 16-byte buffer loads
+ *             that read whole cache lines per instruction (the fastest read
+ *             form measured on gfx950).
  *   never   : a value the XOR of all words read is compared with; only on
  *             equality is anything written (to sink), so the loads stay in
  *             the kernel but nothing is written in practice.
  *   sink    : device buffer of 1024 uint32.
- * chunk_bytes must be a positive multiple of 16.  Enqueued on stream;
+ * chunk_bytes must be a positive multiple of 16 (below 2^31 with offsets).
+ * Enqueued on stream;
  * returns BRS_OK, BRS_E_INVAL or BRS_E_HIP (no message is recorded). */
 int brs_measure_read(const void* base, int64_t chunk_bytes, const int64_t* offsets, int64_t n_chunks,
                      uint32_t never, uint32_t* sink, void* stream);
