@@ -1021,7 +1021,7 @@ constexpr int kSelWaves = 4;           // waves 0..R-1 select (R <= 4 score rows
 constexpr int kStepK = 128;            // largest k selected inside the attention kernel
 constexpr int kStepCand = 256;         // candidates the fast selection ranks (else the radix select)
 constexpr int kWaitVm0 = 0x0F70;       // s_waitcnt vmcnt(0), other counters unconstrained
-constexpr int kVStream = 2;            // cache policy of the whole-row V loads: non-temporal
+constexpr int kKvStream = 2;            // cache policy of the whole-row K/V loads: non-temporal
 
 // A pointer the compiler keeps in scalar registers (a buffer resource built
 // from a vector register would need a loop over its distinct values).
@@ -1232,57 +1232,89 @@ __device__ __forceinline__ void slot_unit(const SplitArgs& a, int unit, SlotLds<
         const int blk = val ? pos / a.B : 0;
         row = tl.row0 >= 0 ? tl.row0 + 16 * sidx + n : ptab[blk] * a.B + (pos - blk * a.B);
       }
-      const int off = val ? row * rs2 + 16 * g4 : kSlotOOR;
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        tl.k[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
       if constexpr (PAGED) {
+        const int off = val ? row * rs2 + 16 * g4 : kSlotOOR;
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+          tl.k[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk)
           tl.v[sidx][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 64 * kk, 0, 0));
       }
     }
     if constexpr (!PAGED) {
-      // V only goes to LDS, so its loads need not follow the operand layout:
-      // load j of lane l takes 16-byte unit vu of tile row VRPI j + vr, so an
-      // instruction reads whole rows (whole cache lines), with the
-      // non-temporal policy (each row is read once)
+      // K and V pass through LDS, so their loads need not follow the operand
+      // layout: load j of lane l takes 16-byte unit vu of tile row
+      // VRPI j + vr, so an instruction reads whole rows (whole cache lines),
+      // with the non-temporal policy (each row is read once)
 #pragma unroll
       for (int j = 0; j < 2 * KC; ++j) {
         const int pos = tl.pos0 + VRPI * j + vr;
         const bool val = (tl.mk != 0u) & (pos >= tl.vlo) & (pos < tl.vhi);
-        tl.v[j / KC][j % KC] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, val ? pos * rs2 + 16 * vu : kSlotOOR, 0, kVStream));
+        const int off = val ? pos * rs2 + 16 * vu : kSlotOOR;
+        tl.k[j / KC][j % KC] =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kKvStream));
+        tl.v[j / KC][j % KC] =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kKvStream));
       }
     }
   };
 
   // one tile: V to LDS, S^T on the matrix cores, the loads of tile tn into
   // the same registers, then softmax and O += P V
-  auto step = [&](Tile& tl, int tn, bool slots) {
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx)
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        if constexpr (PAGED)
-          *reinterpret_cast<uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]) = tl.v[sidx][kk];
-        else
-          *reinterpret_cast<uint4*>(&s_v[wave][VRPI * (sidx * KC + kk) + vr][8 * vu]) = tl.v[sidx][kk];
-      }
-    f32x4_t st2[2];
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) {
-      st2[sidx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        st2[sidx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[sidx][kk]), as_bf16x8(qb[kk]), st2[sidx], 0, 0, 0);
-    }
+  auto wave_sync = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto step = [&](Tile& tl, int tn, bool slots) {
+    f32x4_t st2[2];
     const int p0 = tl.pos0, vlo = tl.vlo, vhi = tl.vhi;
     const bool rowok = (tl.mk & rowbit) != 0u;
-    load(tl, tn, slots);
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+          *reinterpret_cast<uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]) = tl.v[sidx][kk];
+#pragma unroll
+      for (int sidx = 0; sidx < 2; ++sidx) {
+        st2[sidx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+          st2[sidx] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[sidx][kk]), as_bf16x8(qb[kk]), st2[sidx], 0, 0, 0);
+      }
+    } else {
+      // K rows through the wave's LDS tile into the operand layout (lane
+      // (g4, n): 16 bytes of row 16 sidx + n per k chunk), then V into the
+      // same tile
+#pragma unroll
+      for (int j = 0; j < 2 * KC; ++j)
+        *reinterpret_cast<uint4*>(&s_v[wave][VRPI * j + vr][8 * vu]) = tl.k[j / KC][j % KC];
+      wave_sync();
+      uint4 kop[2][KC];
+#pragma unroll
+      for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+          kop[sidx][kk] = *reinterpret_cast<const uint4*>(&s_v[wave][16 * sidx + n][32 * kk + 8 * g4]);
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < 2 * KC; ++j)
+        *reinterpret_cast<uint4*>(&s_v[wave][VRPI * j + vr][8 * vu]) = tl.v[j / KC][j % KC];
+      load(tl, tn, slots);  // the tile's registers are free: the next loads go out now
+#pragma unroll
+      for (int sidx = 0; sidx < 2; ++sidx) {
+        st2[sidx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk)
+          st2[sidx] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[sidx][kk]), as_bf16x8(qb[kk]), st2[sidx], 0, 0, 0);
+      }
+    }
+    wave_sync();
+    if constexpr (PAGED) load(tl, tn, slots);
     // logits of this lane: tokens 4*g4 + i (first half) and 16 + 4*g4 + i, query row n
     float sv[8];
 #pragma unroll
