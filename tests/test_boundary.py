@@ -231,3 +231,23 @@ def test_cache_calls_reject_before_device_work(L):
         assert L.lib.brs_retrieval_attention_cached(mf, c, 0x1000, 2, n_q, 0x80000, 2, 2, 128, 1024, 0.1, 0x3000,
                                                     None, 0x100000, n.value, None) == -3
         assert b"slot-layout and chunked-prefill" in L.lib.brs_last_error()
+
+
+def test_measure_read_rejects_before_device_work(L):
+    """The read-bandwidth reference validates its arguments on the host (fake
+    device addresses: nothing is launched when a check fails)."""
+    lib = L.lib
+    f = lib.brs_measure_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    base, sink, offs = 0x10000, 0x20000, 0x30000
+    inval = -1
+    assert f(None, 1 << 20, None, 1, 0, sink, None) == inval          # no base
+    assert f(base, 1 << 20, None, 1, 0, None, None) == inval          # no sink
+    assert f(base, 8, None, 1, 0, sink, None) == inval                # under one 16-byte unit
+    assert f(base, (1 << 20) + 8, None, 1, 0, sink, None) == inval    # not whole units
+    assert f(base + 8, 1 << 20, None, 1, 0, sink, None) == inval      # misaligned base
+    assert f(base, 1 << 20, None, 2, 0, sink, None) == inval          # a span is one chunk
+    assert f(base, 1 << 31, offs, 4, 0, sink, None) == inval          # gathered chunks under 2^31 bytes
+    assert f(base, 1 << 20, offs, 0, 0, sink, None) == inval          # no chunks
